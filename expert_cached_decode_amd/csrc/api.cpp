@@ -1,0 +1,488 @@
+// C ABI of libexpert_cached_decode.so: context, workspace carving, argument
+// checks and the enqueue order of each MoE layer step.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ec_internal.h"
+#include "host_experts.h"
+#include "prefill.h"
+
+using namespace ec;
+
+namespace {
+
+thread_local std::string g_err; // last error of calls that have no context
+
+uint64_t mailbox_ints(int n) { return 8 + 3ull * n + (4 - (3ull * n) % 4) % 4; }
+
+} // namespace
+
+struct ec_ctx {
+    ec_config cfg{};
+    ec_layout_info lay{};
+    int L = 0, E = 0, k = 0, H = 0, I = 0, wdt = 0, Tmax = 0, Umax = 0, K = 0, C = 0, nmax = 0;
+    uint32_t bp = 0, bh = 1;
+    bool host_branch = false;
+    uint64_t epoch = 1;
+    const uint8_t* host_pool = nullptr;     // host address
+    const uint8_t* host_pool_dev = nullptr; // device address of the same memory
+    uint64_t host_pool_bytes = 0;
+    uint8_t* slot_pool = nullptr;
+    uint64_t slot_pool_bytes = 0;
+    DevState st{};
+    StepBufs sb{};
+    float* act = nullptr;
+    float* y_gpu = nullptr;
+    float* y_host_dev = nullptr;
+    uint32_t* chunk_cnt = nullptr;
+    int32_t* mb_pinned = nullptr;
+    float* y_host_pinned = nullptr;
+    hipStream_t side = nullptr;
+    hipEvent_t ev_ctl = nullptr, ev_side = nullptr;
+    HostPool* pool = nullptr;
+    std::vector<float> host_act;
+    HostJob job{};
+    PrefillState pf{};
+    int prefill_overlap = 1;
+    std::string err;
+};
+
+static ec_status fail(ec_ctx* ctx, ec_status s, const std::string& msg) {
+    if (ctx) ctx->err = msg;
+    g_err = msg;
+    return s;
+}
+
+#define HIPCHK(ctx, call)                                                                      \
+    do {                                                                                       \
+        hipError_t e_ = (call);                                                                \
+        if (e_ != hipSuccess)                                                                  \
+            return fail(ctx, EC_EHIP, std::string(#call) + ": " + hipGetErrorString(e_));      \
+    } while (0)
+
+static ec_status check_shape(const ec_shape* s) {
+    if (!s) return fail(nullptr, EC_EINVAL, "shape is NULL");
+    if (s->layers < 1 || s->experts < 1 || s->experts > kMaxExperts)
+        return fail(nullptr, EC_ESHAPE, "need layers >= 1 and 1 <= experts <= 4096");
+    if (s->top_k < 1 || s->top_k > kMaxTopK || s->top_k > s->experts)
+        return fail(nullptr, EC_ESHAPE, "need 1 <= top_k <= min(32, experts)");
+    if (s->wdtype < EC_DT_F32 || s->wdtype > EC_DT_MXFP4) return fail(nullptr, EC_EUNSUP, "unknown wdtype");
+    // a weight row of the decode GEMV is at most 8 KiB (f32 2048, bf16 4096, MXFP4 8192 elements)
+    const int maxdim = s->wdtype == EC_DT_F32 ? 2048 : s->wdtype == EC_DT_BF16 ? 4096 : 8192;
+    if (s->hidden < 64 || s->inter < 64 || s->hidden % 64 || s->inter % 64 || s->hidden > maxdim ||
+        s->inter > maxdim)
+        return fail(nullptr, EC_ESHAPE, "hidden and inter must be multiples of 64 within the dtype's limit");
+    return EC_OK;
+}
+
+extern "C" {
+
+const char* ec_strerror(ec_status s) {
+    switch (s) {
+    case EC_OK: return "ok";
+    case EC_EINVAL: return "invalid argument";
+    case EC_ESHAPE: return "unsupported or inconsistent shape";
+    case EC_ENOSPC: return "caller buffer too small";
+    case EC_EHIP: return "HIP runtime error";
+    case EC_ESTATE: return "invalid state";
+    case EC_EUNSUP: return "unsupported dtype or device";
+    case EC_EDEVICE: return "device-side check failed";
+    default: return "unknown status";
+    }
+}
+
+const char* ec_last_error(const ec_ctx* ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+ec_status ec_layout(const ec_shape* s, ec_layout_info* o) {
+    ec_status st = check_shape(s);
+    if (st) return st;
+    if (!o) return fail(nullptr, EC_EINVAL, "out is NULL");
+    const uint64_t n = (uint64_t)s->hidden * s->inter;
+    std::memset(o, 0, sizeof(*o));
+    if (s->wdtype == EC_DT_MXFP4) {
+        o->gate_off = 0; o->up_off = n / 2; o->down_off = n;
+        o->gate_scale_off = 3 * n / 2; o->up_scale_off = 3 * n / 2 + n / 32; o->down_scale_off = 3 * n / 2 + 2 * n / 32;
+        o->expert_bytes = 3 * n / 2 + 3 * n / 32;
+    } else {
+        const uint64_t es = s->wdtype == EC_DT_F32 ? 4 : 2;
+        o->gate_off = 0; o->up_off = n * es; o->down_off = 2 * n * es;
+        o->expert_bytes = 3 * n * es;
+    }
+    o->layer_bytes = o->expert_bytes * (uint64_t)s->experts;
+    return EC_OK;
+}
+
+static ec_status check_config(const ec_config* c) {
+    if (!c) return fail(nullptr, EC_EINVAL, "config is NULL");
+    ec_status st = check_shape(&c->shape);
+    if (st) return st;
+    const auto& s = c->shape;
+    if (c->max_tokens < 1 || c->max_tokens > 64 || c->max_tokens * s.top_k > kMaxPairs)
+        return fail(nullptr, EC_ESHAPE, "need 1 <= max_tokens <= 64 and max_tokens * top_k <= 1024");
+    if (c->cache_slots < 0 || (int64_t)c->cache_slots > (int64_t)s.layers * s.experts)
+        return fail(nullptr, EC_EINVAL, "cache_slots must be in [0, layers * experts]");
+    if (c->victim_k < 0 || c->victim_k > kMaxK) return fail(nullptr, EC_EINVAL, "victim_k must be in [0, 64]");
+    if (c->bh_mbps < 1) return fail(nullptr, EC_EINVAL, "BH must be >= 1");
+    if (c->host_threads < 0 || c->host_threads > 256) return fail(nullptr, EC_EINVAL, "host_threads in [0, 256]");
+    if (c->prefill_max_tokens < 0 || c->prefill_max_tokens > (1 << 20))
+        return fail(nullptr, EC_EINVAL, "prefill_max_tokens in [0, 2^20]");
+    if (c->prefill_max_tokens > 0 && s.wdtype == EC_DT_F32)
+        return fail(nullptr, EC_EUNSUP, "prefill needs bf16 or MXFP4 expert weights");
+    return EC_OK;
+}
+
+// Carve the device and pinned workspaces (base pointers may be NULL for sizing).
+static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, uint64_t* pin_bytes) {
+    const int LE = x->L * x->E;
+    Carve d(dev);
+    x->st.resid = d.take<int32_t>(LE);
+    x->st.slot_key = d.take<int32_t>(LE);
+    x->st.slot_lru = d.take<uint64_t>(LE);
+    x->st.clock = d.take<uint64_t>(1);
+    x->st.bw = d.take<uint32_t>(2);
+    x->st.err = d.take<int32_t>(1);
+    x->st.stats = d.take<unsigned long long>((uint64_t)x->L * ST_N);
+    const int n = x->nmax, U = x->Umax;
+    x->sb.ids = d.take<int32_t>(n);
+    x->sb.w = d.take<float>(n);
+    x->sb.uniq = d.take<int32_t>(U);
+    x->sb.counts = d.take<int32_t>(CNT_N);
+    x->sb.pos = d.take<int32_t>(n);
+    x->sb.cls = d.take<int32_t>(U);
+    x->sb.slot = d.take<int32_t>(U);
+    x->sb.fills = d.take<int32_t>(kMaxK);
+    x->sb.victims = d.take<int32_t>(kMaxK);
+    x->sb.evicted = d.take<int32_t>(kMaxK);
+    x->sb.host_list = d.take<int32_t>(U);
+    x->sb.rewritten = d.take<int32_t>(n);
+    x->sb.gpu_slot = d.take<int32_t>(U);
+    x->sb.gpu_rank = d.take<int32_t>(U);
+    x->sb.tok_off = d.take<int32_t>(U + 1);
+    x->sb.tok_pairs = d.take<int32_t>(n);
+    const uint64_t xbytes = (uint64_t)x->Tmax * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
+    const uint64_t mb_bytes = mailbox_ints(n) * 4 + xbytes;
+    x->sb.mailbox = d.take<int32_t>((mb_bytes + 3) / 4);
+    x->act = d.take<float>((uint64_t)n * x->I);
+    x->y_gpu = d.take<float>((uint64_t)n * x->H);
+    x->y_host_dev = d.take<float>((uint64_t)n * x->H);
+    x->chunk_cnt = d.take<uint32_t>((x->H + down_rows_per_chunk() - 1) / down_rows_per_chunk());
+    prefill_carve(x->pf, d, x->cfg.prefill_max_tokens, x->E, x->k, x->H, x->I, x->lay.layer_bytes);
+    *dev_bytes = (d.off + 255) & ~255ull;
+    Carve p(pin);
+    x->mb_pinned = p.take<int32_t>((mb_bytes + 3) / 4);
+    x->y_host_pinned = p.take<float>((uint64_t)n * x->H);
+    *pin_bytes = (p.off + 255) & ~255ull;
+}
+
+static void init_dims(ec_ctx* x, const ec_config* c) {
+    x->cfg = *c;
+    ec_layout(&c->shape, &x->lay);
+    x->L = c->shape.layers; x->E = c->shape.experts; x->k = c->shape.top_k;
+    x->H = c->shape.hidden; x->I = c->shape.inter; x->wdt = c->shape.wdtype;
+    x->Tmax = c->max_tokens;
+    x->nmax = c->max_tokens * x->k;
+    x->Umax = x->nmax < x->E ? x->nmax : x->E;
+    x->K = c->victim_k ? c->victim_k : (x->Umax < kMaxK ? x->Umax : kMaxK);
+    x->C = c->cache_slots;
+    x->bp = c->bp_mbps; x->bh = c->bh_mbps;
+}
+
+static bool needs_host_branch(const ec_ctx* x) {
+    // q = min(m, floor(m*BP/BH), K, C - h) equals m for every step iff BP >= BH, K >= U_max and C >= U_max
+    return !(x->bp >= x->bh && x->K >= x->Umax && x->C >= x->Umax);
+}
+
+ec_status ec_workspace_size(const ec_config* c, uint64_t* dev_bytes, uint64_t* pinned_bytes) {
+    ec_status st = check_config(c);
+    if (st) return st;
+    if (!dev_bytes || !pinned_bytes) return fail(nullptr, EC_EINVAL, "NULL output");
+    ec_ctx tmp;
+    init_dims(&tmp, c);
+    carve(&tmp, nullptr, nullptr, dev_bytes, pinned_bytes);
+    return EC_OK;
+}
+
+ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, void* pinned_ws,
+                    uint64_t pinned_ws_bytes, const void* host_pool, uint64_t host_pool_bytes, void* slot_pool,
+                    uint64_t slot_pool_bytes, ec_ctx** out) {
+    ec_status st = check_config(c);
+    if (st) return st;
+    if (!out || !dev_ws || !pinned_ws || !host_pool) return fail(nullptr, EC_EINVAL, "NULL argument");
+    if (((uintptr_t)dev_ws & 255) || ((uintptr_t)pinned_ws & 255))
+        return fail(nullptr, EC_EINVAL, "workspaces must be 256-byte aligned");
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(nullptr, EC_EHIP, "no HIP device");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(nullptr, EC_EUNSUP, std::string("needs gfx950, found ") + prop.gcnArchName);
+    ec_ctx* x = new ec_ctx();
+    init_dims(x, c);
+    uint64_t need_dev = 0, need_pin = 0;
+    carve(x, nullptr, nullptr, &need_dev, &need_pin);
+    if (dev_ws_bytes < need_dev || pinned_ws_bytes < need_pin) {
+        delete x;
+        return fail(nullptr, EC_ENOSPC, "workspace too small");
+    }
+    if (host_pool_bytes < x->lay.layer_bytes * x->L) {
+        delete x;
+        return fail(nullptr, EC_ENOSPC, "host pool smaller than layers * experts * expert_bytes");
+    }
+    if ((uint64_t)x->C * x->lay.expert_bytes > slot_pool_bytes || (x->C > 0 && !slot_pool)) {
+        delete x;
+        return fail(nullptr, EC_ENOSPC, "slot pool smaller than cache_slots * expert_bytes");
+    }
+    carve(x, (uint8_t*)dev_ws, (uint8_t*)pinned_ws, &need_dev, &need_pin);
+    void* pdev = nullptr;
+    if (hipHostGetDevicePointer(&pdev, const_cast<void*>(host_pool), 0) != hipSuccess || !pdev) {
+        delete x;
+        return fail(nullptr, EC_EINVAL, "host_pool must be pinned, device-accessible memory (hipHostMalloc)");
+    }
+    x->host_pool = (const uint8_t*)host_pool;
+    x->host_pool_dev = (const uint8_t*)pdev;
+    x->host_pool_bytes = host_pool_bytes;
+    x->slot_pool = (uint8_t*)slot_pool;
+    x->slot_pool_bytes = slot_pool_bytes;
+    x->host_branch = needs_host_branch(x);
+    if (hipStreamCreateWithFlags(&x->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&x->ev_ctl, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&x->ev_side, hipEventDisableTiming) != hipSuccess) {
+        delete x;
+        return fail(nullptr, EC_EHIP, "stream/event creation failed");
+    }
+    if (prefill_init(x->pf) != hipSuccess) {
+        delete x;
+        return fail(nullptr, EC_EHIP, "prefill event creation failed");
+    }
+    // initial device state: cold cache, clock 0, zero stats / flags / counters
+    hipStream_t s = x->side;
+    launch_fill_i32((int32_t*)x->st.clock, 0, 2, s);
+    launch_fill_i32(x->st.err, 0, 1, s);
+    launch_fill_i32((int32_t*)x->st.stats, 0, 2ll * x->L * ST_N, s);
+    launch_fill_i32((int32_t*)x->chunk_cnt, 0, (x->H + down_rows_per_chunk() - 1) / down_rows_per_chunk(), s);
+    launch_fill_i32(x->sb.counts, 0, CNT_N, s);
+    launch_reset_cache(x->st, x->L, x->E, x->C, s);
+    launch_set_bw(x->st.bw, x->bp, x->bh, s);
+    prefill_reset_device(x->pf, s);
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) {
+        std::string m = std::string("initialisation failed: ") + hipGetErrorString(e);
+        delete x;
+        return fail(nullptr, EC_EHIP, m);
+    }
+    x->pool = host_pool_create(c->host_threads ? c->host_threads : 8);
+    x->host_act.resize((size_t)x->nmax * x->I);
+    *out = x;
+    return EC_OK;
+}
+
+ec_status ec_destroy(ec_ctx* x) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    (void)hipDeviceSynchronize();
+    if (x->pool) host_pool_destroy(x->pool);
+    prefill_destroy(x->pf);
+    if (x->ev_ctl) (void)hipEventDestroy(x->ev_ctl);
+    if (x->ev_side) (void)hipEventDestroy(x->ev_side);
+    if (x->side) (void)hipStreamDestroy(x->side);
+    delete x;
+    return EC_OK;
+}
+
+ec_status ec_set_bandwidth(ec_ctx* x, uint32_t bp, uint32_t bh, void* stream) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    if (bh < 1) return fail(x, EC_EINVAL, "BH must be >= 1");
+    launch_set_bw(x->st.bw, bp, bh, (hipStream_t)stream);
+    HIPCHK(x, hipGetLastError());
+    x->bp = bp;
+    x->bh = bh;
+    const bool hb = needs_host_branch(x);
+    if (hb != x->host_branch) { x->host_branch = hb; x->epoch++; }
+    return EC_OK;
+}
+
+ec_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* ids, float* w, void* stream) {
+    if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > kMaxTopK || k > E)
+        return fail(nullptr, EC_EINVAL, "need T >= 0, 1 <= E <= 4096, 1 <= k <= min(32, E)");
+    if (T == 0) return EC_OK;
+    if (!logits || !ids || !w) return fail(nullptr, EC_EINVAL, "NULL pointer");
+    launch_route(logits, T, E, k, ids, w, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(nullptr, EC_EHIP, hipGetErrorString(e));
+    return EC_OK;
+}
+
+static CtlArgs ctl_args(ec_ctx* x, int layer, int T) {
+    CtlArgs a{};
+    a.st = x->st;
+    a.sb = x->sb;
+    a.layer = layer; a.E = x->E; a.k = x->k; a.T = T; a.C = x->C; a.K = x->K;
+    return a;
+}
+
+static void fill_view(ec_ctx* x, ec_step_view* v) {
+    if (!v) return;
+    v->uniq = x->sb.uniq; v->counts = x->sb.counts; v->pos = x->sb.pos; v->cls = x->sb.cls;
+    v->slot = x->sb.slot; v->fills = x->sb.fills; v->victims = x->sb.victims; v->evicted = x->sb.evicted;
+    v->host_list = x->sb.host_list; v->rewritten = x->sb.rewritten;
+}
+
+ec_status expert_cache_step(ec_ctx* x, int32_t layer, const int32_t* ids, int32_t T, ec_step_view* out,
+                            void* stream) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    if (layer < 0 || layer >= x->L) return fail(x, EC_EINVAL, "layer out of range");
+    if (T < 1 || T > x->Tmax) return fail(x, EC_EINVAL, "need 1 <= T <= max_tokens");
+    if (!ids) return fail(x, EC_EINVAL, "ids is NULL");
+    CtlArgs a = ctl_args(x, layer, T);
+    a.ids_in = ids;
+    launch_ctl(a, (hipStream_t)stream);
+    HIPCHK(x, hipGetLastError());
+    fill_view(x, out);
+    return EC_OK;
+}
+
+static void host_branch_fn(void* p) {
+    ec_ctx* x = (ec_ctx*)p;
+    const int32_t* mb = x->mb_pinned;
+    const int T = mb[6], layer = mb[7], nhost = mb[CNT_HOST];
+    const int n = T * x->k;
+    HostJob& j = x->job;
+    j.n_experts = nhost;
+    for (int h = 0; h < nhost; ++h)
+        j.expert_base[h] = x->host_pool + ((uint64_t)layer * x->E + mb[CNT_N + h]) * x->lay.expert_bytes;
+    j.rewritten = mb + CNT_N + n;
+    j.T = T; j.k = x->k; j.H = x->H; j.I = x->I; j.wdtype = x->wdt;
+    j.x = mb + mailbox_ints(n);
+    j.y = x->y_host_pinned;
+    j.act = x->host_act.data();
+    host_pool_run(x->pool, j);
+}
+
+ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
+                           void* stream) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    if (layer < 0 || layer >= x->L) return fail(x, EC_EINVAL, "layer out of range");
+    if (T < 1 || T > x->Tmax) return fail(x, EC_EINVAL, "need 1 <= T <= max_tokens");
+    if (!xin || !logits || !out) return fail(x, EC_EINVAL, "NULL pointer");
+    hipStream_t s = (hipStream_t)stream;
+    const int n = T * x->k;
+    const uint64_t xbytes = (uint64_t)T * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
+    CtlArgs a = ctl_args(x, layer, T);
+    a.logits = logits;
+    a.x = xin;
+    a.x_bytes = (int32_t)xbytes;
+    a.host_branch = x->host_branch ? 1 : 0;
+    launch_ctl(a, s);
+    HIPCHK(x, hipGetLastError());
+    if (x->host_branch) {
+        HIPCHK(x, hipEventRecord(x->ev_ctl, s));
+        HIPCHK(x, hipStreamWaitEvent(x->side, x->ev_ctl, 0));
+        HIPCHK(x, hipMemcpyAsync(x->mb_pinned, x->sb.mailbox, mailbox_ints(n) * 4 + xbytes, hipMemcpyDeviceToHost,
+                                 x->side));
+        HIPCHK(x, hipLaunchHostFunc(x->side, host_branch_fn, x));
+        HIPCHK(x, hipMemcpyAsync(x->y_host_dev, x->y_host_pinned, (uint64_t)n * x->H * 4, hipMemcpyHostToDevice,
+                                 x->side));
+        HIPCHK(x, hipEventRecord(x->ev_side, x->side));
+    }
+    DecodeArgs d{};
+    d.pool = x->host_pool_dev; d.slots = x->slot_pool; d.counts = x->sb.counts; d.fills = x->sb.fills;
+    d.victims = x->sb.victims; d.gpu_slot = x->sb.gpu_slot; d.gpu_rank = x->sb.gpu_rank;
+    d.tok_off = x->sb.tok_off; d.tok_pairs = x->sb.tok_pairs; d.rewritten = x->sb.rewritten; d.w = x->sb.w;
+    d.x = xin; d.act = x->act; d.y_gpu = x->y_gpu; d.y_host = x->y_host_dev; d.chunk_cnt = x->chunk_cnt;
+    d.out = out; d.expert_bytes = x->lay.expert_bytes;
+    d.layer = layer; d.E = x->E; d.k = x->k; d.T = T; d.H = x->H; d.I = x->I; d.wdtype = x->wdt; d.U_max = x->Umax;
+    if (x->C > 0) launch_fill(d, x->K, s);
+    launch_gu(d, s);
+    HIPCHK(x, hipGetLastError());
+    if (x->host_branch) HIPCHK(x, hipStreamWaitEvent(s, x->ev_side, 0));
+    launch_down(d, s);
+    HIPCHK(x, hipGetLastError());
+    return EC_OK;
+}
+
+ec_status ec_set_prefill_overlap(ec_ctx* x, int32_t on) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    x->prefill_overlap = on ? 1 : 0;
+    return EC_OK;
+}
+
+ec_status moe_prefill_layer(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
+                            void* compute_stream, void* copy_stream) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    if (x->cfg.prefill_max_tokens <= 0) return fail(x, EC_ESTATE, "context created without prefill buffers");
+    if (layer < 0 || layer >= x->L) return fail(x, EC_EINVAL, "layer out of range");
+    if (T < 1 || T > x->cfg.prefill_max_tokens) return fail(x, EC_EINVAL, "need 1 <= T <= prefill_max_tokens");
+    if (!xin || !logits || !out) return fail(x, EC_EINVAL, "NULL pointer");
+    PrefillCall c{};
+    c.host_pool = x->host_pool;
+    c.layer = layer; c.L = x->L; c.E = x->E; c.k = x->k; c.H = x->H; c.I = x->I; c.T = T; c.wdtype = x->wdt;
+    c.layer_bytes = x->lay.layer_bytes; c.expert_bytes = x->lay.expert_bytes;
+    c.x = xin; c.logits = logits; c.out = out;
+    c.compute = (hipStream_t)compute_stream; c.copy = (hipStream_t)copy_stream;
+    c.overlap = x->prefill_overlap;
+    hipError_t e = prefill_layer(x->pf, c);
+    if (e != hipSuccess) return fail(x, EC_EHIP, std::string("prefill: ") + hipGetErrorString(e));
+    return EC_OK;
+}
+
+ec_status cache_rebuild(ec_ctx* x, int32_t budget_bp, void* new_slot_pool, uint64_t bytes) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    if (budget_bp < 0 || budget_bp > 10000) return fail(x, EC_EINVAL, "budget_bp must be in [0, 10000]");
+    const int64_t C = ((int64_t)budget_bp * x->L * x->E) / 10000;
+    if ((uint64_t)C * x->lay.expert_bytes > bytes || (C > 0 && !new_slot_pool))
+        return fail(x, EC_ENOSPC, "new slot pool smaller than C * expert_bytes");
+    HIPCHK(x, hipDeviceSynchronize()); // safe point: nothing of this context in flight
+    x->C = (int)C;
+    x->slot_pool = (uint8_t*)new_slot_pool;
+    x->slot_pool_bytes = bytes;
+    launch_reset_cache(x->st, x->L, x->E, x->C, x->side);
+    HIPCHK(x, hipStreamSynchronize(x->side));
+    HIPCHK(x, hipGetLastError());
+    x->host_branch = needs_host_branch(x);
+    x->epoch++;
+    return EC_OK;
+}
+
+uint64_t ec_epoch(const ec_ctx* x) { return x ? x->epoch : 0; }
+
+ec_status ec_get_stats(ec_ctx* x, ec_stats* o, int32_t reset) {
+    if (!x || !o) return fail(x, EC_EINVAL, "NULL argument");
+    HIPCHK(x, hipDeviceSynchronize());
+    std::vector<unsigned long long> st((size_t)x->L * ST_N);
+    HIPCHK(x, hipMemcpy(st.data(), x->st.stats, st.size() * 8, hipMemcpyDeviceToHost));
+    int32_t err = 0;
+    uint64_t clk = 0;
+    HIPCHK(x, hipMemcpy(&err, x->st.err, 4, hipMemcpyDeviceToHost));
+    HIPCHK(x, hipMemcpy(&clk, x->st.clock, 8, hipMemcpyDeviceToHost));
+    std::memset(o, 0, sizeof(*o));
+    for (int l = 0; l < x->L; ++l) {
+        const unsigned long long* s = st.data() + (size_t)l * ST_N;
+        o->steps += s[ST_STEPS]; o->hits += s[ST_HITS]; o->misses += s[ST_MISSES];
+        o->fills += s[ST_FILLS]; o->host += s[ST_HOST]; o->evictions += s[ST_EVICT];
+    }
+    o->device_error = err;
+    o->slots = x->C;
+    o->clock = clk;
+    if (reset) {
+        launch_fill_i32((int32_t*)x->st.stats, 0, 2ll * x->L * ST_N, x->side);
+        HIPCHK(x, hipStreamSynchronize(x->side));
+    }
+    return err ? fail(x, EC_EDEVICE, "an expert id outside [0, E) was passed to expert_cache_step") : EC_OK;
+}
+
+ec_status ec_debug_state(ec_ctx* x, int32_t* resid, int32_t* slot_key, uint64_t* slot_lru, uint64_t* clock) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    HIPCHK(x, hipDeviceSynchronize());
+    const uint64_t LE = (uint64_t)x->L * x->E;
+    if (resid) HIPCHK(x, hipMemcpy(resid, x->st.resid, LE * 4, hipMemcpyDeviceToHost));
+    if (slot_key) HIPCHK(x, hipMemcpy(slot_key, x->st.slot_key, (uint64_t)x->C * 4, hipMemcpyDeviceToHost));
+    if (slot_lru) HIPCHK(x, hipMemcpy(slot_lru, x->st.slot_lru, (uint64_t)x->C * 8, hipMemcpyDeviceToHost));
+    if (clock) HIPCHK(x, hipMemcpy(clock, x->st.clock, 8, hipMemcpyDeviceToHost));
+    return EC_OK;
+}
+
+} // extern "C"

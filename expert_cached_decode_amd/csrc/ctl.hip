@@ -1,0 +1,382 @@
+// Routing and the fused cache-control kernel for gfx950 (wave64).
+//
+// FreeToken edge-MoE write-up, "Implementation notes": all routing-dependent
+// control of a decode step runs on the GPU in one kernel (dedup of the routed
+// experts, classification against a residency table shared by all layers,
+// the bandwidth-derived fill count, a single scan that finds the K least
+// recently used candidate slots, and the rewrite of logical routing ids to
+// cache slots), writing fixed-shape buffers plus device-resident counts.
+//
+// The control work is tiny and latency-bound, so it runs in ONE workgroup of
+// 16 wavefronts: bitmap dedup and prefix popcounts in LDS, ballot/popcount
+// block scans for the miss and cache-side lists, and a wave-wide bitonic
+// top-64 for the victims (each wave keeps its 64 oldest candidate slots
+// sorted across its lanes while streaming the slot table once; the 16 wave
+// lists are then merged pairwise in LDS).
+#include "ec_internal.h"
+
+namespace ec {
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+    uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Top-k of one row of E logits by one wavefront: ids by (logit desc, id asc),
+// weights = softmax over the selected logits. ids/w may be global; lds_ids
+// (optional) receives a copy of the ids.
+__device__ void wave_topk(const float* row, int E, int k, int32_t* ids, float* w, int32_t* lds_ids,
+                          float* lds_w) {
+    const int lane = lane_id();
+    uint64_t chosen = 0; // bit i: element lane + 64 i already selected
+    float sel_v = 0.f;
+    int sel_i = 0;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int i = 0, e = lane; e < E; ++i, e += 64) {
+            if ((chosen >> i) & 1) continue;
+            float v = row[e];
+            if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            float ov = __shfl_xor(bv, off);
+            int oi = __shfl_xor(bi, off);
+            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+        }
+        if ((bi & 63) == lane) chosen |= 1ull << (bi >> 6);
+        if (lane == j) { sel_v = bv; sel_i = bi; }
+    }
+    const float top = __shfl(sel_v, 0);
+    float ex = lane < k ? expf(sel_v - top) : 0.f;
+    float s = ex;
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane < k) {
+        ids[lane] = sel_i;
+        w[lane] = ex / s;
+        if (lds_ids) { lds_ids[lane] = sel_i; lds_w[lane] = ex / s; }
+    }
+}
+
+__global__ __launch_bounds__(256) void route_kernel(const float* logits, int T, int E, int k, int32_t* ids,
+                                                    float* w) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    wave_topk(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k, nullptr, nullptr);
+}
+
+// Bitonic sort of 64 (key, val) pairs held one per lane, ascending by key.
+__device__ __forceinline__ void sort64(uint64_t& key, int& val) {
+    const int lane = lane_id();
+    for (int kk = 2; kk <= 64; kk <<= 1) {
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+            uint64_t ok = shfl_xor_u64(key, j);
+            int ov = __shfl_xor(val, j);
+            bool want_min = ((lane & j) == 0) == ((lane & kk) == 0);
+            if (want_min ? (ok < key) : (ok > key)) { key = ok; val = ov; }
+        }
+    }
+}
+
+// Sort a bitonic sequence of 64 pairs (one per lane) ascending.
+__device__ __forceinline__ void merge64(uint64_t& key, int& val) {
+    const int lane = lane_id();
+    for (int j = 32; j > 0; j >>= 1) {
+        uint64_t ok = shfl_xor_u64(key, j);
+        int ov = __shfl_xor(val, j);
+        if (((lane & j) == 0) ? (ok < key) : (ok > key)) { key = ok; val = ov; }
+    }
+}
+
+// Exclusive block scan of one int per thread (kCtlThreads threads).
+__device__ int block_scan(int v, int* s_wtot, int* total) {
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    int incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_wtot[wave] = incl;
+    __syncthreads();
+    int wpre = 0, tot = 0;
+    for (int w2 = 0; w2 < kCtlWaves; ++w2) {
+        int c = s_wtot[w2];
+        wpre += w2 < wave ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return wpre + incl - v;
+}
+
+__global__ __launch_bounds__(kCtlThreads) void ctl_kernel(CtlArgs a) {
+    __shared__ int32_t s_ids[kMaxPairs];
+    __shared__ float s_w[kMaxPairs];
+    __shared__ int32_t s_pos[kMaxPairs];
+    __shared__ uint32_t s_bits[kMaxExperts / 32];
+    __shared__ int32_t s_wpre[kMaxExperts / 32];
+    __shared__ int32_t s_uniq[kMaxPairs];
+    __shared__ int32_t s_slot[kMaxPairs];
+    __shared__ int32_t s_off[kMaxPairs + 1];
+    __shared__ uint64_t s_ck[kCtlWaves][64];
+    __shared__ int32_t s_cs[kCtlWaves][64];
+    __shared__ int32_t s_wtot[kCtlWaves];
+    __shared__ int32_t s_misc[4];
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int E = a.E, k = a.k, T = a.T, l = a.layer, C = a.C;
+    const int n = T * k;
+    const int nwords = (E + 31) >> 5;
+    const uint64_t clk = *a.st.clock;
+
+    // 1. routing (fused) or routed ids from the caller
+    if (a.logits) {
+        for (int t = wave; t < T; t += kCtlWaves)
+            wave_topk(a.logits + (int64_t)t * E, E, k, a.sb.ids + t * k, a.sb.w + t * k, s_ids + t * k,
+                      s_w + t * k);
+    } else {
+        for (int i = tid; i < n; i += kCtlThreads) s_ids[i] = a.ids_in[i];
+    }
+    for (int wd = tid; wd < nwords; wd += kCtlThreads) s_bits[wd] = 0;
+    if (tid == 0) s_misc[0] = 0;
+    __syncthreads();
+
+    // 2. dedup: bitmap of routed experts, ranks by prefix popcount
+    for (int i = tid; i < n; i += kCtlThreads) {
+        int id = s_ids[i];
+        if (id < 0 || id >= E) s_misc[0] = 1;
+        else atomicOr(&s_bits[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+    if (s_misc[0]) { // invalid expert id: flag it, do nothing else
+        if (tid == 0) atomicExch(a.st.err, 1);
+        if (tid < CNT_N) a.sb.counts[tid] = 0;
+        return;
+    }
+    if (wave == 0) {
+        int w0 = 2 * lane, w1 = 2 * lane + 1;
+        int c0 = w0 < nwords ? __popc(s_bits[w0]) : 0;
+        int c1 = w1 < nwords ? __popc(s_bits[w1]) : 0;
+        int v = c0 + c1, incl = v;
+        for (int off = 1; off < 64; off <<= 1) {
+            int o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        if (w0 < nwords) s_wpre[w0] = incl - v;
+        if (w1 < nwords) s_wpre[w1] = incl - v + c0;
+        if (lane == 63) s_misc[1] = incl;
+    }
+    __syncthreads();
+    const int U = s_misc[1];
+    for (int wd = tid; wd < nwords; wd += kCtlThreads) {
+        uint32_t bits = s_bits[wd];
+        int r = s_wpre[wd];
+        while (bits) {
+            int b = __ffs(bits) - 1;
+            s_uniq[r++] = wd * 32 + b;
+            bits &= bits - 1;
+        }
+    }
+    for (int i = tid; i < n; i += kCtlThreads) {
+        int id = s_ids[i];
+        s_pos[i] = s_wpre[id >> 5] + __popc(s_bits[id >> 5] & ((1u << (id & 31)) - 1u));
+    }
+    __syncthreads();
+
+    // 3. classify against the shared residency table
+    const int r = tid;
+    const bool valid = r < U;
+    const int u = valid ? s_uniq[r] : 0;
+    const int sl = valid ? a.st.resid[(int64_t)l * E + u] : -1;
+    const bool miss = valid && sl < 0;
+    int m;
+    const int midx = block_scan(miss ? 1 : 0, s_wtot, &m);
+    const int h = U - m;
+
+    // 4. fill count q = min(m, floor(m*BP/BH), K, C - h)
+    const uint32_t bp = a.st.bw[0], bh = a.st.bw[1];
+    int64_t qq = bh ? (int64_t)(((uint64_t)m * bp) / bh) : 0;
+    qq = min(qq, (int64_t)m);
+    qq = min(qq, (int64_t)a.K);
+    qq = min(qq, (int64_t)(C - h));
+    const int q = qq > 0 ? (int)qq : 0;
+
+    // 5. single scan: the K oldest slots not hit in this step (empty slots first)
+    if (q > 0) {
+        uint64_t bk = ~0ull;
+        int bs = -1;
+        const int nb = (C + 63) >> 6;
+        for (int b = wave; b < nb; b += kCtlWaves) {
+            int s = b * 64 + lane;
+            uint64_t key = ~0ull;
+            if (s < C) {
+                int sk = a.st.slot_key[s];
+                bool hit_here = false;
+                if (sk >= 0 && sk / E == l) {
+                    int e = sk - l * E;
+                    hit_here = (s_bits[e >> 5] >> (e & 31)) & 1u;
+                }
+                if (!hit_here) key = a.st.slot_lru[s];
+            }
+            uint64_t thr = shfl_u64(bk, 63);
+            if (__ballot(key < thr) == 0) continue;
+            int sv = s;
+            sort64(key, sv);
+            uint64_t rk = shfl_u64(key, 63 - lane);
+            int rs = __shfl(sv, 63 - lane);
+            if (rk < bk) { bk = rk; bs = rs; }
+            merge64(bk, bs);
+        }
+        s_ck[wave][lane] = bk;
+        s_cs[wave][lane] = bs;
+        __syncthreads();
+        for (int stride = 1; stride < kCtlWaves; stride <<= 1) {
+            if ((wave % (2 * stride)) == 0 && wave + stride < kCtlWaves) {
+                uint64_t ak = s_ck[wave][lane];
+                int as = s_cs[wave][lane];
+                uint64_t ok = s_ck[wave + stride][63 - lane];
+                int os = s_cs[wave + stride][63 - lane];
+                if (ok < ak) { ak = ok; as = os; }
+                merge64(ak, as);
+                s_ck[wave][lane] = ak;
+                s_cs[wave][lane] = as;
+            }
+            __syncthreads();
+        }
+    }
+    if (tid < a.K) a.sb.victims[tid] = (q > 0 && s_ck[0][tid] != ~0ull) ? s_cs[0][tid] : -1;
+    if (tid < a.K && tid >= q) { a.sb.fills[tid] = -1; a.sb.evicted[tid] = -1; }
+
+    // 6. assign fills to victims (oldest first), host list, LRU update
+    int cls = CLS_HIT, slot_r = sl, ev = 0;
+    if (valid) {
+        if (miss) {
+            if (midx < q) {
+                const int v = s_cs[0][midx];
+                const int old = a.st.slot_key[v];
+                a.sb.evicted[midx] = old;
+                if (old >= 0) { a.st.resid[old] = -1; ev = 1; }
+                a.st.slot_key[v] = l * E + u;
+                a.st.resid[(int64_t)l * E + u] = v;
+                a.sb.fills[midx] = u;
+                cls = CLS_FILL;
+                slot_r = v;
+            } else {
+                const int hidx = midx - q;
+                a.sb.host_list[hidx] = u;
+                cls = CLS_HOST;
+                slot_r = -(1 + hidx);
+            }
+        }
+        if (cls != CLS_HOST) a.st.slot_lru[slot_r] = kLruTouched | ((clk + 1) << 16) | (uint64_t)r;
+        s_slot[r] = slot_r;
+        a.sb.uniq[r] = u;
+        a.sb.cls[r] = cls;
+        a.sb.slot[r] = slot_r;
+    }
+    int n_gpu;
+    const int g = block_scan(valid && cls != CLS_HOST ? 1 : 0, s_wtot, &n_gpu);
+    if (valid && cls != CLS_HOST) { a.sb.gpu_slot[g] = slot_r; a.sb.gpu_rank[g] = r; }
+    int n_ev;
+    (void)block_scan(ev, s_wtot, &n_ev);
+
+    // 7. rewrite (t, j) -> slot or -(1 + host index); token lists per unique expert
+    if (tid <= U) s_off[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kCtlThreads) {
+        a.sb.rewritten[i] = s_slot[s_pos[i]];
+        a.sb.pos[i] = s_pos[i];
+        atomicAdd(&s_off[s_pos[i]], 1);
+    }
+    __syncthreads();
+    int ntot;
+    const int cnt = valid ? s_off[r] : 0;
+    const int off = block_scan(cnt, s_wtot, &ntot);
+    if (valid) { s_off[r] = off; a.sb.tok_off[r] = off; }
+    if (tid == 0) a.sb.tok_off[U] = ntot;
+    __syncthreads();
+    for (int i = tid; i < n; i += kCtlThreads) {
+        const int pr = s_pos[i];
+        int within = 0;
+        for (int i2 = 0; i2 < i; ++i2) within += (s_pos[i2] == pr);
+        a.sb.tok_pairs[s_off[pr] + within] = i;
+    }
+
+    // 8. counts, stats, clock; mailbox for the host branch
+    if (tid == 0) {
+        int32_t* c = a.sb.counts;
+        c[CNT_U] = U; c[CNT_H] = h; c[CNT_M] = m; c[CNT_Q] = q; c[CNT_HOST] = m - q; c[CNT_GPU] = n_gpu;
+        c[6] = 0; c[7] = 0;
+        unsigned long long* st = a.st.stats + (int64_t)l * ST_N;
+        st[ST_STEPS] += 1; st[ST_HITS] += h; st[ST_MISSES] += m; st[ST_FILLS] += q;
+        st[ST_HOST] += m - q; st[ST_EVICT] += n_ev;
+        *a.st.clock = clk + 1;
+    }
+    if (a.host_branch) {
+        // mailbox: [counts 8][host_list n][rewritten n][w n][x bytes], n = T*k
+        int32_t* mb = a.sb.mailbox;
+        if (tid == 0) {
+            mb[CNT_U] = U; mb[CNT_H] = h; mb[CNT_M] = m; mb[CNT_Q] = q; mb[CNT_HOST] = m - q; mb[CNT_GPU] = n_gpu;
+            mb[6] = T; mb[7] = l;
+        }
+        if (valid && cls == CLS_HOST) mb[CNT_N + (-slot_r - 1)] = u;
+        for (int i = tid; i < n; i += kCtlThreads) {
+            mb[CNT_N + n + i] = s_slot[s_pos[i]];
+            reinterpret_cast<float*>(mb)[CNT_N + 2 * n + i] = s_w[i];
+        }
+        const uint4* xs = reinterpret_cast<const uint4*>(a.x);
+        uint4* xd = reinterpret_cast<uint4*>(mb + CNT_N + 3 * n + ((4 - (3 * n) % 4) % 4));
+        for (int i = tid; i < a.x_bytes / 16; i += kCtlThreads) xd[i] = xs[i];
+    }
+}
+
+__global__ void set_bw_kernel(uint32_t* bw, uint32_t bp, uint32_t bh) {
+    if (threadIdx.x == 0) { bw[0] = bp; bw[1] = bh; }
+}
+
+__global__ void reset_cache_kernel(DevState st, int LE, int C) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < LE; i += gridDim.x * blockDim.x) {
+        st.resid[i] = -1;
+        st.slot_key[i] = -1;
+        st.slot_lru[i] = (uint64_t)i; // empty slot s: key s
+    }
+    (void)C;
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
+    if (T <= 0) return;
+    hipLaunchKernelGGL(route_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
+}
+
+void launch_ctl(const CtlArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(ctl_kernel, dim3(1), dim3(kCtlThreads), 0, s, a);
+}
+
+void launch_set_bw(uint32_t* bw, uint32_t bp, uint32_t bh, hipStream_t s) {
+    hipLaunchKernelGGL(set_bw_kernel, dim3(1), dim3(64), 0, s, bw, bp, bh);
+}
+
+void launch_reset_cache(DevState st, int L, int E, int C, hipStream_t s) {
+    int LE = L * E;
+    hipLaunchKernelGGL(reset_cache_kernel, dim3((LE + 255) / 256), dim3(256), 0, s, st, LE, C);
+}
+
+void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+    if (n <= 0) return;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
+}
+
+} // namespace ec

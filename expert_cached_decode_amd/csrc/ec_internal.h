@@ -1,0 +1,116 @@
+// Internal definitions shared by the HIP kernels and the host runtime of
+// libexpert_cached_decode.so (never exported).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ec_api.h"
+
+namespace ec {
+
+// Bump allocator over a caller-owned workspace (NULL base: sizing only).
+struct Carve {
+    uint8_t* base;
+    uint64_t off = 0;
+    explicit Carve(uint8_t* b) : base(b) {}
+    template <class T> T* take(uint64_t count) {
+        off = (off + 255) & ~255ull;
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+constexpr int kMaxPairs = 1024;   // T_max * k
+constexpr int kMaxExperts = 4096; // E
+constexpr int kMaxTopK = 32;
+constexpr int kMaxK = 64;         // victim candidates per step (one wave)
+constexpr int kCtlThreads = 1024; // cache-control workgroup
+constexpr int kCtlWaves = kCtlThreads / 64;
+
+// counts[] layout
+enum { CNT_U = 0, CNT_H = 1, CNT_M = 2, CNT_Q = 3, CNT_HOST = 4, CNT_GPU = 5, CNT_N = 8 };
+// per-layer stats layout (u64)
+enum { ST_STEPS = 0, ST_HITS, ST_MISSES, ST_FILLS, ST_HOST, ST_EVICT, ST_N = 8 };
+enum { CLS_HIT = 0, CLS_FILL = 1, CLS_HOST = 2 };
+
+constexpr uint64_t kLruTouched = 1ull << 63; // LRU key of a slot touched at clock c, rank r:
+                                             // 2^63 | (c + 1) << 16 | r; empty slot s: s
+
+// Device-resident cache state (persistent across steps).
+struct DevState {
+    int32_t* resid;    // [L*E] slot or -1
+    int32_t* slot_key; // [L*E] (only the first C used) l*E+e or -1
+    uint64_t* slot_lru;// [L*E] LRU key
+    uint64_t* clock;   // [1]
+    uint32_t* bw;      // [2] BP, BH
+    int32_t* err;      // [1] device error flag
+    unsigned long long* stats; // [L][ST_N]
+};
+
+// Per-step work buffers (fixed shape, reused by every layer).
+struct StepBufs {
+    int32_t* ids;       // [T_max*k]
+    float* w;           // [T_max*k]
+    int32_t* uniq;      // [U_max]
+    int32_t* counts;    // [CNT_N]
+    int32_t* pos;       // [T_max*k]
+    int32_t* cls;       // [U_max]
+    int32_t* slot;      // [U_max]
+    int32_t* fills;     // [kMaxK]
+    int32_t* victims;   // [kMaxK]
+    int32_t* evicted;   // [kMaxK]
+    int32_t* host_list; // [U_max]
+    int32_t* rewritten; // [T_max*k]
+    int32_t* gpu_slot;  // [U_max] cache-side experts, in uniq order
+    int32_t* gpu_rank;  // [U_max] their index into uniq
+    int32_t* tok_off;   // [U_max+1] pairs of uniq rank r: tok_pairs[tok_off[r] .. tok_off[r+1])
+    int32_t* tok_pairs; // [T_max*k] pair index t*k+j, grouped by rank, ascending inside
+    int32_t* mailbox;   // device staging copied to the host for the host branch (layout in host code)
+};
+
+struct CtlArgs {
+    DevState st;
+    StepBufs sb;
+    const float* logits; // fused routing when non-null
+    const int32_t* ids_in; // routed ids [T*k] when logits is null
+    const void* x;       // layer input, copied into the mailbox when host_branch
+    int32_t x_bytes;     // bytes of x (T*H*elem)
+    int32_t layer, E, k, T, C, K;
+    int32_t host_branch; // 1: write the mailbox for the host branch
+};
+
+// Launchers (defined in the .hip files).
+void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+void launch_ctl(const CtlArgs& a, hipStream_t s);
+void launch_set_bw(uint32_t* bw, uint32_t bp, uint32_t bh, hipStream_t s);
+void launch_reset_cache(DevState st, int L, int E, int C, hipStream_t s);
+void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+struct DecodeArgs {
+    const uint8_t* pool;   // device pointer of the pinned host pool
+    uint8_t* slots;        // slot pool
+    const int32_t* counts;
+    const int32_t* fills;
+    const int32_t* victims;
+    const int32_t* gpu_slot;
+    const int32_t* gpu_rank;
+    const int32_t* tok_off;
+    const int32_t* tok_pairs;
+    const int32_t* rewritten;
+    const float* w;
+    const void* x;
+    float* act;            // [T_max*k][I]
+    float* y_gpu;          // [T_max*k][H]
+    const float* y_host;   // [T_max*k][H] (device copy of host partials)
+    uint32_t* chunk_cnt;   // [H / rows-per-chunk] arrival counters (zero between launches)
+    void* out;
+    uint64_t expert_bytes;
+    int32_t layer, E, k, T, H, I, wdtype, U_max;
+};
+void launch_fill(const DecodeArgs& a, int K, hipStream_t s);
+void launch_gu(const DecodeArgs& a, hipStream_t s);
+void launch_down(const DecodeArgs& a, hipStream_t s);
+int down_rows_per_chunk();
+
+} // namespace ec

@@ -1,0 +1,189 @@
+// Host branch of the decode step: SwiGLU experts computed on host cores,
+// reading the expert bank in host memory.
+//
+// FreeToken edge-MoE write-up, "Bandwidth-adaptive execution" (decode): the
+// misses not filled into the GPU cache are executed directly on the CPU,
+// leaving residency unchanged; host and GPU partial sums are merged exactly.
+// Work is split over worker threads by (expert, block of rows): first the
+// gate/up rows (activations of every token routed to the expert), then the
+// down rows, so each weight byte is read from host memory once per step.
+#include "host_experts.h"
+
+#include <atomic>
+#include <cmath>
+#include <condition_variable>
+#include <cstring>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+namespace ec {
+
+namespace {
+
+inline float bf16f(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// FP4 E2M1 magnitudes (OCP MX v1.0), signed by bit 3.
+const float kE2M1[16] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f,
+                         -0.f, -0.5f, -1.f, -1.5f, -2.f, -3.f, -4.f, -6.f};
+
+inline float e8m0(uint8_t e) {
+    uint32_t u = e ? (uint32_t)e << 23 : 0x00400000u;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
+
+// dot(row, v) over n elements; row in the bank's format (MXFP4: codes + scale row)
+float dot_row(int wdt, const uint8_t* row, const uint8_t* srow, const float* v, int n) {
+    float acc[16] = {0};
+    if (wdt == 0) {
+        const float* w = reinterpret_cast<const float*>(row);
+        for (int i = 0; i < n; i += 16)
+            for (int q = 0; q < 16; ++q) acc[q] += w[i + q] * v[i + q];
+    } else if (wdt == 1) {
+        const uint16_t* w = reinterpret_cast<const uint16_t*>(row);
+        for (int i = 0; i < n; i += 16)
+            for (int q = 0; q < 16; ++q) acc[q] += bf16f(w[i + q]) * v[i + q];
+    } else {
+        for (int b = 0; b < n / 32; ++b) {
+            float blk[16] = {0};
+            const uint8_t* c = row + b * 16;
+            const float* vb = v + b * 32;
+            for (int q = 0; q < 16; ++q) blk[q] = kE2M1[c[q] & 15] * vb[2 * q] + kE2M1[c[q] >> 4] * vb[2 * q + 1];
+            float s = 0.f;
+            for (int q = 0; q < 16; ++q) s += blk[q];
+            acc[b & 15] += s * e8m0(srow[b]);
+        }
+    }
+    float s = 0.f;
+    for (int q = 0; q < 16; ++q) s += acc[q];
+    return s;
+}
+
+} // namespace
+
+struct HostPool {
+    std::vector<std::thread> threads;
+    std::mutex mu;
+    std::condition_variable cv;
+    uint64_t generation = 0;
+    bool stop = false;
+    const HostJob* job = nullptr;
+    // phase bookkeeping
+    std::vector<int> task_expert, task_r0;   // phase-1 and phase-2 task tables
+    std::vector<std::vector<int>> pairs_of;  // host index -> pairs
+    std::vector<float> xf;                   // [T][H] activations widened to f32
+    int n1 = 0, n2 = 0;
+    std::atomic<int> next1{0}, next2{0}, done1{0}, done2{0}, arrived{0};
+    int nworkers = 0;
+    static constexpr int kRows = 32;
+
+    void work() {
+        const HostJob& j = *job;
+        const int H = j.H, I = j.I;
+        const uint64_t rbH = j.wdtype == 0 ? H * 4ull : j.wdtype == 1 ? H * 2ull : H / 2;
+        const uint64_t rbI = j.wdtype == 0 ? I * 4ull : j.wdtype == 1 ? I * 2ull : I / 2;
+        // phase 1: gate/up rows -> act
+        for (int t; (t = next1.fetch_add(1)) < n1;) {
+            const int e = task_expert[t], r0 = task_r0[t];
+            const uint8_t* base = j.expert_base[e];
+            const uint8_t* gsc = base + 3ull * I * rbH;
+            const uint8_t* usc = gsc + (uint64_t)I * (H / 32);
+            for (int i = r0; i < r0 + kRows && i < I; ++i) {
+                const uint8_t* g = base + i * rbH;
+                const uint8_t* u = base + (uint64_t)I * rbH + i * rbH;
+                for (int p : pairs_of[e]) {
+                    const float* xv = xf.data() + (uint64_t)(p / j.k) * H;
+                    float gv = dot_row(j.wdtype, g, gsc + (uint64_t)i * (H / 32), xv, H);
+                    float uv = dot_row(j.wdtype, u, usc + (uint64_t)i * (H / 32), xv, H);
+                    j.act[(uint64_t)p * I + i] = gv / (1.f + std::exp(-gv)) * uv;
+                }
+            }
+            done1.fetch_add(1, std::memory_order_release);
+        }
+        while (done1.load(std::memory_order_acquire) < n1) std::this_thread::yield();
+        // phase 2: down rows -> y
+        for (int t; (t = next2.fetch_add(1)) < n2;) {
+            const int e = task_expert[n1 + t], r0 = task_r0[n1 + t];
+            const uint8_t* base = j.expert_base[e];
+            const uint8_t* d = base + 2ull * I * rbH;
+            const uint8_t* dsc = base + 3ull * I * rbH + 2ull * I * (H / 32);
+            for (int h = r0; h < r0 + kRows && h < H; ++h)
+                for (int p : pairs_of[e])
+                    j.y[(uint64_t)p * H + h] =
+                        dot_row(j.wdtype, d + h * rbI, dsc + (uint64_t)h * (I / 32), j.act + (uint64_t)p * I, I);
+            done2.fetch_add(1, std::memory_order_release);
+        }
+    }
+
+    void loop() {
+        uint64_t seen = 0;
+        for (;;) {
+            {
+                std::unique_lock<std::mutex> lk(mu);
+                cv.wait(lk, [&] { return stop || generation != seen; });
+                if (stop) return;
+                seen = generation;
+            }
+            work();
+            arrived.fetch_add(1, std::memory_order_release);
+        }
+    }
+};
+
+HostPool* host_pool_create(int threads) {
+    HostPool* p = new HostPool();
+    p->nworkers = threads > 1 ? threads - 1 : 0; // the calling thread works too
+    for (int i = 0; i < p->nworkers; ++i) p->threads.emplace_back([p] { p->loop(); });
+    return p;
+}
+
+void host_pool_destroy(HostPool* p) {
+    {
+        std::lock_guard<std::mutex> lk(p->mu);
+        p->stop = true;
+    }
+    p->cv.notify_all();
+    for (auto& t : p->threads) t.join();
+    delete p;
+}
+
+void host_pool_run(HostPool* p, const HostJob& j) {
+    if (j.n_experts <= 0) return;
+    p->job = &j;
+    p->pairs_of.assign(j.n_experts, {});
+    for (int i = 0; i < j.T * j.k; ++i)
+        if (j.rewritten[i] < 0) {
+            int h = -j.rewritten[i] - 1;
+            if (h < j.n_experts) p->pairs_of[h].push_back(i);
+        }
+    p->xf.resize((size_t)j.T * j.H);
+    for (size_t i = 0; i < p->xf.size(); ++i)
+        p->xf[i] = j.wdtype == 0 ? reinterpret_cast<const float*>(j.x)[i]
+                                 : bf16f(reinterpret_cast<const uint16_t*>(j.x)[i]);
+    p->task_expert.clear();
+    p->task_r0.clear();
+    for (int e = 0; e < j.n_experts; ++e)
+        for (int r = 0; r < j.I; r += HostPool::kRows) { p->task_expert.push_back(e); p->task_r0.push_back(r); }
+    p->n1 = (int)p->task_expert.size();
+    for (int e = 0; e < j.n_experts; ++e)
+        for (int r = 0; r < j.H; r += HostPool::kRows) { p->task_expert.push_back(e); p->task_r0.push_back(r); }
+    p->n2 = (int)p->task_expert.size() - p->n1;
+    p->next1 = 0; p->next2 = 0; p->done1 = 0; p->done2 = 0; p->arrived = 0;
+    {
+        std::lock_guard<std::mutex> lk(p->mu);
+        p->generation++;
+    }
+    p->cv.notify_all();
+    p->work();
+    while (p->arrived.load(std::memory_order_acquire) < p->nworkers) std::this_thread::yield();
+    p->job = nullptr;
+}
+
+} // namespace ec

@@ -1,0 +1,364 @@
+// Prefill MoE layer for gfx950.
+//
+// FreeToken edge-MoE write-up, "Bandwidth-adaptive execution" (prefill):
+// because the routing union of a long prompt covers almost every expert of a
+// layer, nothing is fetched on demand; instead, while the GPU computes layer
+// l from one buffer, a dedicated transfer stream loads the complete expert
+// set of layer l+1 into the other buffer, and the buffers swap roles. The
+// mechanism attribution reports the result as transfer-bound (one pass of the
+// expert pool over the host link per prompt chunk).
+//
+// Compute per layer: route every token (top-k, softmax over the selected k),
+// a stable counting sort of the (token, j) pairs by expert, a grouped
+// SwiGLU GEMM on bf16 matrix cores (v_mfma_f32_16x16x32_bf16; 64x64 block
+// tiles, gate and up sharing the A tile), a grouped down-projection GEMM, and
+// the exact merge out[t] = sum_j w[t,j] y[t,j] in j order.
+#include "prefill.h"
+
+namespace ec {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+
+constexpr int BM = 64, BN = 64, BK = 64, LDSP = BK + 8; // LDS row pitch in bf16 elements
+
+void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---- grouping ---------------------------------------------------------------
+__global__ void count_kernel(const int32_t* ids, int n, int32_t* cnt) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) atomicAdd(&cnt[ids[i]], 1);
+}
+
+// off[e] = rows before expert e; toff[e] = 64-row tiles before expert e
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* cnt, int E, int32_t* off, int32_t* toff) {
+    __shared__ int s_w[16][2];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int c[4], tl[4], sc = 0, st = 0;
+    for (int q = 0; q < 4; ++q) {
+        int e = t * 4 + q;
+        c[q] = e < E ? cnt[e] : 0;
+        tl[q] = (c[q] + BM - 1) / BM;
+        sc += c[q];
+        st += tl[q];
+    }
+    int ic = sc, it = st;
+    for (int o = 1; o < 64; o <<= 1) {
+        int a = __shfl_up(ic, o), b = __shfl_up(it, o);
+        if (lane >= o) { ic += a; it += b; }
+    }
+    if (lane == 63) { s_w[wave][0] = ic; s_w[wave][1] = it; }
+    __syncthreads();
+    int pc = 0, pt = 0, tc = 0, tt = 0;
+    for (int w2 = 0; w2 < 16; ++w2) {
+        if (w2 < wave) { pc += s_w[w2][0]; pt += s_w[w2][1]; }
+        tc += s_w[w2][0];
+        tt += s_w[w2][1];
+    }
+    int rc = pc + ic - sc, rt = pt + it - st;
+    for (int q = 0; q < 4; ++q) {
+        int e = t * 4 + q;
+        if (e < E) { off[e] = rc; toff[e] = rt; }
+        rc += c[q];
+        rt += tl[q];
+    }
+    if (t == 0) { off[E] = tc; toff[E] = tt; }
+}
+
+// block e: stable compaction of the pairs routed to expert e
+__global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int n, const int32_t* off, int32_t* perm) {
+    __shared__ int s_w[4];
+    const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int base = off[e];
+    for (int i0 = 0; i0 < n; i0 += 256) {
+        const int i = i0 + threadIdx.x;
+        const bool f = i < n && ids[i] == e;
+        const uint64_t b = __ballot(f);
+        if (lane == 0) s_w[wave] = __popcll(b);
+        __syncthreads();
+        int pre = 0, tot = 0;
+        for (int w2 = 0; w2 < 4; ++w2) { pre += w2 < wave ? s_w[w2] : 0; tot += s_w[w2]; }
+        if (f) perm[base + pre + __popcll(b & ((1ull << lane) - 1ull))] = i;
+        base += tot;
+        __syncthreads();
+    }
+}
+
+// ---- grouped GEMM -------------------------------------------------------------
+// Expert e of tile tt (toff[e] <= tt < toff[e+1]).
+__device__ __forceinline__ int tile_expert(const int32_t* toff, int E, int tt) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (toff[mid] <= tt) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// B tile rows [n0, n0+64) x cols [k0, k0+64) of a [N][K] weight matrix, as 2
+// 16-byte chunks per thread (bf16 source), or decoded from MXFP4.
+template <int WDT>
+__device__ __forceinline__ void load_b(const uint8_t* W, const uint8_t* Ws, int K, int n0, int k0, uint4 (&r)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = threadIdx.x + 256 * q, row = c >> 3, col = (c & 7) * 8;
+        if constexpr (WDT == EC_DT_BF16) {
+            r[q] = *reinterpret_cast<const uint4*>(W + ((uint64_t)(n0 + row) * K + k0 + col) * 2);
+        } else {
+            // 8 MXFP4 elements (4 bytes) -> 8 bf16, exact (E2M1 x 2^(s-127) fits bf16)
+            const uint32_t codes = *reinterpret_cast<const uint32_t*>(W + ((uint64_t)(n0 + row) * K + k0 + col) / 2);
+            const uint32_t se = Ws[(uint64_t)(n0 + row) * (K / 32) + (k0 + col) / 32];
+            const float sc = se ? __uint_as_float(se << 23) : __uint_as_float(0x00400000u);
+            f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, sc, 0);
+            f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, sc, 1);
+            f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, sc, 2);
+            f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, sc, 3);
+            r[q].x = (__float_as_uint(p0.x) >> 16) | (__float_as_uint(p0.y) & 0xffff0000u);
+            r[q].y = (__float_as_uint(p1.x) >> 16) | (__float_as_uint(p1.y) & 0xffff0000u);
+            r[q].z = (__float_as_uint(p2.x) >> 16) | (__float_as_uint(p2.y) & 0xffff0000u);
+            r[q].w = (__float_as_uint(p3.x) >> 16) | (__float_as_uint(p3.y) & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ void store_lds(uint16_t* lds, const uint4 (&r)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = threadIdx.x + 256 * q, row = c >> 3, col = (c & 7) * 8;
+        *reinterpret_cast<uint4*>(lds + row * LDSP + col) = r[q];
+    }
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int col) {
+    uint4 u = *reinterpret_cast<const uint4*>(lds + row * LDSP + col);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+struct GemmArgs {
+    const uint8_t* wbuf;   // full-layer expert buffer
+    uint64_t expert_bytes;
+    uint64_t off_a, off_b, off_sa, off_sb; // byte offsets of the B matrices (and MXFP4 scales) in an expert
+    const uint16_t* x;     // GEMM1: [T][H] bf16 tokens
+    const uint16_t* act_in;// GEMM2: [rows][I] bf16
+    uint16_t* act_out;     // GEMM1 output
+    float* y;              // GEMM2 output [pairs][H]
+    const int32_t* cnt;
+    const int32_t* off;
+    const int32_t* toff;
+    const int32_t* perm;
+    int E, k, H, I;
+};
+
+// GEMM1: act[g][n] = silu(X_g . Wg[n]) * (X_g . Wu[n]) for grouped rows g of expert e.
+// GEMM2: y[perm[g]][n] = act[g] . Wd[n].
+template <int WDT, bool FIRST>
+__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
+    constexpr int NB = FIRST ? 2 : 1;
+    __shared__ uint16_t sA[BM * LDSP];
+    __shared__ uint16_t sB[NB][BN * LDSP];
+    const int tt = blockIdx.x;
+    if (tt >= a.toff[a.E]) return;
+    const int e = tile_expert(a.toff, a.E, tt);
+    const int mt = tt - a.toff[e];
+    const int rows = a.cnt[e] - mt * BM;  // valid rows in this tile (>= 1)
+    const int g0 = a.off[e] + mt * BM;    // first grouped row
+    const int n0 = blockIdx.y * BN;
+    const int K = FIRST ? a.H : a.I;
+    const uint8_t* ebase = a.wbuf + (uint64_t)e * a.expert_bytes;
+    const uint8_t* Wm[2] = {ebase + a.off_a, ebase + a.off_b};
+    const uint8_t* Ws[2] = {ebase + a.off_sa, ebase + a.off_sb};
+
+    // A rows this thread loads (2 chunks), clamped to a valid row
+    const uint16_t* arow[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = threadIdx.x + 256 * q, r = c >> 3;
+        const int rr = r < rows ? r : 0;
+        if (FIRST) arow[q] = a.x + (uint64_t)(a.perm[g0 + rr] / a.k) * a.H;
+        else arow[q] = a.act_in + (uint64_t)(g0 + rr) * a.I;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+    f32x4 acc[NB][2][2];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint4 ra[2], rb[NB][2];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = threadIdx.x + 256 * q, col = (c & 7) * 8;
+            ra[q] = *reinterpret_cast<const uint4*>(arow[q] + k0 + col);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) load_b<WDT>(Wm[b], Ws[b], K, n0, k0, rb[b]);
+    };
+    gload(0);
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        __syncthreads();
+        store_lds(sA, ra);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) store_lds(sB[b], rb[b]);
+        __syncthreads();
+        if (k0 + BK < K) gload(k0 + BK);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 32) {
+            const int kc = kk + (lane >> 4) * 8;
+            bf16x8 fa[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) fa[i] = lds_frag(sA, wm * 32 + i * 16 + (lane & 15), kc);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    bf16x8 fb = lds_frag(sB[b], wn * 32 + j * 16 + (lane & 15), kc);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[b][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb, acc[b][i][j], 0, 0, 0);
+                }
+        }
+    }
+    // epilogue: lane holds D[(lane/16)*4 + q][lane%16] of each 16x16 tile
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = wm * 32 + i * 16 + (lane >> 4) * 4 + q;
+                const int n = n0 + wn * 32 + j * 16 + (lane & 15);
+                if (r >= rows) continue;
+                if constexpr (FIRST) {
+                    const float gv = acc[0][i][j][q], uv = acc[1][i][j][q];
+                    a.act_out[(uint64_t)(g0 + r) * a.I + n] = f32_to_bf16_rne(gv / (1.f + expf(-gv)) * uv);
+                } else {
+                    a.y[(uint64_t)a.perm[g0 + r] * a.H + n] = acc[0][i][j][q];
+                }
+            }
+}
+
+// out[t][h] = sum_j w[t,j] * y[t*k+j][h], j in order
+__global__ __launch_bounds__(256) void combine_kernel(const float* y, const float* w, int k, int H, uint16_t* out) {
+    const int t = blockIdx.x, h = blockIdx.y * 256 + threadIdx.x;
+    if (h >= H) return;
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc = fmaf(w[t * k + j], y[((uint64_t)t * k + j) * H + h], acc);
+    out[(uint64_t)t * H + h] = f32_to_bf16_rne(acc);
+}
+
+// ---- host orchestration --------------------------------------------------------
+void prefill_carve(PrefillState& p, Carve& d, int Tp, int E, int k, int H, int I, uint64_t layer_bytes) {
+    p.Tp = Tp;
+    if (Tp <= 0) return;
+    const uint64_t n = (uint64_t)Tp * k;
+    p.buf[0] = d.take<uint8_t>(layer_bytes);
+    p.buf[1] = d.take<uint8_t>(layer_bytes);
+    p.ids = d.take<int32_t>(n);
+    p.w = d.take<float>(n);
+    p.cnt = d.take<int32_t>(E);
+    p.off = d.take<int32_t>(E + 1);
+    p.toff = d.take<int32_t>(E + 1);
+    p.perm = d.take<int32_t>(n);
+    p.act = d.take<uint16_t>(n * I);
+    p.y = d.take<float>(n * H);
+}
+
+hipError_t prefill_init(PrefillState& p) {
+    for (int b = 0; b < 2; ++b) {
+        hipError_t e = hipEventCreateWithFlags(&p.loaded[b], hipEventDisableTiming);
+        if (e != hipSuccess) return e;
+        e = hipEventCreateWithFlags(&p.done[b], hipEventDisableTiming);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+void prefill_reset_device(PrefillState& p, hipStream_t s) { (void)p; (void)s; }
+
+void prefill_destroy(PrefillState& p) {
+    for (int b = 0; b < 2; ++b) {
+        if (p.loaded[b]) (void)hipEventDestroy(p.loaded[b]);
+        if (p.done[b]) (void)hipEventDestroy(p.done[b]);
+    }
+}
+
+static hipError_t upload(PrefillState& p, const PrefillCall& c, int b, int layer) {
+    hipError_t e;
+    if (p.used[b] && (e = hipStreamWaitEvent(c.copy, p.done[b], 0)) != hipSuccess) return e;
+    e = hipMemcpyAsync(p.buf[b], c.host_pool + (uint64_t)layer * c.layer_bytes, c.layer_bytes,
+                       hipMemcpyHostToDevice, c.copy);
+    if (e != hipSuccess) return e;
+    p.buf_layer[b] = layer;
+    return hipEventRecord(p.loaded[b], c.copy);
+}
+
+hipError_t prefill_layer(PrefillState& p, const PrefillCall& c) {
+    hipError_t e;
+    // the buffer holding (or about to hold) this layer
+    int b = p.buf_layer[0] == c.layer ? 0 : p.buf_layer[1] == c.layer ? 1 : -1;
+    if (b < 0) {
+        b = 1 - p.last;
+        if ((e = upload(p, c, b, c.layer)) != hipSuccess) return e;
+    }
+    if ((e = hipStreamWaitEvent(c.compute, p.loaded[b], 0)) != hipSuccess) return e;
+    if (c.overlap) { // full-layer prefetch of the next layer into the other buffer
+        const int nl = (c.layer + 1) % c.L, nb = 1 - b;
+        if (p.buf_layer[nb] != nl && nl != c.layer)
+            if ((e = upload(p, c, nb, nl)) != hipSuccess) return e;
+    }
+    const int n = c.T * c.k;
+    hipStream_t s = c.compute;
+    launch_route(c.logits, c.T, c.E, c.k, p.ids, p.w, s);
+    launch_fill_i32(p.cnt, 0, c.E, s);
+    hipLaunchKernelGGL(count_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p.ids, n, p.cnt);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, p.cnt, c.E, p.off, p.toff);
+    hipLaunchKernelGGL(place_kernel, dim3(c.E), dim3(256), 0, s, p.ids, n, p.off, p.perm);
+    GemmArgs g{};
+    g.wbuf = p.buf[b];
+    g.expert_bytes = c.expert_bytes;
+    const uint64_t hi = (uint64_t)c.H * c.I;
+    if (c.wdtype == EC_DT_MXFP4) {
+        g.off_a = 0; g.off_b = hi / 2; g.off_sa = 3 * hi / 2; g.off_sb = 3 * hi / 2 + hi / 32;
+    } else {
+        g.off_a = 0; g.off_b = hi * 2;
+    }
+    g.x = (const uint16_t*)c.x;
+    g.act_out = p.act;
+    g.act_in = p.act;
+    g.y = p.y;
+    g.cnt = p.cnt; g.off = p.off; g.toff = p.toff; g.perm = p.perm;
+    g.E = c.E; g.k = c.k; g.H = c.H; g.I = c.I;
+    const int max_tiles = (n + BM - 1) / BM + c.E;
+    if (c.wdtype == EC_DT_MXFP4)
+        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_MXFP4, true>), dim3(max_tiles, c.I / BN), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_BF16, true>), dim3(max_tiles, c.I / BN), dim3(256), 0, s, g);
+    GemmArgs g2 = g;
+    if (c.wdtype == EC_DT_MXFP4) {
+        g2.off_a = hi; g2.off_sa = 3 * hi / 2 + 2 * hi / 32;
+        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_MXFP4, false>), dim3(max_tiles, c.H / BN), dim3(256), 0, s, g2);
+    } else {
+        g2.off_a = 4 * hi;
+        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_BF16, false>), dim3(max_tiles, c.H / BN), dim3(256), 0, s, g2);
+    }
+    hipLaunchKernelGGL(combine_kernel, dim3(c.T, (c.H + 255) / 256), dim3(256), 0, s, p.y, p.w, c.k, c.H,
+                       (uint16_t*)c.out);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipEventRecord(p.done[b], s)) != hipSuccess) return e;
+    p.used[b] = true;
+    p.last = b;
+    return hipSuccess;
+}
+
+} // namespace ec

@@ -1,0 +1,167 @@
+"""expert_cache_step on the GPU vs the literal LRU simulator (oracle/lru_sim.py).
+
+Every step of every trace is compared bit-exactly: unique experts, counts
+(h, m, q, host), classes, slots, fills, victims, evicted keys, host list and
+rewritten ids; the residency table and slot keys are compared at the end, and
+the device LRU keys must order the occupied slots exactly as the simulator's
+recency list. Cache control reads no expert bytes, so these traces use the
+workloads' L, E, k, C, K, T and BP:BH with small H = I = 64 experts (the
+decisions do not depend on H, I or the weight dtype).
+"""
+import numpy as np
+import pytest
+
+import gen
+from gen.configs import BF16, DSV4_DECODE, QWEN_DECODE, STRESS, TINY, budget_slots
+from oracle.lru_sim import LRUSim
+from tests.harness import make_ctx, make_pool, route_ids
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(cfg):
+    return cfg.with_(H=64, I=64, wdtype=BF16)
+
+
+def run_trace(cfg, steps, p=None, T=None, C=None, K=None, bp=None, bh=None, rebuild=None, ids_override=None,
+              check_every=1):
+    import torch
+    import expert_cached_decode_amd as EC
+    from expert_cached_decode_amd.binding import memcpy_async
+    T = cfg.T if T is None else T
+    C = cfg.slots if C is None else C
+    K = cfg.K if K is None else K
+    bp = cfg.bp if bp is None else bp
+    bh = cfg.bh if bh is None else bh
+    rebuild = rebuild or {}
+    sc = _small(cfg)
+    pool = make_pool(sc, layer_period=1)
+    ctx = make_ctx(sc, pool, C=C, K=K, bp=bp, bh=bh, T=T)
+    sim = LRUSim(cfg.L, cfg.E, C, ctx.cfg.victim_k or min(64, min(cfg.E, T * cfg.k)), bp, bh)
+    Kc = ctx.cfg.victim_k or min(64, min(cfg.E, T * cfg.k))
+    if ids_override is None:
+        logits = gen.decode_logits(cfg, steps=steps, p=cfg.p if p is None else p, T=T)
+    n = T * cfg.k
+    Umax = min(cfg.E, n)
+    rec = 8 + 5 * Umax + 3 * Kc + n  # ints logged per step
+    log = torch.empty((steps * cfg.L, rec), dtype=torch.int32, device="cuda")
+    ids_dev = torch.empty((steps * cfg.L, T, cfg.k), dtype=torch.int32, device="cuda")
+    all_ids = []
+    for s in range(steps):
+        for l in range(cfg.L):
+            ids = ids_override(s, l) if ids_override else route_ids(logits[s, l], cfg.k)
+            all_ids.append(ids)
+    ids_dev.copy_(torch.from_numpy(np.stack(all_ids)))
+    results = []
+    i = 0
+    for s in range(steps):
+        if s in rebuild:
+            torch.cuda.synchronize()
+            newC = ctx.rebuild(rebuild[s])
+            sim.rebuild(newC)
+        for l in range(cfg.L):
+            v = EC.expert_cache_step(ctx, l, ids_dev[i], T)
+            row = log[i]
+            o = 0
+            for ptr, cnt in ((v.counts, 8), (v.uniq, Umax), (v.cls, Umax), (v.slot, Umax), (v.fills, Kc),
+                             (v.victims, Kc), (v.evicted, Kc), (v.host_list, Umax), (v.rewritten, n)):
+                memcpy_async(row.data_ptr() + 4 * o, ptr, 4 * cnt)
+                o += cnt
+            results.append(sim.step(l, all_ids[i].tolist()))
+            i += 1
+    torch.cuda.synchronize()
+    got = log.cpu().numpy()
+    for i, r in enumerate(results):
+        g = got[i]
+        U = len(r["uniq"])
+        o = 8
+        cnt = list(g[:6])
+        assert cnt == [U, r["h"], r["m"], r["q"], r["nhost"], r["h"] + r["q"]], (i, cnt, r)
+        uniq = list(g[o:o + U]); o += Umax
+        cls = list(g[o:o + U]); o += Umax
+        slot = list(g[o:o + U]); o += Umax
+        fills = list(g[o:o + r["q"]]); o += Kc
+        victims = list(g[o:o + r["q"]]); o += Kc
+        evicted = list(g[o:o + r["q"]]); o += Kc
+        host = list(g[o:o + r["nhost"]]); o += Umax
+        rew = list(g[o:o + n])
+        assert uniq == r["uniq"], i
+        assert cls == r["cls"], i
+        assert slot == r["slot"], i
+        assert fills == r["fills"], i
+        assert victims == r["victims"], (i, victims, r["victims"])
+        assert evicted == [-1 if e is None else e[0] * cfg.E + e[1] for e in r["evicted"]], i
+        assert host == r["host_list"], i
+        assert rew == [x for row in r["rewritten"] for x in row], i
+    resid, sk, lru, clk = ctx.debug_state()
+    sresid, ssk = sim.state_arrays()
+    assert list(resid) == sresid and list(sk) == ssk
+    assert clk == steps * cfg.L
+    occupied = [s for s in range(len(sk)) if sk[s] >= 0]
+    assert [s for s in sorted(occupied, key=lambda s: int(lru[s]))] == list(sim.recency.keys())
+    assert all(int(lru[s]) == s for s in range(len(sk)) if sk[s] < 0)
+    st = ctx.stats()
+    assert st["device_error"] == 0
+    assert st["hits"] == sum(r["h"] for r in results) and st["fills"] == sum(r["q"] for r in results)
+    ctx.close()
+    return results
+
+
+def test_tiny_trace():
+    res = run_trace(TINY, TINY.steps)
+    assert sum(r["nhost"] for r in res) > 0 and sum(r["q"] for r in res) > 0
+
+
+def test_qwen_decode_full_trace():
+    res = run_trace(QWEN_DECODE, QWEN_DECODE.steps)
+    assert all(r["nhost"] == 0 for r in res)  # BP = BH: every miss is filled
+
+
+@pytest.mark.parametrize("bp,steps", [(300, 1024), (1000, 256), (2000, 256)])
+def test_dsv4_decode_ratios(bp, steps):
+    res = run_trace(DSV4_DECODE, steps, bp=bp, bh=1000)
+    if bp >= 1000:
+        assert all(r["q"] == r["m"] for r in res)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.9])
+def test_stress_batch16_k64(p):
+    run_trace(STRESS, 48, p=p, T=16)
+
+
+def test_stress_rebuild_40_15_40():
+    c5 = STRESS.with_(T=1, slots=budget_slots(43, 256, 4000))
+    run_trace(c5, 96, T=1, rebuild={32: 1500, 64: 4000})
+
+
+def test_budget_zero_and_tiny_caches():
+    run_trace(TINY.with_(L=2), 40, C=0)
+    run_trace(TINY.with_(L=2), 40, C=1, K=2, bp=1000, bh=1000)
+    run_trace(TINY.with_(L=3, k=4), 40, T=3, C=5, K=64, bp=700, bh=1000)
+
+
+def test_max_pairs_and_wide_expert_table():
+    cfg = TINY.with_(L=2, E=4096, k=16, slots=300, K=64, T=64, p=0.3)
+    run_trace(cfg, 6)
+
+
+def test_duplicate_ids_in_a_step():
+    cfg = TINY.with_(L=2, E=16, k=3, slots=4, K=3, T=4)
+    rng = np.random.default_rng(9)
+    run_trace(cfg, 30, ids_override=lambda s, l: rng.integers(0, 5, size=(4, 3)).astype(np.int32))
+
+
+def test_invalid_id_sets_device_error():
+    import torch
+    import expert_cached_decode_amd as EC
+    sc = _small(TINY)
+    pool = make_pool(sc)
+    ctx = make_ctx(sc, pool)
+    bad = torch.tensor([[3, 99]], dtype=torch.int32, device="cuda")
+    EC.expert_cache_step(ctx, 0, bad, 1)
+    st = ctx.stats()
+    assert st["device_error"] == 1 and st["steps"] == 0
+    with pytest.raises(EC.ECError):
+        EC.binding.check(EC.lib().ec_get_stats(ctx.handle, EC.binding.ctypes.byref(EC.binding.ec_stats()), 0),
+                         ctx.handle)
+    ctx.close()

@@ -1,0 +1,148 @@
+"""moe_decode_layer on the GPU vs the fp64 oracle MoE layer.
+
+Outputs must be within 1e-2 per-row relative error of the oracle (bf16 and
+MXFP4 weights, fp32 accumulation, bf16 output); fp32 workloads are checked
+to 1e-5. Cache counters must equal the literal LRU simulator's. The layer
+output must not depend on the cache size or on the BP:BH split.
+"""
+import numpy as np
+import pytest
+
+import gen
+from gen.configs import DSV4_DECODE, QWEN_DECODE, STRESS, TINY
+from oracle.lru_sim import LRUSim
+from tests.harness import (empty_out, make_ctx, make_pool, oracle_layer, out_to_host, route_ids, row_rel_err,
+                           x_to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(cfg, ctx, steps, L, T, keep):
+    """Run steps x layers through moe_decode_layer; return {(s, l): out} for keep(s, l)."""
+    import torch
+    import expert_cached_decode_amd as EC
+    logits = gen.decode_logits(cfg, steps=steps, T=T, L=L)
+    lg_dev = torch.from_numpy(logits).cuda()
+    outs = {}
+    out = empty_out(cfg, T)
+    for s in range(steps):
+        for l in range(L):
+            x = gen.decode_x(cfg, s, l, T)
+            xd = x_to_device(cfg, x)
+            EC.moe_decode_layer(ctx, l, xd, lg_dev[s, l], T, out)
+            if keep(s, l):
+                torch.cuda.synchronize()
+                outs[(s, l)] = (out_to_host(cfg, out), x, logits[s, l])
+    torch.cuda.synchronize()
+    return outs, logits
+
+
+def check_against_oracle(cfg, outs, tol, layer_period=0, max_checks=None):
+    worst = 0.0
+    items = sorted(outs.items())
+    if max_checks:
+        items = items[:max_checks]
+    for (s, l), (got, x, lg) in items:
+        ref, _, _ = oracle_layer(cfg, l, x, lg, layer_period=layer_period)
+        e = row_rel_err(got, ref)
+        worst = max(worst, e)
+        assert e <= tol, ((s, l), e)
+    return worst
+
+
+def sim_counts(cfg, logits, L, T, C, K, bp, bh):
+    sim = LRUSim(L, cfg.E, C, K, bp, bh)
+    tot = dict(hits=0, misses=0, fills=0, host=0)
+    for s in range(logits.shape[0]):
+        for l in range(L):
+            r = sim.step(l, route_ids(logits[s, l], cfg.k).tolist())
+            tot["hits"] += r["h"]; tot["misses"] += r["m"]; tot["fills"] += r["q"]; tot["host"] += r["nhost"]
+    return tot
+
+
+def test_tiny_all_steps():
+    pool = make_pool(TINY)
+    ctx = make_ctx(TINY, pool)
+    outs, logits = run_decode(TINY, ctx, TINY.steps, TINY.L, 1, lambda s, l: True)
+    worst = check_against_oracle(TINY, outs, 1e-5)
+    st = ctx.stats()
+    ref = sim_counts(TINY, logits, TINY.L, 1, TINY.slots, TINY.K, TINY.bp, TINY.bh)
+    assert {k: st[k] for k in ref} == ref
+    assert ref["host"] > 0 and ref["fills"] > 0  # both sides of the split were exercised
+    print("tiny worst row error", worst)
+    ctx.close()
+
+
+def test_qwen_shapes_two_layers():
+    cfg = QWEN_DECODE.with_(L=2, slots=64)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool)
+    outs, logits = run_decode(cfg, ctx, 24, 2, 1, lambda s, l: s % 3 == 0)
+    check_against_oracle(cfg, outs, 1e-2)
+    st = ctx.stats()
+    ref = sim_counts(cfg, logits, 2, 1, 64, cfg.K, cfg.bp, cfg.bh)
+    assert {k: st[k] for k in ref} == ref
+    ctx.close()
+
+
+@pytest.mark.parametrize("split", [(300, 1000, 40), (1000, 1000, 40), (2000, 1000, 40), (300, 1000, 0),
+                                   (1000, 1000, 1024)])
+def test_output_independent_of_split_and_capacity(split):
+    """Same inputs, different BP:BH and cache sizes: outputs agree with the oracle (and so with each other)."""
+    bp, bh, C = split
+    cfg = QWEN_DECODE.with_(L=4, slots=C, bp=bp, bh=bh, K=8)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool)
+    outs, logits = run_decode(cfg, ctx, 12, 4, 1, lambda s, l: s in (0, 5, 11) and l in (0, 3))
+    check_against_oracle(cfg, outs, 1e-2)
+    st = ctx.stats()
+    ref = sim_counts(cfg, logits, 4, 1, C, 8, bp, bh)
+    assert {k: st[k] for k in ref} == ref
+    ctx.close()
+
+
+def test_mxfp4_host_split_ratios():
+    cfg = DSV4_DECODE.with_(L=3, slots=192)
+    pool = make_pool(cfg)
+    res = {}
+    for bp in (300, 1000, 2000):
+        ctx = make_ctx(cfg, pool, bp=bp, bh=1000)
+        outs, logits = run_decode(cfg, ctx, 6, 3, 1, lambda s, l: s in (1, 5))
+        res[bp] = outs
+        st = ctx.stats()
+        ref = sim_counts(cfg, logits, 3, 1, 192, cfg.K, bp, 1000)
+        assert {k: st[k] for k in ref} == ref
+        if bp == 300:
+            assert ref["host"] > 0
+        ctx.close()
+    check_against_oracle(cfg, res[300], 1e-2)
+    for bp in (1000, 2000):
+        for key in res[300]:
+            assert row_rel_err(res[bp][key][0], res[300][key][0]) <= 2e-2
+
+
+def test_batch16_mxfp4():
+    cfg = STRESS.with_(L=2, slots=256, K=64, T=16)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool, bp=500, bh=1000)
+    outs, logits = run_decode(cfg, ctx, 3, 2, 16, lambda s, l: s == 2)
+    for (s, l), (got, x, lg) in outs.items():
+        toks = [0, 7, 15]
+        ref, _, _ = oracle_layer(cfg, l, x, lg, tokens=toks)
+        assert row_rel_err(got[toks], ref) <= 1e-2
+    ctx.close()
+
+
+@pytest.mark.slow
+def test_qwen_decode_full_size_sampled():
+    """The full bf16 workload (40 layers, 64.4 GB pinned expert bank, 3072 slots) on sampled outputs."""
+    cfg = QWEN_DECODE
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool)
+    steps = 48
+    outs, logits = run_decode(cfg, ctx, steps, cfg.L, 1, lambda s, l: (s * 7 + l) % 97 == 0)
+    check_against_oracle(cfg, outs, 1e-2, max_checks=12)
+    st = ctx.stats()
+    ref = sim_counts(cfg, logits, cfg.L, 1, cfg.slots, cfg.K, cfg.bp, cfg.bh)
+    assert {k: st[k] for k in ref} == ref
+    ctx.close()
