@@ -1,0 +1,279 @@
+"""Benchmark: one MoE layer step with a GPU expert cache on one MI355X.
+
+A step is one batch-1 decode token through all 40 MoE layers of the
+Qwen3.6-35B-A3B-shaped workload (E = 256, top-8, H = 2048, I = 512, bf16
+experts, 64.4 GB pinned expert bank, 3072-slot shared LRU cache, routing with
+60% step-to-step overlap, BP:BH = 1000:1000), i.e. route -> cache control ->
+fill -> grouped SwiGLU GEMV -> exact merge, per layer, captured in one
+hipGraph per token. Inputs (router logits and layer inputs for every step)
+are resident in HBM before the timed region.
+
+Also measured in the same run: the expert GEMV's HBM roofline (event-timed
+kernels), prefill seconds per 8192-token chunk with full-layer double
+buffering against the measured host-link bound, and the CPU oracle on a
+bounded sample (cpu_baseline). Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--eager", action="store_true", help="no graph capture")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--timing-steps", type=int, default=64)
+    ap.add_argument("--prefill-chunks", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gen
+    from gen.configs import QWEN_DECODE, QWEN_PREFILL
+    import expert_cached_decode_amd as EC
+
+    cfg = QWEN_DECODE
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+    total_steps = W + K + args.timing_steps
+
+    t0 = time.time()
+    pool = EC.PinnedBuffer(cfg.L * cfg.E * cfg.expert_bytes)
+    gen.fill_pool_ptr(cfg, pool.ptr, 0, cfg.L)
+    log("expert bank %.1f GB pinned and drawn in %.1f s" % (pool.nbytes / 1e9, time.time() - t0))
+
+    prefill_T = 0 if args.no_prefill else QWEN_PREFILL.T
+    ctx = EC.Context(cfg.L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype, max_tokens=1, cache_slots=cfg.slots,
+                     victim_k=cfg.K, bp=cfg.bp, bh=cfg.bh, host_pool=pool, prefill_max_tokens=prefill_T)
+
+    # inputs resident in HBM
+    t0 = time.time()
+    logits = torch.from_numpy(gen.decode_logits(cfg, steps=total_steps)).cuda()  # [S, L, 1, E]
+    xs = torch.empty((total_steps, cfg.L, 1, cfg.H), dtype=torch.int16, device="cuda")
+    for s in range(total_steps):
+        xs[s].copy_(torch.from_numpy(np.stack([gen.decode_x(cfg, s, l) for l in range(cfg.L)]).view(np.int16)))
+    log("decode inputs for %d steps generated in %.1f s" % (total_steps, time.time() - t0))
+
+    stream = torch.cuda.current_stream()
+    x_stage = torch.empty((cfg.L, 1, cfg.H), dtype=torch.int16, device="cuda")
+    lg_stage = torch.empty((cfg.L, 1, cfg.E), dtype=torch.float32, device="cuda")
+    outs = torch.empty((cfg.L, 1, cfg.H), dtype=torch.int16, device="cuda")
+
+    def token_layers(xsrc, lsrc):
+        for l in range(cfg.L):
+            EC.moe_decode_layer(ctx, l, xsrc[l], lsrc[l], 1, outs[l], stream)
+
+    graph = None
+    if not args.eager:
+        # capture one token (all layers) reading fixed staging buffers
+        x_stage.copy_(xs[0]); lg_stage.copy_(logits[0])
+        torch.cuda.synchronize()
+        # warm the allocator and the first step eagerly, then capture
+        token_layers(x_stage, lg_stage)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        with torch.cuda.graph(graph, stream=side):
+            for l in range(cfg.L):
+                EC.moe_decode_layer(ctx, l, x_stage[l], lg_stage[l], 1, outs[l], side)
+        torch.cuda.synchronize()
+        # the eager warm step and the capture did not run the graph; restart from a cold cache
+        ctx.rebuild(3000)
+        torch.cuda.synchronize()
+
+    def run_step(s):
+        if graph is not None:
+            x_stage.copy_(xs[s]); lg_stage.copy_(logits[s])
+            graph.replay()
+        else:
+            token_layers(xs[s], logits[s])
+
+    for s in range(W):
+        run_step(s)
+    torch.cuda.synchronize()
+    ctx.stats(reset=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    t_wall = time.time()
+    for s in range(W, W + K):
+        run_step(s)
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.time() - t_wall
+    ms_total = e0.elapsed_time(e1)
+    st = ctx.stats(reset=True)
+    ms_per_step = ms_total / K
+    tok_s = 1000.0 / ms_per_step
+    lookups = st["hits"] + st["misses"]
+    log("decode: %d steps in %.3f s (wall %.3f s): %.2f tok/s; miss rate %.3f, fills/token %.2f"
+        % (K, ms_total / 1e3, t_wall, tok_s, st["misses"] / max(lookups, 1), st["fills"] / K))
+
+    # kernel timing pass (eager, event-bracketed kernels), continuing the same workload
+    ctx.kernel_timing(True)
+    for s in range(W + K, total_steps):
+        token_layers(xs[s], logits[s])
+    torch.cuda.synchronize()
+    st2 = ctx.stats(reset=True)
+    kt = {k: ctx.kernel_time(k) for k in ("ctl", "fill", "gate_up", "down")}
+    ctx.kernel_timing(False)
+    n_launch = kt["gate_up"][1]
+    side_experts = st2["hits"] + st2["fills"]  # cache-side experts over the pass = sum of n_gpu per launch
+    gu_bytes = side_experts * 2 * cfg.I * cfg.H * 2 / max(n_launch, 1)
+    dn_bytes = side_experts * cfg.H * cfg.I * 2 / max(n_launch, 1)
+    gu_us = kt["gate_up"][0] * 1e3 / max(n_launch, 1)
+    dn_us = kt["down"][0] * 1e3 / max(kt["down"][1], 1)
+    gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
+    dn_gbs = dn_bytes / (dn_us * 1e-6) / 1e9
+    fill_ms, fill_n = kt["fill"]
+    fill_gbs = st2["fills"] * cfg.expert_bytes / max(fill_ms * 1e-3, 1e-9) / 1e9
+    log("gate/up GEMV %.2f us/launch, %.1f MB -> %.0f GB/s; down %.2f us, %.1f MB -> %.0f GB/s; ctl %.2f us; "
+        "fill %.0f GB/s over the link"
+        % (gu_us, gu_bytes / 1e6, gu_gbs, dn_us, dn_bytes / 1e6, dn_gbs, kt["ctl"][0] * 1e3 / max(kt["ctl"][1], 1),
+           fill_gbs))
+
+    result = {
+        "metric": "MoE decode tok/s (batch 1) + % HBM roofline; prefill s per 8192-token chunk",
+        "value": round(tok_s, 3), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen3.6-35B-A3B-shaped MoE decode: 40 layers, 256 experts, top-8, hidden 2048, "
+                               "expert intermediate 512, bf16 experts (64.4 GB pinned bank), shared LRU cache of "
+                               "3072 slots (30%), batch 1, 60% step-to-step routing overlap, BP:BH 1000:1000",
+                   "global_batch": 1, "layers": cfg.L, "cache_slots": cfg.slots,
+                   "graph": graph is not None},
+        "roofline": {"bound": "hbm", "kernel": "gate/up SwiGLU GEMV (gu_kernel)", "achieved": round(gu_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": int(gu_bytes), "us_per_launch": round(gu_us, 3),
+                     "launches": int(n_launch)},
+        "down_kernel": {"achieved": round(dn_gbs, 1), "unit": "GB/s", "frac": round(dn_gbs / HBM_PEAK_GBS, 4),
+                        "bytes_per_launch": int(dn_bytes), "us_per_launch": round(dn_us, 3)},
+        "cache": {"miss_rate": round(st["misses"] / max(lookups, 1), 4), "fills_per_token": round(st["fills"] / K, 3),
+                  "host_per_token": round(st["host"] / K, 3),
+                  "fill_link_GBs": round(fill_gbs, 2)},
+    }
+
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(ctx, cfg, QWEN_PREFILL, args.prefill_chunks)
+    if not args.no_cpu:
+        result["cpu_baseline"] = bench_cpu(cfg, logits.cpu().numpy())
+    ctx.close()
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(ctx, cfg, pcfg, chunks):
+    import torch
+    import gen
+    import expert_cached_decode_amd as EC
+    T = pcfg.T
+    lb = cfg.E * cfg.expert_bytes
+    # measured host-link bound: raw pinned H2D copy of one layer, best of 3
+    dst = torch.empty(lb, dtype=torch.uint8, device="cuda")
+    best = 1e9
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        EC.binding.memcpy_async(dst.data_ptr(), ctx.host_pool.ptr, lb)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del dst
+    link_gbs = lb / (best * 1e-3) / 1e9
+    xs = torch.empty((cfg.L, T, cfg.H), dtype=torch.int16, device="cuda")
+    lgs = torch.empty((cfg.L, T, cfg.E), dtype=torch.float32, device="cuda")
+    for l in range(cfg.L):
+        xs[l].copy_(torch.from_numpy(gen.prefill_x(pcfg, l).view(np.int16)))
+        lgs[l].copy_(torch.from_numpy(gen.prefill_logits(pcfg, l)))
+    out = torch.empty((T, cfg.H), dtype=torch.int16, device="cuda")
+    compute = torch.cuda.current_stream()
+
+    def chunk():
+        for l in range(cfg.L):
+            EC.moe_prefill_layer(ctx, l, xs[l], lgs[l], T, out, compute, ctx.copy_stream)
+
+    times = []
+    ctx.set_prefill_overlap(True)
+    for c in range(chunks + 1):  # the first chunk starts from empty buffers: not counted
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        chunk()
+        b.record()
+        torch.cuda.synchronize()
+        if c > 0:
+            times.append(a.elapsed_time(b) / 1e3)
+    torch.cuda.synchronize()
+    ctx.set_prefill_overlap(False)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    chunk()
+    b.record()
+    torch.cuda.synchronize()
+    t_off = a.elapsed_time(b) / 1e3
+    ctx.set_prefill_overlap(True)
+    s_chunk = float(np.median(times))
+    bound = cfg.L * lb / (link_gbs * 1e9)
+    log("prefill: %.3f s per 8192-token chunk (double buffer off: %.3f s); link bound %.3f s at %.1f GB/s"
+        % (s_chunk, t_off, bound, link_gbs))
+    return {"s_per_chunk": round(s_chunk, 4), "tokens": T, "layers": cfg.L, "chunks_timed": len(times),
+            "bytes_per_chunk": cfg.L * lb, "link_GBs_measured": round(link_gbs, 2),
+            "link_bound_s": round(bound, 4), "ratio_to_link_bound": round(s_chunk / bound, 4),
+            "s_per_chunk_no_double_buffer": round(t_off, 4), "tok_s": round(T / s_chunk, 1)}
+
+
+def bench_cpu(cfg, logits, budget_s=15.0):
+    """The CPU oracle (fp64 plain-loop MoE + literal LRU simulator) on a bounded sample of the same workload."""
+    import gen
+    from oracle import moe
+    from oracle.lru_sim import LRUSim
+    from oracle.route import route_row
+    cores = len(os.sched_getaffinity(0))
+    sim = LRUSim(cfg.L, cfg.E, cfg.slots, cfg.K, cfg.bp, cfg.bh)
+    t_moe = t_lru = 0.0
+    tokens = 0
+    t_start = time.time()
+    while time.time() - t_start < budget_s or tokens == 0:
+        s = tokens
+        for l in range(cfg.L):
+            lg = logits[s, l]                                   # [1, E]
+            x = gen.bf16_to_f32(gen.decode_x(cfg, s, l)).astype(np.float64)
+            routed, _ = route_row(lg[0], cfg.k)
+            mats = {e: gen.expert_logical(cfg, l, e) for e in routed}  # input preparation, not timed
+            t0 = time.time()
+            sim.step(l, [routed])
+            t1 = time.time()
+            moe.moe_tokens(cfg.wdtype, x, lg, cfg.k, mats.__getitem__)
+            t2 = time.time()
+            t_lru += t1 - t0
+            t_moe += t2 - t1
+        tokens += 1
+    sec = t_moe + t_lru
+    log("cpu oracle: %d tokens x %d layers in %.2f s of compute (%.2f s LRU sim) on %d cores"
+        % (tokens, cfg.L, sec, t_lru, cores))
+    return {"value": round(tokens / sec, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": "first %d batch-1 decode tokens x %d layers of the same workload (fp64 C MoE layer with "
+                      "OpenMP over rows, routing and literal LRU simulator in Python; weight generation not timed)"
+                      % (tokens, cfg.L),
+            "lru_sim_s": round(t_lru, 3), "moe_s": round(t_moe, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -54,7 +54,9 @@ class ec_stats(ctypes.Structure):
 _lib = None
 EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec_create", "ec_destroy",
            "ec_set_bandwidth", "moe_route", "expert_cache_step", "moe_decode_layer", "moe_prefill_layer",
-           "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state"]
+           "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
+           "ec_kernel_timing", "ec_kernel_time"]
+KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
 def lib():
@@ -85,6 +87,8 @@ def lib():
         L.ec_epoch.argtypes = [c_vp]
         L.ec_get_stats.argtypes = [c_vp, P(ec_stats), c_i32]
         L.ec_debug_state.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp]
+        L.ec_kernel_timing.argtypes = [c_vp, c_i32]
+        L.ec_kernel_time.argtypes = [c_vp, c_i32, ctypes.POINTER(ctypes.c_double), P(c_u64), c_i32]
         for f in EXPORTS:
             getattr(L, f).restype = getattr(L, f).restype or c_i32
         L.ec_strerror.restype = ctypes.c_char_p
@@ -239,6 +243,16 @@ class Context:
               self.handle)
         self.slot_pool = new_slot_pool
         return C
+
+    def kernel_timing(self, on):
+        check(lib().ec_kernel_timing(self.handle, 1 if on else 0), self.handle)
+
+    def kernel_time(self, kind, reset=False):
+        """(total ms, launches) of one kernel kind ('ctl', 'fill', 'gate_up', 'down')."""
+        ms, n = ctypes.c_double(), c_u64()
+        check(lib().ec_kernel_time(self.handle, KERNEL_KINDS[kind], ctypes.byref(ms), ctypes.byref(n),
+                                   1 if reset else 0), self.handle)
+        return ms.value, n.value
 
     def epoch(self):
         return lib().ec_epoch(self.handle)

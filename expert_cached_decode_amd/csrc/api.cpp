@@ -36,9 +36,7 @@ struct ec_ctx {
     DevState st{};
     StepBufs sb{};
     float* act = nullptr;
-    float* y_gpu = nullptr;
     float* y_host_dev = nullptr;
-    uint32_t* chunk_cnt = nullptr;
     int32_t* mb_pinned = nullptr;
     float* y_host_pinned = nullptr;
     hipStream_t side = nullptr;
@@ -48,8 +46,43 @@ struct ec_ctx {
     HostJob job{};
     PrefillState pf{};
     int prefill_overlap = 1;
+    // kernel timing (measurement support)
+    struct Timer {
+        std::vector<hipEvent_t> ev; // pairs: 2i start, 2i+1 end
+        int used = 0;
+        double total_ms = 0;
+        uint64_t launches = 0;
+    };
+    bool timing = false;
+    Timer timers[4];
     std::string err;
 };
+
+static constexpr int kTimerPairs = 1024;
+
+static void timers_free(ec_ctx* x);
+
+static hipError_t timer_drain(ec_ctx::Timer& t) {
+    for (int i = 0; i < t.used; ++i) {
+        hipError_t e = hipEventSynchronize(t.ev[2 * i + 1]);
+        if (e != hipSuccess) return e;
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]);
+        if (e != hipSuccess) return e;
+        t.total_ms += ms;
+        t.launches++;
+    }
+    t.used = 0;
+    return hipSuccess;
+}
+
+// returns the event pair to bracket the next launch of a kernel kind (nullptr when timing is off)
+static hipEvent_t* timer_next(ec_ctx* x, int kind) {
+    if (!x->timing) return nullptr;
+    ec_ctx::Timer& t = x->timers[kind];
+    if (t.used == kTimerPairs && timer_drain(t) != hipSuccess) return nullptr;
+    return &t.ev[2 * t.used++];
+}
 
 static ec_status fail(ec_ctx* ctx, ec_status s, const std::string& msg) {
     if (ctx) ctx->err = msg;
@@ -159,17 +192,13 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     x->sb.evicted = d.take<int32_t>(kMaxK);
     x->sb.host_list = d.take<int32_t>(U);
     x->sb.rewritten = d.take<int32_t>(n);
-    x->sb.gpu_slot = d.take<int32_t>(U);
-    x->sb.gpu_rank = d.take<int32_t>(U);
-    x->sb.tok_off = d.take<int32_t>(U + 1);
+    x->sb.gpu_desc = d.take<int4>(U);
     x->sb.tok_pairs = d.take<int32_t>(n);
     const uint64_t xbytes = (uint64_t)x->Tmax * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
     const uint64_t mb_bytes = mailbox_ints(n) * 4 + xbytes;
     x->sb.mailbox = d.take<int32_t>((mb_bytes + 3) / 4);
     x->act = d.take<float>((uint64_t)n * x->I);
-    x->y_gpu = d.take<float>((uint64_t)n * x->H);
     x->y_host_dev = d.take<float>((uint64_t)n * x->H);
-    x->chunk_cnt = d.take<uint32_t>((x->H + down_rows_per_chunk() - 1) / down_rows_per_chunk());
     prefill_carve(x->pf, d, x->cfg.prefill_max_tokens, x->E, x->k, x->H, x->I, x->lay.layer_bytes);
     *dev_bytes = (d.off + 255) & ~255ull;
     Carve p(pin);
@@ -263,7 +292,7 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
     launch_fill_i32((int32_t*)x->st.clock, 0, 2, s);
     launch_fill_i32(x->st.err, 0, 1, s);
     launch_fill_i32((int32_t*)x->st.stats, 0, 2ll * x->L * ST_N, s);
-    launch_fill_i32((int32_t*)x->chunk_cnt, 0, (x->H + down_rows_per_chunk() - 1) / down_rows_per_chunk(), s);
+    launch_fill_i32((int32_t*)x->sb.gpu_desc, 0, 4ll * x->Umax, s);
     launch_fill_i32(x->sb.counts, 0, CNT_N, s);
     launch_reset_cache(x->st, x->L, x->E, x->C, s);
     launch_set_bw(x->st.bw, x->bp, x->bh, s);
@@ -285,6 +314,7 @@ ec_status ec_destroy(ec_ctx* x) {
     if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
     (void)hipDeviceSynchronize();
     if (x->pool) host_pool_destroy(x->pool);
+    timers_free(x);
     prefill_destroy(x->pf);
     if (x->ev_ctl) (void)hipEventDestroy(x->ev_ctl);
     if (x->ev_side) (void)hipEventDestroy(x->ev_side);
@@ -376,7 +406,10 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     a.x = xin;
     a.x_bytes = (int32_t)xbytes;
     a.host_branch = x->host_branch ? 1 : 0;
+    hipEvent_t* tm = timer_next(x, 0);
+    if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
     launch_ctl(a, s);
+    if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
     HIPCHK(x, hipGetLastError());
     if (x->host_branch) {
         HIPCHK(x, hipEventRecord(x->ev_ctl, s));
@@ -390,17 +423,64 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     }
     DecodeArgs d{};
     d.pool = x->host_pool_dev; d.slots = x->slot_pool; d.counts = x->sb.counts; d.fills = x->sb.fills;
-    d.victims = x->sb.victims; d.gpu_slot = x->sb.gpu_slot; d.gpu_rank = x->sb.gpu_rank;
-    d.tok_off = x->sb.tok_off; d.tok_pairs = x->sb.tok_pairs; d.rewritten = x->sb.rewritten; d.w = x->sb.w;
-    d.x = xin; d.act = x->act; d.y_gpu = x->y_gpu; d.y_host = x->y_host_dev; d.chunk_cnt = x->chunk_cnt;
+    d.victims = x->sb.victims; d.gpu_desc = x->sb.gpu_desc;
+    d.tok_pairs = x->sb.tok_pairs; d.rewritten = x->sb.rewritten; d.w = x->sb.w;
+    d.x = xin; d.act = x->act; d.y_host = x->y_host_dev;
     d.out = out; d.expert_bytes = x->lay.expert_bytes;
     d.layer = layer; d.E = x->E; d.k = x->k; d.T = T; d.H = x->H; d.I = x->I; d.wdtype = x->wdt; d.U_max = x->Umax;
-    if (x->C > 0) launch_fill(d, x->K, s);
+    if (x->C > 0) {
+        tm = timer_next(x, 1);
+        if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
+        launch_fill(d, x->K, s);
+        if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
+    }
+    tm = timer_next(x, 2);
+    if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
     launch_gu(d, s);
+    if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
     HIPCHK(x, hipGetLastError());
     if (x->host_branch) HIPCHK(x, hipStreamWaitEvent(s, x->ev_side, 0));
+    tm = timer_next(x, 3);
+    if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
     launch_down(d, s);
+    if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
     HIPCHK(x, hipGetLastError());
+    return EC_OK;
+}
+
+static void timers_free(ec_ctx* x) {
+    for (auto& t : x->timers) {
+        for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+        t.ev.clear();
+        t.used = 0;
+    }
+}
+
+ec_status ec_kernel_timing(ec_ctx* x, int32_t on) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    if (on && !x->timing) {
+        for (auto& t : x->timers) {
+            t.ev.resize(2 * kTimerPairs);
+            for (auto& e : t.ev) HIPCHK(x, hipEventCreate(&e));
+            t.used = 0; t.total_ms = 0; t.launches = 0;
+        }
+        x->timing = true;
+    } else if (!on && x->timing) {
+        HIPCHK(x, hipDeviceSynchronize());
+        for (auto& t : x->timers) HIPCHK(x, timer_drain(t));
+        timers_free(x);
+        x->timing = false;
+    }
+    return EC_OK;
+}
+
+ec_status ec_kernel_time(ec_ctx* x, int32_t kind, double* total_ms, uint64_t* launches, int32_t reset) {
+    if (!x || kind < 0 || kind > 3 || !total_ms || !launches) return fail(x, EC_EINVAL, "bad argument");
+    ec_ctx::Timer& t = x->timers[kind];
+    if (x->timing) HIPCHK(x, timer_drain(t));
+    *total_ms = t.total_ms;
+    *launches = t.launches;
+    if (reset) { t.total_ms = 0; t.launches = 0; }
     return EC_OK;
 }
 

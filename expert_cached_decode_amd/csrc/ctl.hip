@@ -28,30 +28,83 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Wave-wide maximum of a 64-bit key through DPP row shifts and row broadcasts
+// (no LDS traffic); the result is returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#define EC_DPP_MAX_STEP(CTRL, RMASK)                                                               \
+    {                                                                                              \
+        const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);                                 \
+        const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, RMASK, 0xf, false);         \
+        const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, RMASK, 0xf, false);         \
+        const uint64_t o = ((uint64_t)ohi << 32) | olo;                                            \
+        v = o > v ? o : v;                                                                         \
+    }
+    EC_DPP_MAX_STEP(0x111, 0xf) // row_shr:1
+    EC_DPP_MAX_STEP(0x112, 0xf) // row_shr:2
+    EC_DPP_MAX_STEP(0x114, 0xf) // row_shr:4
+    EC_DPP_MAX_STEP(0x118, 0xf) // row_shr:8  -> lane 15 of each row holds the row maximum
+    EC_DPP_MAX_STEP(0x142, 0xa) // row_bcast:15 into rows 1 and 3
+    EC_DPP_MAX_STEP(0x143, 0xc) // row_bcast:31 into rows 2 and 3 -> lane 63 holds the maximum
+#undef EC_DPP_MAX_STEP
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Order-preserving key of (logit, expert): larger logit first, then lower id.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+    uint32_t u = __float_as_uint(v + 0.0f); // -0 -> +0: equal logits tie on the id
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+
 // Top-k of one row of E logits by one wavefront: ids by (logit desc, id asc),
-// weights = softmax over the selected logits. ids/w may be global; lds_ids
-// (optional) receives a copy of the ids.
+// weights = softmax over the selected logits. ids/w may be global; lds_ids /
+// lds_w (optional) receive copies. Rows of up to 512 logits are held in
+// registers (8 per lane) so the k selection rounds touch memory once.
 __device__ void wave_topk(const float* row, int E, int k, int32_t* ids, float* w, int32_t* lds_ids,
                           float* lds_w) {
     const int lane = lane_id();
-    uint64_t chosen = 0; // bit i: element lane + 64 i already selected
     float sel_v = 0.f;
     int sel_i = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-        for (int i = 0, e = lane; e < E; ++i, e += 64) {
-            if ((chosen >> i) & 1) continue;
-            float v = row[e];
-            if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
+    if (E <= 512) {
+        uint64_t key[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = lane + 64 * i;
+            key[i] = e < E ? route_key(row[e], e) : 0ull;
         }
-        for (int off = 32; off > 0; off >>= 1) {
-            float ov = __shfl_xor(bv, off);
-            int oi = __shfl_xor(bi, off);
-            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+        for (int j = 0; j < k; ++j) {
+            uint64_t b = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) b = key[i] > b ? key[i] : b;
+            b = wave_max_u64(b);
+            const int e = (int)(0xffffffffu - (uint32_t)b);
+            if ((e & 63) == lane) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (i == (e >> 6)) key[i] = 0ull;
+            }
+            if (lane == j) { sel_i = e; sel_v = row[e]; }
         }
-        if ((bi & 63) == lane) chosen |= 1ull << (bi >> 6);
-        if (lane == j) { sel_v = bv; sel_i = bi; }
+    } else {
+        uint64_t chosen = 0; // bit i: element lane + 64 i already selected
+        for (int j = 0; j < k; ++j) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            for (int i = 0, e = lane; e < E; ++i, e += 64) {
+                if ((chosen >> i) & 1) continue;
+                float v = row[e];
+                if (v > bv || (v == bv && e < bi)) { bv = v; bi = e; }
+            }
+            for (int off = 32; off > 0; off >>= 1) {
+                float ov = __shfl_xor(bv, off);
+                int oi = __shfl_xor(bi, off);
+                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+            }
+            if ((bi & 63) == lane) chosen |= 1ull << (bi >> 6);
+            if (lane == j) { sel_v = bv; sel_i = bi; }
+        }
     }
     const float top = __shfl(sel_v, 0);
     float ex = lane < k ? expf(sel_v - top) : 0.f;
@@ -71,31 +124,51 @@ __global__ __launch_bounds__(256) void route_kernel(const float* logits, int T, 
     wave_topk(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k, nullptr, nullptr);
 }
 
-// Bitonic sort of 64 (key, val) pairs held one per lane, ascending by key.
-__device__ __forceinline__ void sort64(uint64_t& key, int& val) {
-    const int lane = lane_id();
-    for (int kk = 2; kk <= 64; kk <<= 1) {
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-            uint64_t ok = shfl_xor_u64(key, j);
-            int ov = __shfl_xor(val, j);
-            bool want_min = ((lane & j) == 0) == ((lane & kk) == 0);
-            if (want_min ? (ok < key) : (ok > key)) { key = ok; val = ov; }
-        }
+// Wave-wide minimum of a 64-bit key through DPP row shifts and row broadcasts.
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#define EC_DPP_MIN_STEP(CTRL, RMASK)                                                               \
+    {                                                                                              \
+        const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);                                 \
+        const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, RMASK, 0xf, false);         \
+        const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, RMASK, 0xf, false);         \
+        const uint64_t o = ((uint64_t)ohi << 32) | olo;                                            \
+        v = o < v ? o : v;                                                                         \
     }
+    EC_DPP_MIN_STEP(0x111, 0xf)
+    EC_DPP_MIN_STEP(0x112, 0xf)
+    EC_DPP_MIN_STEP(0x114, 0xf)
+    EC_DPP_MIN_STEP(0x118, 0xf)
+    EC_DPP_MIN_STEP(0x142, 0xa)
+    EC_DPP_MIN_STEP(0x143, 0xc)
+#undef EC_DPP_MIN_STEP
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
-// Sort a bitonic sequence of 64 pairs (one per lane) ascending.
-__device__ __forceinline__ void merge64(uint64_t& key, int& val) {
-    const int lane = lane_id();
-    for (int j = 32; j > 0; j >>= 1) {
-        uint64_t ok = shfl_xor_u64(key, j);
-        int ov = __shfl_xor(val, j);
-        if (((lane & j) == 0) ? (ok < key) : (ok > key)) { key = ok; val = ov; }
+// Exclusive block scan of a flag (ballot + popcount; NT threads).
+template <int NT>
+__device__ int block_scan_flag(bool f, int* s_wtot, int* total) {
+    constexpr int kCtlWaves = NT / 64;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint64_t b = __ballot(f);
+    if (lane == 0) s_wtot[wave] = __popcll(b);
+    __syncthreads();
+    int wpre = 0, tot = 0;
+    for (int w2 = 0; w2 < kCtlWaves; ++w2) {
+        const int c = s_wtot[w2];
+        wpre += w2 < wave ? c : 0;
+        tot += c;
     }
+    __syncthreads();
+    *total = tot;
+    return wpre + __popcll(b & ((1ull << lane) - 1ull));
 }
 
-// Exclusive block scan of one int per thread (kCtlThreads threads).
+// Exclusive block scan of one int per thread (NT threads).
+template <int NT>
 __device__ int block_scan(int v, int* s_wtot, int* total) {
+    constexpr int kCtlWaves = NT / 64;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     int incl = v;
     for (int off = 1; off < 64; off <<= 1) {
@@ -115,7 +188,15 @@ __device__ int block_scan(int v, int* s_wtot, int* total) {
     return wpre + incl - v;
 }
 
-__global__ __launch_bounds__(kCtlThreads) void ctl_kernel(CtlArgs a) {
+// NT threads (256 when T*k <= 256: one wavefront per SIMD keeps the VALU cost of
+// this latency-bound kernel low; 1024 otherwise). Each thread holds SR entries
+// of the slot table in registers (slots tid + NT p): 5120 slots; larger tables
+// are re-read from memory in the victim rounds.
+template <int NT>
+__global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
+    constexpr int kCtlThreads = NT;
+    constexpr int kCtlWaves = NT / 64;
+    constexpr int kSlotRegs = 5120 / NT;
     __shared__ int32_t s_ids[kMaxPairs];
     __shared__ float s_w[kMaxPairs];
     __shared__ int32_t s_pos[kMaxPairs];
@@ -124,8 +205,11 @@ __global__ __launch_bounds__(kCtlThreads) void ctl_kernel(CtlArgs a) {
     __shared__ int32_t s_uniq[kMaxPairs];
     __shared__ int32_t s_slot[kMaxPairs];
     __shared__ int32_t s_off[kMaxPairs + 1];
-    __shared__ uint64_t s_ck[kCtlWaves][64];
-    __shared__ int32_t s_cs[kCtlWaves][64];
+    __shared__ int32_t s_first[kMaxPairs];
+    __shared__ int32_t s_g[kMaxPairs];
+    __shared__ uint64_t s_wmin[2][kCtlWaves];
+    __shared__ int32_t s_vslot[kMaxK];
+    __shared__ int32_t s_vocc[kMaxK];
     __shared__ int32_t s_wtot[kCtlWaves];
     __shared__ int32_t s_misc[4];
 
@@ -189,17 +273,26 @@ __global__ __launch_bounds__(kCtlThreads) void ctl_kernel(CtlArgs a) {
     }
     __syncthreads();
 
-    // 3. classify against the shared residency table
+    // 3. one round of global reads: residency of the unique experts, and the
+    //    slot table for the victim scan (LRU key + occupant of each slot)
     const int r = tid;
     const bool valid = r < U;
     const int u = valid ? s_uniq[r] : 0;
     const int sl = valid ? a.st.resid[(int64_t)l * E + u] : -1;
+    uint64_t pk[kSlotRegs];
+    int po[kSlotRegs];
+#pragma unroll
+    for (int p = 0; p < kSlotRegs; ++p) {
+        const int s = tid + kCtlThreads * p;
+        pk[p] = s < C ? a.st.slot_lru[s] : ~0ull;
+        po[p] = s < C ? a.st.slot_key[s] : -1;
+    }
+
+    // 4. classify, fill count q = min(m, floor(m*BP/BH), K, C - h)
     const bool miss = valid && sl < 0;
     int m;
-    const int midx = block_scan(miss ? 1 : 0, s_wtot, &m);
+    const int midx = block_scan_flag<NT>(miss, s_wtot, &m);
     const int h = U - m;
-
-    // 4. fill count q = min(m, floor(m*BP/BH), K, C - h)
     const uint32_t bp = a.st.bw[0], bh = a.st.bw[1];
     int64_t qq = bh ? (int64_t)(((uint64_t)m * bp) / bh) : 0;
     qq = min(qq, (int64_t)m);
@@ -207,50 +300,50 @@ __global__ __launch_bounds__(kCtlThreads) void ctl_kernel(CtlArgs a) {
     qq = min(qq, (int64_t)(C - h));
     const int q = qq > 0 ? (int)qq : 0;
 
-    // 5. single scan: the K oldest slots not hit in this step (empty slots first)
+    // 5. victims: the q oldest slots not hit in this step (empty slots first, in slot
+    //    order), selected from the slot table read once above: q rounds of block-wide
+    //    argmin over the unique LRU keys (each round takes the smallest key above the
+    //    previous one), the owner of each minimum records its slot and occupant.
     if (q > 0) {
-        uint64_t bk = ~0ull;
-        int bs = -1;
-        const int nb = (C + 63) >> 6;
-        for (int b = wave; b < nb; b += kCtlWaves) {
-            int s = b * 64 + lane;
-            uint64_t key = ~0ull;
-            if (s < C) {
-                int sk = a.st.slot_key[s];
-                bool hit_here = false;
-                if (sk >= 0 && sk / E == l) {
-                    int e = sk - l * E;
-                    hit_here = (s_bits[e >> 5] >> (e & 31)) & 1u;
-                }
-                if (!hit_here) key = a.st.slot_lru[s];
-            }
-            uint64_t thr = shfl_u64(bk, 63);
-            if (__ballot(key < thr) == 0) continue;
-            int sv = s;
-            sort64(key, sv);
-            uint64_t rk = shfl_u64(key, 63 - lane);
-            int rs = __shfl(sv, 63 - lane);
-            if (rk < bk) { bk = rk; bs = rs; }
-            merge64(bk, bs);
+#pragma unroll
+        for (int p = 0; p < kSlotRegs; ++p) { // slots hit in this step are not candidates
+            const uint32_t e = (uint32_t)(po[p] - l * E); // occupant in this layer?
+            if (e < (uint32_t)E && ((s_bits[e >> 5] >> (e & 31)) & 1u)) pk[p] = ~0ull;
         }
-        s_ck[wave][lane] = bk;
-        s_cs[wave][lane] = bs;
-        __syncthreads();
-        for (int stride = 1; stride < kCtlWaves; stride <<= 1) {
-            if ((wave % (2 * stride)) == 0 && wave + stride < kCtlWaves) {
-                uint64_t ak = s_ck[wave][lane];
-                int as = s_cs[wave][lane];
-                uint64_t ok = s_ck[wave + stride][63 - lane];
-                int os = s_cs[wave + stride][63 - lane];
-                if (ok < ak) { ak = ok; as = os; }
-                merge64(ak, as);
-                s_ck[wave][lane] = ak;
-                s_cs[wave][lane] = as;
+        // each thread's smallest key (above lo), kept across rounds: only the owner of a
+        // round's minimum has to look again
+        auto local_min = [&](uint64_t lo, uint64_t& mine, int& ms, int& mo) {
+            mine = ~0ull; ms = -1; mo = -1;
+#pragma unroll
+            for (int p = 0; p < kSlotRegs; ++p)
+                if (pk[p] >= lo && pk[p] < mine) { mine = pk[p]; ms = tid + kCtlThreads * p; mo = po[p]; }
+            for (int s = tid + kCtlThreads * kSlotRegs; s < C; s += kCtlThreads) { // tables beyond the registers
+                uint64_t key = a.st.slot_lru[s];
+                const int occ = a.st.slot_key[s];
+                const uint32_t e = (uint32_t)(occ - l * E);
+                if (e < (uint32_t)E && ((s_bits[e >> 5] >> (e & 31)) & 1u)) key = ~0ull;
+                if (key >= lo && key < mine) { mine = key; ms = s; mo = occ; }
             }
+        };
+        uint64_t mine;
+        int ms, mo;
+        local_min(0, mine, ms, mo);
+        for (int rr = 0; rr < q; ++rr) {
+            const uint64_t wm = wave_min_u64(mine);
+            if (lane == 0) s_wmin[rr & 1][wave] = wm;
             __syncthreads();
+            uint64_t gm = ~0ull;
+#pragma unroll
+            for (int w2 = 0; w2 < kCtlWaves; ++w2) gm = s_wmin[rr & 1][w2] < gm ? s_wmin[rr & 1][w2] : gm;
+            if (mine == gm) { // keys are unique: one owner
+                s_vslot[rr] = ms;
+                s_vocc[rr] = mo;
+                local_min(gm + 1, mine, ms, mo);
+            }
         }
+        __syncthreads();
     }
-    if (tid < a.K) a.sb.victims[tid] = (q > 0 && s_ck[0][tid] != ~0ull) ? s_cs[0][tid] : -1;
+    if (tid < a.K) a.sb.victims[tid] = tid < q ? s_vslot[tid] : -1;
     if (tid < a.K && tid >= q) { a.sb.fills[tid] = -1; a.sb.evicted[tid] = -1; }
 
     // 6. assign fills to victims (oldest first), host list, LRU update
@@ -258,8 +351,8 @@ __global__ __launch_bounds__(kCtlThreads) void ctl_kernel(CtlArgs a) {
     if (valid) {
         if (miss) {
             if (midx < q) {
-                const int v = s_cs[0][midx];
-                const int old = a.st.slot_key[v];
+                const int v = s_vslot[midx];
+                const int old = s_vocc[midx];
                 a.sb.evicted[midx] = old;
                 if (old >= 0) { a.st.resid[old] = -1; ev = 1; }
                 a.st.slot_key[v] = l * E + u;
@@ -281,12 +374,12 @@ __global__ __launch_bounds__(kCtlThreads) void ctl_kernel(CtlArgs a) {
         a.sb.slot[r] = slot_r;
     }
     int n_gpu;
-    const int g = block_scan(valid && cls != CLS_HOST ? 1 : 0, s_wtot, &n_gpu);
-    if (valid && cls != CLS_HOST) { a.sb.gpu_slot[g] = slot_r; a.sb.gpu_rank[g] = r; }
+    const int g = block_scan_flag<NT>(valid && cls != CLS_HOST, s_wtot, &n_gpu);
+    if (valid) s_g[r] = cls != CLS_HOST ? g : -1;
     int n_ev;
-    (void)block_scan(ev, s_wtot, &n_ev);
+    (void)block_scan_flag<NT>(ev != 0, s_wtot, &n_ev);
 
-    // 7. rewrite (t, j) -> slot or -(1 + host index); token lists per unique expert
+    // 7. rewrite (t, j) -> slot or -(1 + host index); pair lists per unique expert
     if (tid <= U) s_off[tid] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kCtlThreads) {
@@ -297,16 +390,19 @@ __global__ __launch_bounds__(kCtlThreads) void ctl_kernel(CtlArgs a) {
     __syncthreads();
     int ntot;
     const int cnt = valid ? s_off[r] : 0;
-    const int off = block_scan(cnt, s_wtot, &ntot);
-    if (valid) { s_off[r] = off; a.sb.tok_off[r] = off; }
-    if (tid == 0) a.sb.tok_off[U] = ntot;
+    const int off = block_scan<NT>(cnt, s_wtot, &ntot);
+    if (valid) s_off[r] = off;
     __syncthreads();
     for (int i = tid; i < n; i += kCtlThreads) {
         const int pr = s_pos[i];
         int within = 0;
         for (int i2 = 0; i2 < i; ++i2) within += (s_pos[i2] == pr);
         a.sb.tok_pairs[s_off[pr] + within] = i;
+        if (within == 0) s_first[pr] = i;
     }
+    __syncthreads();
+    // work descriptor of each cache-side expert: slot, first entry in tok_pairs, pair count, first pair
+    if (valid && s_g[r] >= 0) a.sb.gpu_desc[s_g[r]] = make_int4(slot_r, off, cnt, s_first[r]);
 
     // 8. counts, stats, clock; mailbox for the host branch
     if (tid == 0) {
@@ -360,7 +456,8 @@ void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float*
 }
 
 void launch_ctl(const CtlArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(ctl_kernel, dim3(1), dim3(kCtlThreads), 0, s, a);
+    if (a.T * a.k <= 256) hipLaunchKernelGGL(ctl_kernel<256>, dim3(1), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(ctl_kernel<1024>, dim3(1), dim3(1024), 0, s, a);
 }
 
 void launch_set_bw(uint32_t* bw, uint32_t bp, uint32_t bh, hipStream_t s) {

@@ -19,10 +19,9 @@ constexpr int kGuWaves = 4;     // 256 threads
 constexpr int kGuRowsPerWave = 2;
 constexpr int kGuRows = kGuWaves * kGuRowsPerWave;
 constexpr int kDnWaves = 4;
-constexpr int kDnRowsPerWave = 8;
-constexpr int kDnRows = kDnWaves * kDnRowsPerWave; // rows of W_down per block (one chunk)
-
-int down_rows_per_chunk() { return kDnRows; }
+constexpr int kDnRowsPerWave = 2;
+constexpr int kDnRows = kDnWaves * kDnRowsPerWave; // rows of W_down per block
+constexpr int kActLdsMaxFloats = 16384;            // stage act in LDS up to 64 KiB
 
 __device__ __forceinline__ float wave_sum(float v) {
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
@@ -136,18 +135,19 @@ __global__ __launch_bounds__(256) void fill_kernel(DecodeArgs a, int chunks) {
 // ---------------------------------------------------------------------------
 // Gate/up GEMV: for each cache-side expert g and each token routed to it,
 // act[pair][i] = silu(W_gate[i] . x) * (W_up[i] . x), one wavefront per row
-// pair, kGuRowsPerWave rows in flight per wavefront.
+// pair, kGuRowsPerWave row pairs in flight per wavefront. Grid: U_max x
+// (I / kGuRows); blocks past the step's cache-side count exit.
 template <int WDT, int NCH>
 __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
     constexpr int EPC = Fmt<WDT>::EPC;
     const int g = blockIdx.x / chunks, ch = blockIdx.x % chunks;
-    if (g >= a.counts[CNT_GPU]) return;
+    const int n_gpu = a.counts[CNT_GPU];
+    const int4 d = a.gpu_desc[g];
+    if (g >= n_gpu) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H, I = a.I;
     const int rb = row_bytes<WDT>(H), n16 = rb >> 4;
-    const int slot = a.gpu_slot[g], rank = a.gpu_rank[g];
-    const int p0 = a.tok_off[rank], p1 = a.tok_off[rank + 1];
-    const uint8_t* base = a.slots + (uint64_t)slot * a.expert_bytes;
+    const uint8_t* base = a.slots + (uint64_t)d.x * a.expert_bytes;
     const uint8_t* gate = base;
     const uint8_t* up = base + (uint64_t)I * rb;
     const uint8_t* gsc = base + 3ull * I * rb;             // MXFP4 scale rows (H/32 bytes each)
@@ -155,15 +155,9 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
     const int row0 = ch * kGuRows + wave * kGuRowsPerWave;
     const bool xbf16 = WDT != EC_DT_F32;
 
-    for (int pp = p0; pp < p1; ++pp) {
-        const int pair = a.tok_pairs[pp];
+    for (int pi = 0; pi < d.z; ++pi) {
+        const int pair = pi == 0 ? d.w : a.tok_pairs[d.y + pi];
         const int t = pair / a.k;
-        float xv[NCH][EPC];
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const int c = lane + 64 * j;
-            if (c < n16) load_vec<EPC>(a.x, (int64_t)t * H + (int64_t)c * EPC, xbf16, xv[j]);
-        }
         uint4 wg[kGuRowsPerWave][NCH], wu[kGuRowsPerWave][NCH];
         uint32_t sg[kGuRowsPerWave][NCH], su[kGuRowsPerWave][NCH];
 #pragma unroll
@@ -182,6 +176,12 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
                 }
             }
         }
+        float xv[NCH][EPC];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int c = lane + 64 * j;
+            if (c < n16) load_vec<EPC>(a.x, (int64_t)t * H + (int64_t)c * EPC, xbf16, xv[j]);
+        }
 #pragma unroll
         for (int rr = 0; rr < kGuRowsPerWave; ++rr) {
             const int row = row0 + rr;
@@ -197,92 +197,111 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
             accg = wave_sum(accg);
             accu = wave_sum(accu);
             if (lane == 0 && row < I) {
-                const float s = accg / (1.f + expf(-accg));
-                a.act[(int64_t)pair * I + row] = s * accu;
+                const float sv = accg / (1.f + expf(-accg));
+                a.act[(int64_t)pair * I + row] = sv * accu;
             }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Down GEMV + exact merge: y[pair][h] = W_down[h] . act[pair] for cache-side
-// pairs; then the last block to finish each chunk of rows merges
-// out[t][h] = sum_j w[t,j] * y[t,j][h] in j order, reading host-side pairs'
-// partial sums from y_host. Grid: U_max x (H / kDnRows).
+// Down GEMV + exact merge. Each block owns kDnRows output rows and, for every
+// token t, computes y[t,j] = W_down,e(t,j)[row] . act[t,j] for the cache-side
+// pairs (reading host-side pairs' partial sums from y_host) and merges
+// out[t][row] = sum_j w[t,j] * y[t,j][row] in j order. No cross-block
+// communication: the merge happens where the rows are produced.
+// act is staged in LDS when it fits (act_lds_floats > 0).
 template <int WDT, int NCH>
-__global__ __launch_bounds__(256) void down_kernel(DecodeArgs a, int nchunks) {
+__global__ __launch_bounds__(256) void down_kernel(DecodeArgs a, int act_lds_floats) {
     constexpr int EPC = Fmt<WDT>::EPC;
-    __shared__ int s_last;
-    const int g = blockIdx.x / nchunks, ch = blockIdx.x % nchunks;
+    constexpr int G = NCH >= 8 ? 1 : 8 / NCH; // pairs per load group
+    extern __shared__ float s_act[];
+    __shared__ int32_t s_rw[kMaxPairs];
+    __shared__ float s_wt[kMaxPairs];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H, I = a.I;
-    if (g < a.counts[CNT_GPU]) {
-        const int rb = row_bytes<WDT>(I), n16 = rb >> 4;
-        const int slot = a.gpu_slot[g], rank = a.gpu_rank[g];
-        const int p0 = a.tok_off[rank], p1 = a.tok_off[rank + 1];
-        const uint8_t* base = a.slots + (uint64_t)slot * a.expert_bytes;
-        const uint8_t* down = base + 2ull * I * row_bytes<WDT>(H);
-        const uint8_t* dsc = base + 3ull * I * row_bytes<WDT>(H) + 2ull * I * (H / 32);
-        const int row0 = ch * kDnRows + wave * kDnRowsPerWave;
-        for (int pp = p0; pp < p1; ++pp) {
-            const int pair = a.tok_pairs[pp];
-            float av[NCH][EPC];
+    const int H = a.H, I = a.I, k = a.k, T = a.T, n = T * k;
+    for (int i = threadIdx.x; i < n; i += 256) { s_rw[i] = a.rewritten[i]; s_wt[i] = a.w[i]; }
+    if (act_lds_floats > 0) {
+        const float4* src = reinterpret_cast<const float4*>(a.act);
+        float4* dst = reinterpret_cast<float4*>(s_act);
+        for (int i = threadIdx.x; i < act_lds_floats / 4; i += 256) dst[i] = src[i];
+    }
+    __syncthreads();
+    const float* actp = act_lds_floats > 0 ? s_act : a.act;
+    const int rbi = row_bytes<WDT>(I), n16 = rbi >> 4;
+    const uint64_t down_off = 2ull * I * row_bytes<WDT>(H);
+    const uint64_t dsc_off = 3ull * I * row_bytes<WDT>(H) + 2ull * I * (H / 32);
+    const int row0 = blockIdx.x * kDnRows + wave * kDnRowsPerWave;
+    for (int t = 0; t < T; ++t) {
+        float acc[kDnRowsPerWave];
 #pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const int c = lane + 64 * j;
-                if (c < n16) load_vec<EPC>(a.act, (int64_t)pair * I + (int64_t)c * EPC, false, av[j]);
-            }
-            uint4 wd[kDnRowsPerWave][NCH];
-            uint32_t sd[kDnRowsPerWave][NCH];
+        for (int rr = 0; rr < kDnRowsPerWave; ++rr) acc[rr] = 0.f;
+        for (int j0 = 0; j0 < k; j0 += G) {
+            uint4 wd[kDnRowsPerWave][G][NCH];
+            uint32_t sd[kDnRowsPerWave][G][NCH];
 #pragma unroll
-            for (int rr = 0; rr < kDnRowsPerWave; ++rr) {
-                const int row = row0 + rr;
+            for (int jj = 0; jj < G; ++jj) {
+                const int j = j0 + jj;
+                const int rw = j < k ? s_rw[t * k + j] : -1;
+                if (rw < 0) continue;
+                const uint8_t* base = a.slots + (uint64_t)rw * a.expert_bytes;
 #pragma unroll
-                for (int j = 0; j < NCH; ++j) {
-                    const int c = lane + 64 * j;
-                    if (row < H && c < n16) {
-                        wd[rr][j] = reinterpret_cast<const uint4*>(down + (uint64_t)row * rb)[c];
-                        if (WDT == EC_DT_MXFP4) sd[rr][j] = dsc[(uint64_t)row * (I / 32) + c];
+                for (int rr = 0; rr < kDnRowsPerWave; ++rr) {
+                    const int row = row0 + rr;
+#pragma unroll
+                    for (int q = 0; q < NCH; ++q) {
+                        const int c = lane + 64 * q;
+                        if (row < H && c < n16) {
+                            wd[rr][jj][q] = reinterpret_cast<const uint4*>(base + down_off + (uint64_t)row * rbi)[c];
+                            if (WDT == EC_DT_MXFP4) sd[rr][jj][q] = base[dsc_off + (uint64_t)row * (I / 32) + c];
+                        }
                     }
                 }
             }
 #pragma unroll
-            for (int rr = 0; rr < kDnRowsPerWave; ++rr) {
-                const int row = row0 + rr;
-                float acc = 0.f;
+            for (int jj = 0; jj < G; ++jj) {
+                const int j = j0 + jj;
+                if (j >= k) break;
+                const int pair = t * k + j;
+                const int rw = s_rw[pair];
+                if (rw >= 0) {
+                    float av[NCH][EPC];
 #pragma unroll
-                for (int j = 0; j < NCH; ++j) {
-                    const int c = lane + 64 * j;
-                    if (row < H && c < n16)
-                        acc = chunk_dot<WDT>(wd[rr][j], WDT == EC_DT_MXFP4 ? sd[rr][j] : 0u, av[j], acc);
+                    for (int q = 0; q < NCH; ++q) {
+                        const int c = lane + 64 * q;
+                        if (c < n16) load_vec<EPC>(actp, (int64_t)pair * I + (int64_t)c * EPC, false, av[q]);
+                    }
+#pragma unroll
+                    for (int rr = 0; rr < kDnRowsPerWave; ++rr) {
+                        const int row = row0 + rr;
+                        float part = 0.f;
+#pragma unroll
+                        for (int q = 0; q < NCH; ++q) {
+                            const int c = lane + 64 * q;
+                            if (row < H && c < n16)
+                                part = chunk_dot<WDT>(wd[rr][jj][q], WDT == EC_DT_MXFP4 ? sd[rr][jj][q] : 0u, av[q],
+                                                      part);
+                        }
+                        acc[rr] = fmaf(s_wt[pair], wave_sum(part), acc[rr]);
+                    }
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < kDnRowsPerWave; ++rr) {
+                        const int row = row0 + rr;
+                        if (row < H) acc[rr] = fmaf(s_wt[pair], a.y_host[(int64_t)pair * H + row], acc[rr]);
+                    }
                 }
-                acc = wave_sum(acc);
-                if (lane == 0 && row < H) a.y_gpu[(int64_t)pair * H + row] = acc;
             }
         }
-    }
-    // arrival: the last of the U_max blocks of this row chunk merges it
-    __syncthreads();
-    __threadfence();
-    if (threadIdx.x == 0) s_last = atomicAdd(&a.chunk_cnt[ch], 1u) == (unsigned)(a.U_max - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (threadIdx.x == 0) a.chunk_cnt[ch] = 0;
-    const int k = a.k;
-    for (int idx = threadIdx.x; idx < a.T * kDnRows; idx += blockDim.x) {
-        const int t = idx / kDnRows, row = ch * kDnRows + idx % kDnRows;
-        if (row >= H) continue;
-        float acc = 0.f;
-        for (int j = 0; j < k; ++j) {
-            const int pair = t * k + j;
-            const float* yp = a.rewritten[pair] >= 0 ? a.y_gpu : a.y_host;
-            const float y = __hip_atomic_load(yp + (int64_t)pair * H + row, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-            acc = fmaf(a.w[pair], y, acc);
+        if (lane == 0) {
+#pragma unroll
+            for (int rr = 0; rr < kDnRowsPerWave; ++rr) {
+                const int row = row0 + rr;
+                if (row >= H) continue;
+                if (WDT == EC_DT_F32) reinterpret_cast<float*>(a.out)[(int64_t)t * H + row] = acc[rr];
+                else reinterpret_cast<uint16_t*>(a.out)[(int64_t)t * H + row] = f32_to_bf16(acc[rr]);
+            }
         }
-        if (WDT == EC_DT_F32) reinterpret_cast<float*>(a.out)[(int64_t)t * H + row] = acc;
-        else reinterpret_cast<uint16_t*>(a.out)[(int64_t)t * H + row] = f32_to_bf16(acc);
     }
 }
 
@@ -313,11 +332,21 @@ void launch_gu(const DecodeArgs& a, hipStream_t s) {
 }
 
 void launch_down(const DecodeArgs& a, hipStream_t s) {
-    const int nchunks = (a.H + kDnRows - 1) / kDnRows;
-    const dim3 grid(a.U_max * nchunks);
-    if (a.wdtype == EC_DT_F32) { EC_DISPATCH_NCH(down_kernel, EC_DT_F32, nch_for<EC_DT_F32>(a.I), grid, a, nchunks) }
-    else if (a.wdtype == EC_DT_BF16) { EC_DISPATCH_NCH(down_kernel, EC_DT_BF16, nch_for<EC_DT_BF16>(a.I), grid, a, nchunks) }
-    else { EC_DISPATCH_NCH(down_kernel, EC_DT_MXFP4, nch_for<EC_DT_MXFP4>(a.I), grid, a, nchunks) }
+    const dim3 grid((a.H + kDnRows - 1) / kDnRows);
+    const int act_floats = a.T * a.k * a.I;
+    const int lds = act_floats <= kActLdsMaxFloats ? act_floats : 0;
+    const size_t shm = (size_t)lds * 4;
+#define EC_DISPATCH_DOWN(WDT, NCH)                                                                 \
+    switch (NCH) {                                                                                 \
+    case 1: hipLaunchKernelGGL((down_kernel<WDT, 1>), grid, dim3(256), shm, s, a, lds); break;     \
+    case 2: hipLaunchKernelGGL((down_kernel<WDT, 2>), grid, dim3(256), shm, s, a, lds); break;     \
+    case 3: case 4: hipLaunchKernelGGL((down_kernel<WDT, 4>), grid, dim3(256), shm, s, a, lds); break; \
+    default: hipLaunchKernelGGL((down_kernel<WDT, 8>), grid, dim3(256), shm, s, a, lds); break;    \
+    }
+    if (a.wdtype == EC_DT_F32) { EC_DISPATCH_DOWN(EC_DT_F32, nch_for<EC_DT_F32>(a.I)) }
+    else if (a.wdtype == EC_DT_BF16) { EC_DISPATCH_DOWN(EC_DT_BF16, nch_for<EC_DT_BF16>(a.I)) }
+    else { EC_DISPATCH_DOWN(EC_DT_MXFP4, nch_for<EC_DT_MXFP4>(a.I)) }
+#undef EC_DISPATCH_DOWN
 }
 
 } // namespace ec

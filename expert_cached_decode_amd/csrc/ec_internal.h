@@ -25,8 +25,6 @@ constexpr int kMaxPairs = 1024;   // T_max * k
 constexpr int kMaxExperts = 4096; // E
 constexpr int kMaxTopK = 32;
 constexpr int kMaxK = 64;         // victim candidates per step (one wave)
-constexpr int kCtlThreads = 1024; // cache-control workgroup
-constexpr int kCtlWaves = kCtlThreads / 64;
 
 // counts[] layout
 enum { CNT_U = 0, CNT_H = 1, CNT_M = 2, CNT_Q = 3, CNT_HOST = 4, CNT_GPU = 5, CNT_N = 8 };
@@ -62,10 +60,9 @@ struct StepBufs {
     int32_t* evicted;   // [kMaxK]
     int32_t* host_list; // [U_max]
     int32_t* rewritten; // [T_max*k]
-    int32_t* gpu_slot;  // [U_max] cache-side experts, in uniq order
-    int32_t* gpu_rank;  // [U_max] their index into uniq
-    int32_t* tok_off;   // [U_max+1] pairs of uniq rank r: tok_pairs[tok_off[r] .. tok_off[r+1])
-    int32_t* tok_pairs; // [T_max*k] pair index t*k+j, grouped by rank, ascending inside
+    int4* gpu_desc;     // [U_max] cache-side experts in uniq order: {slot, first entry in tok_pairs,
+                        //          number of pairs, first pair}
+    int32_t* tok_pairs; // [T_max*k] pair index t*k+j, grouped by unique expert, ascending inside
     int32_t* mailbox;   // device staging copied to the host for the host branch (layout in host code)
 };
 
@@ -93,17 +90,13 @@ struct DecodeArgs {
     const int32_t* counts;
     const int32_t* fills;
     const int32_t* victims;
-    const int32_t* gpu_slot;
-    const int32_t* gpu_rank;
-    const int32_t* tok_off;
+    const int4* gpu_desc;
     const int32_t* tok_pairs;
     const int32_t* rewritten;
     const float* w;
     const void* x;
     float* act;            // [T_max*k][I]
-    float* y_gpu;          // [T_max*k][H]
     const float* y_host;   // [T_max*k][H] (device copy of host partials)
-    uint32_t* chunk_cnt;   // [H / rows-per-chunk] arrival counters (zero between launches)
     void* out;
     uint64_t expert_bytes;
     int32_t layer, E, k, T, H, I, wdtype, U_max;
@@ -111,6 +104,5 @@ struct DecodeArgs {
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s);
 void launch_gu(const DecodeArgs& a, hipStream_t s);
 void launch_down(const DecodeArgs& a, hipStream_t s);
-int down_rows_per_chunk();
 
 } // namespace ec

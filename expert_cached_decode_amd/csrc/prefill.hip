@@ -306,10 +306,16 @@ static hipError_t upload(PrefillState& p, const PrefillCall& c, int b, int layer
 hipError_t prefill_layer(PrefillState& p, const PrefillCall& c) {
     hipError_t e;
     // the buffer holding (or about to hold) this layer
-    int b = p.buf_layer[0] == c.layer ? 0 : p.buf_layer[1] == c.layer ? 1 : -1;
-    if (b < 0) {
-        b = 1 - p.last;
-        if ((e = upload(p, c, b, c.layer)) != hipSuccess) return e;
+    int b;
+    if (c.overlap) {
+        b = p.buf_layer[0] == c.layer ? 0 : p.buf_layer[1] == c.layer ? 1 : -1;
+        if (b < 0) {
+            b = 1 - p.last;
+            if ((e = upload(p, c, b, c.layer)) != hipSuccess) return e;
+        }
+    } else { // one buffer: each upload waits for the previous layer's compute
+        b = 0;
+        if (p.buf_layer[0] != c.layer && (e = upload(p, c, 0, c.layer)) != hipSuccess) return e;
     }
     if ((e = hipStreamWaitEvent(c.compute, p.loaded[b], 0)) != hipSuccess) return e;
     if (c.overlap) { // full-layer prefetch of the next layer into the other buffer
