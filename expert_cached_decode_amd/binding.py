@@ -56,7 +56,7 @@ EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec
            "ec_set_bandwidth", "moe_route", "expert_cache_step", "moe_decode_layer", "moe_prefill_layer",
            "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
            "ec_kernel_timing", "ec_kernel_time"]
-KERNEL_KINDS = {"ctl": 0, "fill": 1, "gemv": 2, "merge": 3}
+KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
 def lib():
@@ -248,7 +248,7 @@ class Context:
         check(lib().ec_kernel_timing(self.handle, 1 if on else 0), self.handle)
 
     def kernel_time(self, kind, reset=False):
-        """(total ms, launches) of one kernel kind ('ctl', 'fill', 'gemv', 'merge')."""
+        """(total ms, launches) of one kernel kind ('ctl', 'fill', 'gate_up', 'down')."""
         ms, n = ctypes.c_double(), c_u64()
         check(lib().ec_kernel_time(self.handle, KERNEL_KINDS[kind], ctypes.byref(ms), ctypes.byref(n),
                                    1 if reset else 0), self.handle)

@@ -35,8 +35,7 @@ struct ec_ctx {
     uint64_t slot_pool_bytes = 0;
     DevState st{};
     StepBufs sb{};
-    float* part = nullptr;
-    int units_per_block = 16;
+    float* act = nullptr;
     float* y_host_dev = nullptr;
     int32_t* mb_pinned = nullptr;
     float* y_host_pinned = nullptr;
@@ -198,8 +197,7 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     const uint64_t xbytes = (uint64_t)x->Tmax * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
     const uint64_t mb_bytes = mailbox_ints(n) * 4 + xbytes;
     x->sb.mailbox = d.take<int32_t>((mb_bytes + 3) / 4);
-    x->units_per_block = gemv_units_per_block(x->wdt, x->I);
-    x->part = d.take<float>((uint64_t)n * (x->I / x->units_per_block) * x->H);
+    x->act = d.take<float>((uint64_t)n * x->I);
     x->y_host_dev = d.take<float>((uint64_t)n * x->H);
     prefill_carve(x->pf, d, x->cfg.prefill_max_tokens, x->E, x->k, x->H, x->I, x->lay.layer_bytes);
     *dev_bytes = (d.off + 255) & ~255ull;
@@ -427,9 +425,10 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     d.pool = x->host_pool_dev; d.slots = x->slot_pool; d.counts = x->sb.counts; d.fills = x->sb.fills;
     d.victims = x->sb.victims; d.gpu_desc = x->sb.gpu_desc;
     d.tok_pairs = x->sb.tok_pairs; d.rewritten = x->sb.rewritten; d.w = x->sb.w;
-    d.x = xin; d.part = x->part; d.y_host = x->y_host_dev; d.units_per_block = x->units_per_block;
+    d.x = xin; d.act = x->act; d.y_host = x->y_host_dev;
     d.out = out; d.expert_bytes = x->lay.expert_bytes;
     d.layer = layer; d.E = x->E; d.k = x->k; d.T = T; d.H = x->H; d.I = x->I; d.wdtype = x->wdt; d.U_max = x->Umax;
+    d.host_pairs = x->host_branch ? 1 : 0;
     if (x->C > 0) {
         tm = timer_next(x, 1);
         if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
@@ -438,13 +437,13 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     }
     tm = timer_next(x, 2);
     if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
-    launch_gemv(d, s);
+    launch_gu(d, s);
     if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
     HIPCHK(x, hipGetLastError());
     if (x->host_branch) HIPCHK(x, hipStreamWaitEvent(s, x->ev_side, 0));
     tm = timer_next(x, 3);
     if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
-    launch_merge(d, s);
+    launch_down(d, s);
     if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
     HIPCHK(x, hipGetLastError());
     return EC_OK;

@@ -15,7 +15,14 @@ namespace ec {
 
 typedef float f2v __attribute__((ext_vector_type(2)));
 
+constexpr int kGuWaves = 4;     // 256 threads
+constexpr int kGuRowsPerWave = 1;
+constexpr int kGuRows = kGuWaves * kGuRowsPerWave;
 
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -29,6 +36,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // 2^(e - 127) for an E8M0 byte (e = 255 is never produced by a valid bank)
 __device__ __forceinline__ float e8m0_scale(uint32_t e) {
     return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streamed weight chunk: read once per step, so it is loaded non-temporally.
+__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Elements covered by one 16-byte chunk of a weight row.
@@ -121,193 +136,167 @@ __global__ __launch_bounds__(256) void fill_kernel(DecodeArgs a, int chunks) {
     for (; idx < b1; idx += 256) dst[idx] = src[idx];
 }
 
-// Wave-wide sum through DPP row shifts and row broadcasts (fixed order; the
-// result is returned to every lane).
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-#define EC_DPP_ADD_STEP(CTRL, RMASK)                                                                   \
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, RMASK, 0xf, false));
-    EC_DPP_ADD_STEP(0x111, 0xf) // row_shr:1
-    EC_DPP_ADD_STEP(0x112, 0xf) // row_shr:2
-    EC_DPP_ADD_STEP(0x114, 0xf) // row_shr:4
-    EC_DPP_ADD_STEP(0x118, 0xf) // row_shr:8 -> lane 15 of each row holds the row sum
-    EC_DPP_ADD_STEP(0x142, 0xa) // row_bcast:15 into rows 1 and 3
-    EC_DPP_ADD_STEP(0x143, 0xc) // row_bcast:31 into rows 2 and 3 -> lane 63 holds the sum
-#undef EC_DPP_ADD_STEP
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// Add a * (down^T chunk) into the lane's output slice. MXFP4 chunks are decoded
-// unscaled (the per-output scale of the 32-unit group is applied at the end).
-template <int WDT>
-__device__ __forceinline__ void chunk_axpy(uint4 wv, float a, float* y) {
-    if constexpr (WDT == EC_DT_F32) {
-        y[0] = fmaf(a, __uint_as_float(wv.x), y[0]); y[1] = fmaf(a, __uint_as_float(wv.y), y[1]);
-        y[2] = fmaf(a, __uint_as_float(wv.z), y[2]); y[3] = fmaf(a, __uint_as_float(wv.w), y[3]);
-    } else if constexpr (WDT == EC_DT_BF16) {
-        y[0] = fmaf(a, bf16_lo(wv.x), y[0]); y[1] = fmaf(a, bf16_hi(wv.x), y[1]);
-        y[2] = fmaf(a, bf16_lo(wv.y), y[2]); y[3] = fmaf(a, bf16_hi(wv.y), y[3]);
-        y[4] = fmaf(a, bf16_lo(wv.z), y[4]); y[5] = fmaf(a, bf16_hi(wv.z), y[5]);
-        y[6] = fmaf(a, bf16_lo(wv.w), y[6]); y[7] = fmaf(a, bf16_hi(wv.w), y[7]);
-    } else {
-        const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            f2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[q], 1.0f, 0);
-            f2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[q], 1.0f, 1);
-            f2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[q], 1.0f, 2);
-            f2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(words[q], 1.0f, 3);
-            y[q * 8 + 0] = fmaf(a, p0.x, y[q * 8 + 0]); y[q * 8 + 1] = fmaf(a, p0.y, y[q * 8 + 1]);
-            y[q * 8 + 2] = fmaf(a, p1.x, y[q * 8 + 2]); y[q * 8 + 3] = fmaf(a, p1.y, y[q * 8 + 3]);
-            y[q * 8 + 4] = fmaf(a, p2.x, y[q * 8 + 4]); y[q * 8 + 5] = fmaf(a, p2.y, y[q * 8 + 5]);
-            y[q * 8 + 6] = fmaf(a, p3.x, y[q * 8 + 6]); y[q * 8 + 7] = fmaf(a, p3.y, y[q * 8 + 7]);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Expert GEMV (fused gate/up/down): block (g, c) takes cache-side expert g and
-// the R intermediate units [c R, (c+1) R). Each unit i is one row of gate, one
-// of up and one of down^T (each H elements, in that order of the bank), so a
-// wavefront streams 3 rows per unit: a_i = silu(gate_i . x) * (up_i . x), then
-// y += a_i * downT_i over its slice of the H outputs. The block's partial y
-// (summed over its waves in a fixed order) goes to part[pair][c][:]; the merge
-// kernel adds the R-unit partials and merges the experts of each token.
-constexpr int kGvWaves = 4;
-
-template <int WDT, int NCH, int UPW>
-__global__ __launch_bounds__(kGvWaves * 64) void gemv_kernel(DecodeArgs a, int chunks) {
+// Gate/up GEMV: for each cache-side expert g and each token routed to it,
+// act[pair][i] = silu(W_gate[i] . x) * (W_up[i] . x), one wavefront per row
+// pair, kGuRowsPerWave row pairs in flight per wavefront. Grid: U_max x
+// (I / kGuRows); blocks past the step's cache-side count exit.
+template <int WDT, int NCH, bool T1>
+__global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
     constexpr int EPC = Fmt<WDT>::EPC;
-    extern __shared__ float s_y[]; // [kGvWaves][H]
     const int g = blockIdx.x / chunks, ch = blockIdx.x % chunks;
     const int n_gpu = a.counts[CNT_GPU];
     const int4 d = a.gpu_desc[g];
     if (g >= n_gpu) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H, I = a.I, R = a.units_per_block;
+    const int H = a.H, I = a.I;
     const int rb = row_bytes<WDT>(H), n16 = rb >> 4;
     const uint8_t* base = a.slots + (uint64_t)d.x * a.expert_bytes;
     const uint8_t* gate = base;
     const uint8_t* up = base + (uint64_t)I * rb;
-    const uint8_t* down = base + 2ull * I * rb;
-    const uint8_t* gsc = base + 3ull * I * rb;               // MXFP4: [I][H/32]
-    const uint8_t* usc = gsc + (uint64_t)I * (H / 32);        //        [I][H/32]
-    const uint8_t* dsc = gsc + 2ull * I * (H / 32);           //        [I/32][H]
-    const int u0 = ch * R;
-    const int per_wave = R / kGvWaves;
+    const uint8_t* gsc = base + 3ull * I * rb;             // MXFP4 scale rows (H/32 bytes each)
+    const uint8_t* usc = gsc + (uint64_t)I * (H / 32);
+    const int row0 = ch * kGuRows + wave * kGuRowsPerWave;
     const bool xbf16 = WDT != EC_DT_F32;
 
-    for (int pi = 0; pi < d.z; ++pi) {
+    const int np = T1 ? 1 : d.z; // batch 1: one token per expert
+    for (int pi = 0; pi < np; ++pi) {
         const int pair = pi == 0 ? d.w : a.tok_pairs[d.y + pi];
-        const int t = pair / a.k;
-        float xv[NCH][EPC], y[NCH][EPC];
+        const int t = T1 ? 0 : pair / a.k;
+        uint4 wg[kGuRowsPerWave][NCH], wu[kGuRowsPerWave][NCH];
+        uint32_t sg[kGuRowsPerWave][NCH], su[kGuRowsPerWave][NCH];
+#pragma unroll
+        for (int rr = 0; rr < kGuRowsPerWave; ++rr) {
+            const int row = row0 + rr;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const int c = lane + 64 * j;
+                if (row < I && c < n16) {
+                    wg[rr][j] = load_stream(gate + (uint64_t)row * rb + 16ull * c);
+                    wu[rr][j] = load_stream(up + (uint64_t)row * rb + 16ull * c);
+                    if (WDT == EC_DT_MXFP4) {
+                        sg[rr][j] = gsc[(uint64_t)row * (H / 32) + c];
+                        su[rr][j] = usc[(uint64_t)row * (H / 32) + c];
+                    }
+                }
+            }
+        }
+        float xv[NCH][EPC];
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const int c = lane + 64 * j;
             if (c < n16) load_vec<EPC>(a.x, (int64_t)t * H + (int64_t)c * EPC, xbf16, xv[j]);
-#pragma unroll
-            for (int q = 0; q < EPC; ++q) y[j][q] = 0.f;
         }
-        for (int ub = 0; ub < per_wave; ub += UPW) {
-            uint4 wg[UPW][NCH], wu[UPW][NCH], wd[UPW][NCH];
-            uint32_t sg[UPW][NCH], su[UPW][NCH];
 #pragma unroll
-            for (int uu = 0; uu < UPW; ++uu) {
-                const int i = u0 + wave * per_wave + ub + uu;
-#pragma unroll
-                for (int j = 0; j < NCH; ++j) {
-                    const int c = lane + 64 * j;
-                    if (c < n16) {
-                        wg[uu][j] = reinterpret_cast<const uint4*>(gate + (uint64_t)i * rb)[c];
-                        wu[uu][j] = reinterpret_cast<const uint4*>(up + (uint64_t)i * rb)[c];
-                        wd[uu][j] = reinterpret_cast<const uint4*>(down + (uint64_t)i * rb)[c];
-                        if (WDT == EC_DT_MXFP4) {
-                            sg[uu][j] = gsc[(uint64_t)i * (H / 32) + c];
-                            su[uu][j] = usc[(uint64_t)i * (H / 32) + c];
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int uu = 0; uu < UPW; ++uu) {
-                float ag = 0.f, au = 0.f;
-#pragma unroll
-                for (int j = 0; j < NCH; ++j) {
-                    const int c = lane + 64 * j;
-                    if (c < n16) {
-                        ag = chunk_dot<WDT>(wg[uu][j], WDT == EC_DT_MXFP4 ? sg[uu][j] : 0u, xv[j], ag);
-                        au = chunk_dot<WDT>(wu[uu][j], WDT == EC_DT_MXFP4 ? su[uu][j] : 0u, xv[j], au);
-                    }
-                }
-                ag = wave_sum_dpp(ag);
-                au = wave_sum_dpp(au);
-                const float av = ag / (1.f + expf(-ag)) * au;
-#pragma unroll
-                for (int j = 0; j < NCH; ++j)
-                    if (lane + 64 * j < n16) chunk_axpy<WDT>(wd[uu][j], av, y[j]);
-            }
-        }
-        if (WDT == EC_DT_MXFP4) { // apply the down scales of the wave's 32-unit group
+        for (int rr = 0; rr < kGuRowsPerWave; ++rr) {
+            const int row = row0 + rr;
+            float accg = 0.f, accu = 0.f;
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
                 const int c = lane + 64 * j;
-                if (c < n16) {
-                    const uint8_t* sp = dsc + (uint64_t)((u0 + wave * per_wave) / 32) * H + (uint64_t)c * EPC;
-#pragma unroll
-                    for (int q = 0; q < EPC; ++q) y[j][q] *= e8m0_scale(sp[q]);
+                if (row < I && c < n16) {
+                    accg = chunk_dot<WDT>(wg[rr][j], WDT == EC_DT_MXFP4 ? sg[rr][j] : 0u, xv[j], accg);
+                    accu = chunk_dot<WDT>(wu[rr][j], WDT == EC_DT_MXFP4 ? su[rr][j] : 0u, xv[j], accu);
                 }
             }
+            accg = wave_sum(accg);
+            accu = wave_sum(accu);
+            if (lane == 0 && row < I) {
+                const float sv = accg / (1.f + expf(-accg));
+                a.act[(int64_t)pair * I + row] = sv * accu;
+            }
         }
-        // block sum over waves in a fixed order
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const int c = lane + 64 * j;
-            if (c < n16)
-#pragma unroll
-                for (int q = 0; q < EPC; ++q) s_y[wave * H + c * EPC + q] = y[j][q];
-        }
-        __syncthreads();
-        float* dst = a.part + ((int64_t)pair * chunks + ch) * H;
-        for (int h = threadIdx.x; h < H; h += kGvWaves * 64) {
-            float v = s_y[h];
-#pragma unroll
-            for (int w2 = 1; w2 < kGvWaves; ++w2) v += s_y[w2 * H + h];
-            dst[h] = v;
-        }
-        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------
-// Exact merge: out[t][h] = sum_j w[t,j] * y[t,j][h], j in order, where y of a
-// cache-side pair is the fixed-order sum of its R-unit partials and y of a
-// host-side pair is the host partial sum. Block: 64 outputs of one token; wave w
-// sums the partials c = w, w + 4, ...; wave 0 combines.
-__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int chunks) {
-    __shared__ float s_r[4][kMaxTopK][64];
-    const int t = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int h = blockIdx.x * 64 + lane, H = a.H, k = a.k;
-    if (h < H) {
-        for (int j = 0; j < k; ++j) {
-            const int pair = t * k + j;
-            float v = 0.f;
-            if (a.rewritten[pair] >= 0) {
-                const float* p = a.part + (int64_t)pair * chunks * H + h;
-                for (int c = wave; c < chunks; c += 4) v += p[(int64_t)c * H];
+// Down GEMV + exact merge. One wavefront owns one output row h: for every token
+// t it computes y[t,j][h] = W_down,e(t,j)[h] . act[t,j] for the cache-side
+// pairs (the rows of up to 8 experts in flight at once, activation slices in
+// registers) and merges out[t][h] = sum_j w[t,j] y[t,j][h] in j order, taking
+// host-side pairs' partial sums from y_host. No LDS and no cross-block
+// communication; a block is 4 rows. T1: batch-1 specialisation (no token
+// loop); HOST: the step may have host-side pairs (else every pair is cache-side).
+template <int WDT, int NCH, bool HOST>
+__device__ __forceinline__ float down_group(const DecodeArgs& a, int t, int j0, int row, int lane) {
+    constexpr int EPC = Fmt<WDT>::EPC;
+    constexpr int G = 128 / (NCH * EPC) >= 8 ? 8 : (128 / (NCH * EPC) >= 1 ? 128 / (NCH * EPC) : 1);
+    const int H = a.H, I = a.I, k = a.k, last = t * k + k - 1;
+    const int rbi = row_bytes<WDT>(I), n16 = rbi >> 4;
+    const uint64_t down_off = 2ull * I * row_bytes<WDT>(H) + (uint64_t)row * rbi;
+    const uint64_t dsc_off = 3ull * I * row_bytes<WDT>(H) + 2ull * I * (H / 32) + (uint64_t)row * (I / 32);
+    int rw[G], pr[G];
+    float wt[G];
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) { // pairs past k repeat the last pair with weight 0
+        pr[jj] = min(t * k + j0 + jj, last);
+        rw[jj] = a.rewritten[pr[jj]];
+        wt[jj] = a.w[pr[jj]];
+        if (j0 + jj >= k) wt[jj] = 0.f;
+    }
+    // weight rows; a host-side pair reads a dummy row of the activation buffer
+    // (always allocated, larger than one weight row) and is discarded below, so
+    // every load of the group is issued back to back
+    uint4 wd[G][NCH];
+    uint32_t sd[G][NCH];
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+        const uint8_t* base = a.slots + (uint64_t)(HOST && rw[jj] < 0 ? 0 : rw[jj]) * a.expert_bytes;
+        const uint8_t* rowp = base + down_off;
+        const uint8_t* scp = base + dsc_off;
+        if (HOST && rw[jj] < 0) rowp = scp = reinterpret_cast<const uint8_t*>(a.act);
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            const int c = lane + 64 * q;
+            if (c < n16) {
+                wd[jj][q] = load_stream(rowp + 16ull * c);
+                if (WDT == EC_DT_MXFP4) sd[jj][q] = scp[c];
             }
-            s_r[wave][j][lane] = v;
         }
     }
-    __syncthreads();
-    if (wave != 0 || h >= H) return;
+    float av[G][NCH][EPC];
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj)
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            const int c = lane + 64 * q;
+            if (c < n16) load_vec<EPC>(a.act, (int64_t)pr[jj] * I + (int64_t)c * EPC, false, av[jj][q]);
+        }
     float acc = 0.f;
-    for (int j = 0; j < k; ++j) {
-        const int pair = t * k + j;
-        const float y = a.rewritten[pair] >= 0 ? ((s_r[0][j][lane] + s_r[1][j][lane]) + s_r[2][j][lane]) + s_r[3][j][lane]
-                                               : a.y_host[(int64_t)pair * H + h];
-        acc = fmaf(a.w[pair], y, acc);
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+        float part = 0.f;
+#pragma unroll
+        for (int q = 0; q < NCH; ++q)
+            if (lane + 64 * q < n16)
+                part = chunk_dot<WDT>(wd[jj][q], WDT == EC_DT_MXFP4 ? sd[jj][q] : 0u, av[jj][q], part);
+        float y = wave_sum(part);
+        if (HOST) {
+            const float yh = a.y_host[(int64_t)pr[jj] * H + row];
+            y = rw[jj] >= 0 ? y : yh;
+        }
+        acc = fmaf(wt[jj], y, acc);
     }
-    if (a.wdtype == EC_DT_F32) reinterpret_cast<float*>(a.out)[(int64_t)t * H + h] = acc;
-    else reinterpret_cast<uint16_t*>(a.out)[(int64_t)t * H + h] = f32_to_bf16(acc);
+    return acc;
+}
+
+template <int WDT, int NCH, bool T1, bool HOST>
+__global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
+    constexpr int EPC = Fmt<WDT>::EPC;
+    constexpr int G = 128 / (NCH * EPC) >= 8 ? 8 : (128 / (NCH * EPC) >= 1 ? 128 / (NCH * EPC) : 1);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * 4 + wave;
+    if (row >= a.H) return;
+    auto token = [&](int t) {
+        float acc = down_group<WDT, NCH, HOST>(a, t, 0, row, lane);
+        for (int j0 = G; j0 < a.k; j0 += G) acc += down_group<WDT, NCH, HOST>(a, t, j0, row, lane);
+        if (lane == 0) {
+            if (WDT == EC_DT_F32) reinterpret_cast<float*>(a.out)[(int64_t)t * a.H + row] = acc;
+            else reinterpret_cast<uint16_t*>(a.out)[(int64_t)t * a.H + row] = f32_to_bf16(acc);
+        }
+    };
+    if (T1) token(0);
+    else for (int t = 0; t < a.T; ++t) token(t);
 }
 
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s) {
@@ -320,36 +309,56 @@ template <int WDT> static int nch_for(int n) {
     return (rb + 1023) / 1024;
 }
 
-// Units per block: 16 (32 for MXFP4, one scale group of the down projection);
-// doubled while a pair would have more than 64 partials. MXFP4 keeps every
-// wavefront's units inside one 32-unit scale group (R / 4 divides 32).
-int gemv_units_per_block(int wdtype, int I) {
-    int R = wdtype == EC_DT_MXFP4 ? 32 : 16;
-    while (I / R > 64 && R < 128 && I % (2 * R) == 0) R *= 2; // R always divides I (a multiple of 64)
-    return R;
-}
-
-void launch_gemv(const DecodeArgs& a, hipStream_t s) {
-    const int chunks = a.I / a.units_per_block;
-    const dim3 grid(a.U_max * chunks);
-    const size_t shm = (size_t)kGvWaves * a.H * 4;
-#define EC_GEMV(WDT, NCH) hipLaunchKernelGGL((gemv_kernel<WDT, NCH, 2>), grid, dim3(kGvWaves * 64), shm, s, a, chunks)
-#define EC_GEMV_NCH(WDT, N)                                                                        \
-    switch (N) {                                                                                   \
-    case 1: EC_GEMV(WDT, 1); break;                                                                \
-    case 2: EC_GEMV(WDT, 2); break;                                                                \
-    case 3: case 4: EC_GEMV(WDT, 4); break;                                                        \
-    default: EC_GEMV(WDT, 8); break;                                                               \
+#define EC_DISPATCH_NCH(KERNEL, WDT, NCH, GRID, ...)                                              \
+    switch (NCH) {                                                                                \
+    case 1: hipLaunchKernelGGL((KERNEL<WDT, 1>), GRID, dim3(256), 0, s, __VA_ARGS__); break;      \
+    case 2: hipLaunchKernelGGL((KERNEL<WDT, 2>), GRID, dim3(256), 0, s, __VA_ARGS__); break;      \
+    case 3: case 4: hipLaunchKernelGGL((KERNEL<WDT, 4>), GRID, dim3(256), 0, s, __VA_ARGS__); break; \
+    default: hipLaunchKernelGGL((KERNEL<WDT, 8>), GRID, dim3(256), 0, s, __VA_ARGS__); break;     \
     }
-    if (a.wdtype == EC_DT_F32) { EC_GEMV_NCH(EC_DT_F32, nch_for<EC_DT_F32>(a.H)) }
-    else if (a.wdtype == EC_DT_BF16) { EC_GEMV_NCH(EC_DT_BF16, nch_for<EC_DT_BF16>(a.H)) }
-    else { EC_GEMV_NCH(EC_DT_MXFP4, nch_for<EC_DT_MXFP4>(a.H)) }
-#undef EC_GEMV_NCH
-#undef EC_GEMV
+
+void launch_gu(const DecodeArgs& a, hipStream_t s) {
+    const int chunks = (a.I + kGuRows - 1) / kGuRows;
+    const dim3 grid(a.U_max * chunks);
+#define EC_GU(WDT, NCH)                                                                            \
+    do {                                                                                           \
+        if (a.T == 1) hipLaunchKernelGGL((gu_kernel<WDT, NCH, true>), grid, dim3(256), 0, s, a, chunks); \
+        else hipLaunchKernelGGL((gu_kernel<WDT, NCH, false>), grid, dim3(256), 0, s, a, chunks);  \
+    } while (0)
+#define EC_GU_NCH(WDT, N)                                                                          \
+    switch (N) {                                                                                   \
+    case 1: EC_GU(WDT, 1); break;                                                                  \
+    case 2: EC_GU(WDT, 2); break;                                                                  \
+    case 3: case 4: EC_GU(WDT, 4); break;                                                          \
+    default: EC_GU(WDT, 8); break;                                                                 \
+    }
+    if (a.wdtype == EC_DT_F32) { EC_GU_NCH(EC_DT_F32, nch_for<EC_DT_F32>(a.H)) }
+    else if (a.wdtype == EC_DT_BF16) { EC_GU_NCH(EC_DT_BF16, nch_for<EC_DT_BF16>(a.H)) }
+    else { EC_GU_NCH(EC_DT_MXFP4, nch_for<EC_DT_MXFP4>(a.H)) }
+#undef EC_GU_NCH
+#undef EC_GU
 }
 
-void launch_merge(const DecodeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3((a.H + 63) / 64, a.T), dim3(256), 0, s, a, a.I / a.units_per_block);
+void launch_down(const DecodeArgs& a, hipStream_t s) {
+    const dim3 grid((a.H + 3) / 4);
+#define EC_DOWN(WDT, NCH)                                                                          \
+    do {                                                                                           \
+        if (a.T == 1 && !a.host_pairs) hipLaunchKernelGGL((down_kernel<WDT, NCH, true, false>), grid, dim3(256), 0, s, a); \
+        else if (a.T == 1) hipLaunchKernelGGL((down_kernel<WDT, NCH, true, true>), grid, dim3(256), 0, s, a); \
+        else hipLaunchKernelGGL((down_kernel<WDT, NCH, false, true>), grid, dim3(256), 0, s, a);  \
+    } while (0)
+#define EC_DOWN_NCH(WDT, N)                                                                        \
+    switch (N) {                                                                                   \
+    case 1: EC_DOWN(WDT, 1); break;                                                                \
+    case 2: EC_DOWN(WDT, 2); break;                                                                \
+    case 3: case 4: EC_DOWN(WDT, 4); break;                                                        \
+    default: EC_DOWN(WDT, 8); break;                                                               \
+    }
+    if (a.wdtype == EC_DT_F32) { EC_DOWN_NCH(EC_DT_F32, nch_for<EC_DT_F32>(a.I)) }
+    else if (a.wdtype == EC_DT_BF16) { EC_DOWN_NCH(EC_DT_BF16, nch_for<EC_DT_BF16>(a.I)) }
+    else { EC_DOWN_NCH(EC_DT_MXFP4, nch_for<EC_DT_MXFP4>(a.I)) }
+#undef EC_DOWN_NCH
+#undef EC_DOWN
 }
 
 } // namespace ec

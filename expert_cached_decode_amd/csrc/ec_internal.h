@@ -95,15 +95,15 @@ struct DecodeArgs {
     const int32_t* rewritten;
     const float* w;
     const void* x;
-    float* part;           // [T_max*k][I / units_per_block][H] expert-GEMV partial sums
+    float* act;            // [T_max*k][I] SwiGLU activations of cache-side pairs
     const float* y_host;   // [T_max*k][H] (device copy of host partials)
     void* out;
     uint64_t expert_bytes;
-    int32_t layer, E, k, T, H, I, wdtype, U_max, units_per_block;
+    int32_t layer, E, k, T, H, I, wdtype, U_max;
+    int32_t host_pairs; // 1 when the step can have host-side pairs (the host branch is on)
 };
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s);
-void launch_gemv(const DecodeArgs& a, hipStream_t s);
-void launch_merge(const DecodeArgs& a, hipStream_t s);
-int gemv_units_per_block(int wdtype, int I);
+void launch_gu(const DecodeArgs& a, hipStream_t s);
+void launch_down(const DecodeArgs& a, hipStream_t s);
 
 } // namespace ec

@@ -82,12 +82,13 @@ struct HostPool {
     int n1 = 0, n2 = 0;
     std::atomic<int> next1{0}, next2{0}, done1{0}, done2{0}, arrived{0};
     int nworkers = 0;
-    static constexpr int kRows = 64;
+    static constexpr int kRows = 32;
 
     void work() {
         const HostJob& j = *job;
         const int H = j.H, I = j.I;
         const uint64_t rbH = j.wdtype == 0 ? H * 4ull : j.wdtype == 1 ? H * 2ull : H / 2;
+        const uint64_t rbI = j.wdtype == 0 ? I * 4ull : j.wdtype == 1 ? I * 2ull : I / 2;
         // phase 1: gate/up rows -> act
         for (int t; (t = next1.fetch_add(1)) < n1;) {
             const int e = task_expert[t], r0 = task_r0[t];
@@ -107,33 +108,16 @@ struct HostPool {
             done1.fetch_add(1, std::memory_order_release);
         }
         while (done1.load(std::memory_order_acquire) < n1) std::this_thread::yield();
-        // phase 2: outputs h in [r0, r0 + kRows) -> y: sum over units i of act_i * down^T[i][h]
+        // phase 2: down rows -> y
         for (int t; (t = next2.fetch_add(1)) < n2;) {
             const int e = task_expert[n1 + t], r0 = task_r0[n1 + t];
-            const int r1 = r0 + kRows < H ? r0 + kRows : H;
             const uint8_t* base = j.expert_base[e];
             const uint8_t* d = base + 2ull * I * rbH;
-            const uint8_t* dsc = base + 3ull * I * rbH + 2ull * I * (H / 32); // [I/32][H]
-            for (int p : pairs_of[e]) {
-                float acc[kRows] = {0};
-                const float* av = j.act + (uint64_t)p * I;
-                for (int i = 0; i < I; ++i) {
-                    const float a = av[i];
-                    const uint8_t* row = d + (uint64_t)i * rbH;
-                    if (j.wdtype == 0) {
-                        const float* w = reinterpret_cast<const float*>(row);
-                        for (int h = r0; h < r1; ++h) acc[h - r0] += a * w[h];
-                    } else if (j.wdtype == 1) {
-                        const uint16_t* w = reinterpret_cast<const uint16_t*>(row);
-                        for (int h = r0; h < r1; ++h) acc[h - r0] += a * bf16f(w[h]);
-                    } else {
-                        const uint8_t* sc = dsc + (uint64_t)(i / 32) * H;
-                        for (int h = r0; h < r1; ++h)
-                            acc[h - r0] += a * kE2M1[(row[h / 2] >> (4 * (h & 1))) & 15] * e8m0(sc[h]);
-                    }
-                }
-                for (int h = r0; h < r1; ++h) j.y[(uint64_t)p * H + h] = acc[h - r0];
-            }
+            const uint8_t* dsc = base + 3ull * I * rbH + 2ull * I * (H / 32);
+            for (int h = r0; h < r0 + kRows && h < H; ++h)
+                for (int p : pairs_of[e])
+                    j.y[(uint64_t)p * H + h] =
+                        dot_row(j.wdtype, d + h * rbI, dsc + (uint64_t)h * (I / 32), j.act + (uint64_t)p * I, I);
             done2.fetch_add(1, std::memory_order_release);
         }
     }

@@ -129,49 +129,6 @@ __device__ __forceinline__ void load_b(const uint8_t* W, const uint8_t* Ws, int 
     }
 }
 
-// B tile rows [k0, k0+64) x cols [n0, n0+64) of a [K][N] matrix (the stored
-// down^T), as 2 chunks of 8 consecutive n per thread; MXFP4 scales are [K/32][N].
-template <int WDT>
-__device__ __forceinline__ void load_bt(const uint8_t* W, const uint8_t* Ws, int N, int n0, int k0, uint4 (&r)[2]) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int c = threadIdx.x + 256 * q, kr = c >> 3, nc = (c & 7) * 8;
-        const uint64_t e0 = (uint64_t)(k0 + kr) * N + n0 + nc;
-        if constexpr (WDT == EC_DT_BF16) {
-            r[q] = *reinterpret_cast<const uint4*>(W + e0 * 2);
-        } else {
-            const uint32_t codes = *reinterpret_cast<const uint32_t*>(W + e0 / 2);
-            const uint2 sc8 = *reinterpret_cast<const uint2*>(Ws + (uint64_t)((k0 + kr) / 32) * N + n0 + nc);
-            const uint32_t sw[2] = {sc8.x, sc8.y};
-            const f2v p[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0),
-                              __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1),
-                              __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2),
-                              __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3)};
-            uint32_t out[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) { // byte b: elements 2b (low nibble), 2b + 1
-                const uint32_t s0 = (sw[(2 * b) >> 2] >> (8 * ((2 * b) & 3))) & 0xffu;
-                const uint32_t s1 = (sw[(2 * b + 1) >> 2] >> (8 * ((2 * b + 1) & 3))) & 0xffu;
-                const float v0 = p[b].x * (s0 ? __uint_as_float(s0 << 23) : __uint_as_float(0x00400000u));
-                const float v1 = p[b].y * (s1 ? __uint_as_float(s1 << 23) : __uint_as_float(0x00400000u));
-                out[b] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xffff0000u);
-            }
-            r[q] = make_uint4(out[0], out[1], out[2], out[3]);
-        }
-    }
-}
-
-// Store a load_bt tile transposed: lds[n][k].
-__device__ __forceinline__ void store_lds_t(uint16_t* lds, const uint4 (&r)[2]) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int c = threadIdx.x + 256 * q, kr = c >> 3, nc = (c & 7) * 8;
-        const uint32_t w[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lds[(nc + e) * LDSP + kr] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    }
-}
-
 __device__ __forceinline__ void store_lds(uint16_t* lds, const uint4 (&r)[2]) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -201,8 +158,7 @@ struct GemmArgs {
 };
 
 // GEMM1: act[g][n] = silu(X_g . Wg[n]) * (X_g . Wu[n]) for grouped rows g of expert e.
-// GEMM2: y[perm[g]][n] = act[g] . Wd[n] with Wd read from the stored down^T [I][H]
-//        (transposed into LDS on the way in).
+// GEMM2: y[perm[g]][n] = act[g] . Wd[n].
 template <int WDT, bool FIRST>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     constexpr int NB = FIRST ? 2 : 1;
@@ -245,23 +201,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
             const int c = threadIdx.x + 256 * q, col = (c & 7) * 8;
             ra[q] = *reinterpret_cast<const uint4*>(arow[q] + k0 + col);
         }
-        if constexpr (FIRST) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) load_b<WDT>(Wm[b], Ws[b], K, n0, k0, rb[b]);
-        } else {
-            load_bt<WDT>(Wm[0], Ws[0], a.H, n0, k0, rb[0]);
-        }
+        for (int b = 0; b < NB; ++b) load_b<WDT>(Wm[b], Ws[b], K, n0, k0, rb[b]);
     };
     gload(0);
     for (int k0 = 0; k0 < K; k0 += BK) {
         __syncthreads();
         store_lds(sA, ra);
-        if constexpr (FIRST) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) store_lds(sB[b], rb[b]);
-        } else {
-            store_lds_t(sB[0], rb[0]);
-        }
+        for (int b = 0; b < NB; ++b) store_lds(sB[b], rb[b]);
         __syncthreads();
         if (k0 + BK < K) gload(k0 + BK);
 #pragma unroll

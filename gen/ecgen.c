@@ -236,16 +236,12 @@ void ecg_expert_matrix_mxfp4(uint64_t seed, int layer, int expert, int tag, int 
 
 /* ---- packed expert bank -----------------------------------------------------
  * Byte layout of one expert (the library's expert-bank format):
- *   f32 / bf16 : [gate I*H][up I*H][down^T I*H] elements, row-major; gate and up
- *                rows are the logical rows (intermediate unit i), and row i of
- *                down^T holds column i of the logical down matrix (its H outputs).
- *   MXFP4      : [gate codes I*H/2][up codes I*H/2][down^T codes I*H/2]
- *                [gate scales I*H/32][up scales I*H/32][down scales I/32*H]
- *                codes packed two per byte along the stored row, even element in
- *                the low nibble; gate/up scales one byte per 32-element row block;
- *                down scales one byte per (32-unit block of i, output h), stored
- *                [i/32][h] (the blocks run along the down projection's
- *                contraction dimension i).
+ *   f32 / bf16 : [gate I*H][up I*H][down H*I] elements, each matrix row-major
+ *                in its logical orientation.
+ *   MXFP4      : [gate codes I*H/2][up codes I*H/2][down codes H*I/2]
+ *                [gate scales I*H/32][up scales I*H/32][down scales H*I/32]
+ *                codes packed two per byte along the row, even element in
+ *                the low nibble; scales one byte per 32-element row block.
  * The pool is [L][E][expert bytes]. */
 uint64_t ecg_expert_bytes(int dtype, int H, int I) {
     uint64_t n = (uint64_t)H * I;
@@ -260,52 +256,26 @@ static void pack_expert(uint64_t seed, int dtype, int layer, int expert, int H, 
     int maxc = H > I ? H : I;
     double* w = (double*)malloc(sizeof(double) * maxc);
     uint8_t* codes = (uint8_t*)malloc(maxc);
-    uint8_t* prev_codes = (uint8_t*)malloc(maxc);
     for (int tag = 0; tag < 3; ++tag) {
         int rows, cols;
         matrix_dims(tag, H, I, &rows, &cols);
         uint64_t key = ecg_key(seed, tag, layer, expert, 0);
         for (int r = 0; r < rows; ++r) {
             draw_row(key, (uint64_t)r * cols, cols, sigma, w);
-            if (tag < 2) {
-                if (dtype == DT_F32) {
-                    float* o = (float*)(dst + tag * n * 4) + (uint64_t)r * cols;
-                    for (int c = 0; c < cols; ++c) o[c] = (float)w[c];
-                } else if (dtype == DT_BF16) {
-                    uint16_t* o = (uint16_t*)(dst + tag * n * 2) + (uint64_t)r * cols;
-                    for (int c = 0; c < cols; ++c) o[c] = f32_to_bf16_rne((float)w[c]);
-                } else {
-                    uint8_t* prow = dst + tag * (n / 2) + (uint64_t)r * (cols / 2);
-                    uint8_t* ps = dst + 3 * (n / 2) + tag * (n / 32) + (uint64_t)r * (cols / 32);
-                    quant_row_mxfp4(w, cols, codes, ps);
-                    for (int c = 0; c < cols; c += 2) prow[c / 2] = (uint8_t)(codes[c] | (codes[c + 1] << 4));
-                }
+            if (dtype == DT_F32) {
+                float* o = (float*)(dst + tag * n * 4) + (uint64_t)r * cols;
+                for (int c = 0; c < cols; ++c) o[c] = (float)w[c];
+            } else if (dtype == DT_BF16) {
+                uint16_t* o = (uint16_t*)(dst + tag * n * 2) + (uint64_t)r * cols;
+                for (int c = 0; c < cols; ++c) o[c] = f32_to_bf16_rne((float)w[c]);
             } else {
-                /* logical down row r = output h (cols = I); stored transposed: element (i, h) */
-                const int h = r;
-                if (dtype == DT_F32) {
-                    float* o = (float*)(dst + 2 * n * 4);
-                    for (int i = 0; i < cols; ++i) o[(uint64_t)i * H + h] = (float)w[i];
-                } else if (dtype == DT_BF16) {
-                    uint16_t* o = (uint16_t*)(dst + 2 * n * 2);
-                    for (int i = 0; i < cols; ++i) o[(uint64_t)i * H + h] = f32_to_bf16_rne((float)w[i]);
-                } else {
-                    uint8_t* pc = dst + 2 * (n / 2);                   /* [I][H/2] */
-                    uint8_t* ps = dst + 3 * (n / 2) + 2 * (n / 32);    /* [I/32][H] */
-                    uint8_t blk[256]; /* I/32 scale bytes, I <= 8192 */
-                    quant_row_mxfp4(w, cols, codes, blk);
-                    for (int b = 0; b < cols / 32; ++b) ps[(uint64_t)b * H + h] = blk[b];
-                    if (h & 1) { /* pack (h-1, h) for every i */
-                        for (int i = 0; i < cols; ++i)
-                            pc[(uint64_t)i * (H / 2) + h / 2] = (uint8_t)(prev_codes[i] | (codes[i] << 4));
-                    } else {
-                        memcpy(prev_codes, codes, cols);
-                    }
-                }
+                uint8_t* prow = dst + tag * (n / 2) + (uint64_t)r * (cols / 2);
+                uint8_t* ps = dst + 3 * (n / 2) + tag * (n / 32) + (uint64_t)r * (cols / 32);
+                quant_row_mxfp4(w, cols, codes, ps);
+                for (int c = 0; c < cols; c += 2) prow[c / 2] = (uint8_t)(codes[c] | (codes[c + 1] << 4));
             }
         }
     }
-    free(prev_codes);
     free(codes);
     free(w);
 }

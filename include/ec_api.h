@@ -83,16 +83,12 @@ typedef struct ec_shape {
 
 /* Expert-bank byte layout ("expert bank": layer x expert are the leading
  * dimensions). The host pool is [L][E][expert_bytes]; a cache slot holds one
- * expert in the same layout. Logical matrices: gate [I][H], up [I][H], down
- * [H][I]. Stored: gate and up row-major (row i = intermediate unit i) and the
- * transpose of down, down^T [I][H] (row i = the H outputs fed by unit i), so
- * that the three rows of one unit have the same length and shape.
- * f32 / bf16: gate, up, down^T back to back as elements.
- * MXFP4: codes of gate, up, down^T (two per byte along the stored row, even
- * element in the low nibble), then the E8M0 scale bytes: gate and up one per
- * 32 consecutive row elements ([I][H/32] each), down one per 32 consecutive
- * units i for each output h ([I/32][H]; the blocks run along the down
- * projection's contraction dimension). Offsets are bytes from the expert start. */
+ * expert in the same layout. Logical matrices: gate [I][H], up [I][H],
+ * down [H][I], each row-major; the contraction dimension is the row.
+ * f32 / bf16: gate, up, down stored back to back as elements.
+ * MXFP4: codes of gate, up, down (two per byte along the row, even element in
+ * the low nibble), then the E8M0 scale bytes of gate, up, down (one per 32
+ * consecutive row elements). Offsets are in bytes from the expert start. */
 typedef struct ec_layout_info {
     uint64_t expert_bytes;
     uint64_t layer_bytes; /* E * expert_bytes */
@@ -244,8 +240,8 @@ ec_status ec_debug_state(ec_ctx* ctx, int32_t* resid, int32_t* slot_key, uint64_
 /* Kernel timing (measurement support). While on, moe_decode_layer brackets
  * each of its kernels with HIP events recorded on the caller's stream (so a
  * step is then not capturable). Switching on allocates the events; off frees
- * them. Kinds: 0 cache control (route + control), 1 fill, 2 expert GEMV
- * (gate, up and down streamed together), 3 partial-sum merge. */
+ * them. Kinds: 0 cache control (route + control), 1 fill, 2 gate/up GEMV,
+ * 3 down GEMV + exact merge. */
 ec_status ec_kernel_timing(ec_ctx* ctx, int32_t on);
 
 /* Sum of event-measured durations (ms) and number of launches of one kernel
