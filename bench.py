@@ -41,6 +41,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--timing-steps", type=int, default=64)
     ap.add_argument("--prefill-chunks", type=int, default=4)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
@@ -53,6 +55,13 @@ def main():
 
     cfg = QWEN_DECODE
     torch.cuda.set_device(0)
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     K, W = args.steps, args.warmup
     total_steps = W + K + args.timing_steps
 

@@ -462,7 +462,7 @@ ec_status ec_kernel_timing(ec_ctx* x, int32_t on) {
     if (on && !x->timing) {
         for (auto& t : x->timers) {
             t.ev.resize(2 * kTimerPairs);
-            for (auto& e : t.ev) HIPCHK(x, hipEventCreate(&e));
+            for (auto& e : t.ev) HIPCHK(x, hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
             t.used = 0; t.total_ms = 0; t.launches = 0;
         }
         x->timing = true;
