@@ -25,6 +25,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_gemv_qwen35b.json")
+
+
+def measured_traffic(kernel_prefix):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) from the committed counter runs,
+    or None when the kernels' source has changed since they were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    src = open(os.path.join(ROOT, "expert_cached_decode_amd", "csrc", "decode.hip"), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec.get("decode_hip_sha256"):
+        return None
+    for name, k in rec["kernels"].items():
+        if kernel_prefix in name:
+            return int(k["fetch_bytes"] + k["write_bytes"])
+    return None
 
 
 def log(msg):
@@ -172,7 +190,7 @@ def main():
                    "graph": graph is not None},
         "roofline": {"bound": "hbm", "kernel": "gate/up SwiGLU GEMV (gu_kernel)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gu_kernel"),
                      "bytes_per_launch": int(gu_bytes), "us_per_launch": round(gu_us, 3),
                      "launches": int(n_launch), "timing": "HIP events around each launch, eager pass"},
         "down_kernel": {"achieved": round(dn_gbs, 1), "unit": "GB/s", "frac": round(dn_gbs / HBM_PEAK_GBS, 4),
