@@ -1,0 +1,82 @@
+"""A decode step captured as one graph (all layers, fixed shapes, device-resident
+counts, host branch as a host node) replays bit-identically to the eager calls:
+every replay's outputs and the final cache state (residency, slot keys, LRU keys,
+clock) match an eager run on an identical context. Replays alternate with eager
+work and synchronisations on the same process."""
+import numpy as np
+import pytest
+
+import gen
+from gen.configs import DSV4_DECODE, QWEN_DECODE
+from tests.harness import empty_out, make_ctx, make_pool
+
+pytestmark = pytest.mark.gpu
+
+
+def inputs(cfg, steps, L):
+    import torch
+    logits = torch.from_numpy(gen.decode_logits(cfg, steps=steps, L=L)).cuda()        # [S, L, 1, E]
+    xs = np.stack([np.stack([gen.decode_x(cfg, s, l) for l in range(L)]) for s in range(steps)])
+    x = torch.from_numpy(xs.view(np.int16)).cuda()                                    # [S, L, 1, H]
+    return logits, x
+
+
+def eager_run(cfg, pool, L, steps, logits, x, **kw):
+    import torch
+    import expert_cached_decode_amd as EC
+    ctx = make_ctx(cfg, pool, L=L, **kw)
+    outs = torch.empty((L, 1, cfg.H), dtype=torch.int16, device="cuda")
+    res = []
+    for s in range(steps):
+        for l in range(L):
+            EC.moe_decode_layer(ctx, l, x[s, l], logits[s, l], 1, outs[l])
+        torch.cuda.synchronize()
+        res.append(outs.clone())
+    state = ctx.debug_state()
+    ctx.close()
+    return res, state
+
+
+def graph_run(cfg, pool, L, steps, logits, x, **kw):
+    import torch
+    import expert_cached_decode_amd as EC
+    ctx = make_ctx(cfg, pool, L=L, **kw)
+    xs = torch.empty((L, 1, cfg.H), dtype=torch.int16, device="cuda")
+    ls = torch.empty((L, 1, cfg.E), dtype=torch.float32, device="cuda")
+    outs = torch.empty((L, 1, cfg.H), dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        for l in range(L):
+            EC.moe_decode_layer(ctx, l, xs[l], ls[l], 1, outs[l], cap)
+    torch.cuda.synchronize()
+    res = []
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for s in range(steps):
+        xs.copy_(x[s]); ls.copy_(logits[s])
+        g.replay()
+        torch.cuda.synchronize()
+        res.append(outs.clone())
+        scratch.add_(1.0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+    state = ctx.debug_state()
+    ctx.close()
+    return res, state
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    (QWEN_DECODE.with_(L=4, slots=48), dict(C=48)),
+    (DSV4_DECODE.with_(L=2, slots=24, H=1024, I=512), dict(C=24, bp=300, bh=1000)),
+], ids=["bf16-no-host-branch", "mxfp4-host-branch"])
+def test_graph_replay_matches_eager(cfg, kw):
+    L, steps = cfg.L, 12
+    pool = make_pool(cfg)
+    logits, x = inputs(cfg, steps, L)
+    a, sa = eager_run(cfg, pool, L, steps, logits, x, **kw)
+    b, sb = graph_run(cfg, pool, L, steps, logits, x, **kw)
+    for s in range(steps):
+        assert np.array_equal(a[s].cpu().numpy(), b[s].cpu().numpy()), s
+    for u, v in zip(sa[:3], sb[:3]):
+        assert np.array_equal(u, v)
+    assert sa[3] == sb[3] == steps * L
