@@ -1,17 +1,20 @@
 """Benchmark: one MoE layer step with a GPU expert cache on one MI355X.
 
-A step is one batch-1 decode token through all 40 MoE layers of the
-Qwen3.6-35B-A3B-shaped workload (E = 256, top-8, H = 2048, I = 512, bf16
-experts, 64.4 GB pinned expert bank, 3072-slot shared LRU cache, routing with
-60% step-to-step overlap, BP:BH = 1000:1000), i.e. route -> cache control ->
-fill -> grouped SwiGLU GEMV -> exact merge, per layer, captured in one
-hipGraph per token. Inputs (router logits and layer inputs for every step)
-are resident in HBM before the timed region.
+Default (the headline): a step is one batch-1 decode token through all 40 MoE
+layers of the Qwen3.6-35B-A3B-shaped workload (E = 256, top-8, H = 2048,
+I = 512, bf16 experts, 64.4 GB pinned expert bank, 3072-slot shared LRU cache,
+routing with 60% step-to-step overlap, BP:BH = 1000:1000): route -> cache
+control -> fill -> gate/up GEMV -> down GEMV + exact merge, per layer, captured
+in one hipGraph per token. Inputs (router logits and layer inputs of every
+step) are resident in HBM before the timed region.
 
-Also measured in the same run: the expert GEMV's HBM roofline (event-timed
-kernels), prefill seconds per 8192-token chunk with full-layer double
-buffering against the measured host-link bound, and the CPU oracle on a
-bounded sample (cpu_baseline). Prints one JSON line.
+Also measured in the same run: the gate/up GEMV's HBM roofline (kernels
+bracketed by HIP events in an eager pass), prefill seconds per 8192-token chunk
+with full-layer double buffering against the measured host-link bound, and the
+CPU oracle on a bounded sample (cpu_baseline). Prints one JSON line.
+
+Other workloads (`--workload dsv4 | stress`) measure the DeepSeek-V4-Flash-shaped
+MXFP4 decode and the batch-16 / K = 64 stress case the same way.
 """
 import argparse
 import json
@@ -49,11 +52,49 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def workload(args):
+    from gen.configs import DSV4_DECODE, QWEN_DECODE, STRESS, budget_slots
+    if args.workload == "qwen":
+        cfg = QWEN_DECODE
+        text = ("Qwen3.6-35B-A3B-shaped MoE decode: 40 layers, 256 experts, top-8, hidden 2048, expert "
+                "intermediate 512, bf16 experts (64.4 GB pinned bank), shared LRU cache of 3072 slots (30%)")
+    elif args.workload == "dsv4":
+        cfg = DSV4_DECODE.with_(bp=1000, bh=1000)
+        text = ("DeepSeek-V4-Flash-shaped MoE decode: 43 layers, 256 experts, top-6, hidden 4096, expert "
+                "intermediate 2048, MXFP4 experts (147.2 GB pinned bank), shared LRU cache of 2752 slots (25%)")
+    else:
+        cfg = STRESS.with_(T=args.tokens or 16)
+        text = ("stress: DeepSeek-V4-Flash shapes (MXFP4), 4096-slot cache, K = 64")
+    if args.bpbh:
+        bp, bh = (int(v) for v in args.bpbh.split(":"))
+        cfg = cfg.with_(bp=bp, bh=bh)
+    if args.p is not None:
+        cfg = cfg.with_(p=args.p)
+    if args.tokens and args.workload != "stress":
+        cfg = cfg.with_(T=args.tokens)
+    text += ", batch %d, %d%% step-to-step routing overlap, BP:BH %d:%d" % (cfg.T, round(100 * cfg.p), cfg.bp,
+                                                                             cfg.bh)
+    return cfg, text
+
+
+def gemv_bytes(cfg):
+    """Algorithmic bytes per cache-side expert: (gate + up) and down, codes plus MXFP4 scales."""
+    n = cfg.H * cfg.I
+    if cfg.wdtype == 2:
+        return 2 * (n // 2 + n // 32), n // 2 + n // 32
+    es = 4 if cfg.wdtype == 0 else 2
+    return 2 * n * es, n * es
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", choices=["qwen", "dsv4", "stress"], default="qwen")
+    ap.add_argument("--bpbh", default=None, help="BP:BH integers, e.g. 300:1000")
+    ap.add_argument("--p", type=float, default=None, help="step-to-step routing overlap")
+    ap.add_argument("--tokens", type=int, default=0, help="decode batch T")
     ap.add_argument("--eager", action="store_true", help="no graph capture")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -68,10 +109,10 @@ def main():
 
     import torch
     import gen
-    from gen.configs import QWEN_DECODE, QWEN_PREFILL
+    from gen.configs import MXFP4, QWEN_PREFILL
     import expert_cached_decode_amd as EC
 
-    cfg = QWEN_DECODE
+    cfg, text = workload(args)
     torch.cuda.set_device(0)
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
@@ -80,51 +121,47 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    K, W = args.steps, args.warmup
+    K, W, T, L = args.steps, args.warmup, cfg.T, cfg.L
     total_steps = W + K + args.timing_steps
+    # The MXFP4 bank (147 GB) exceeds what the host can pin (about 64 GiB): the host pool then
+    # holds P = 16 layers and layer l reads pool layer l mod 16 (bytes per fill unchanged). Its
+    # layers are drawn once (period 1) and copied; every byte is still distinct memory.
+    P = 16 if cfg.wdtype == MXFP4 else L
+    period = 1 if cfg.wdtype == MXFP4 else 0
 
     t0 = time.time()
-    pool = EC.PinnedBuffer(cfg.L * cfg.E * cfg.expert_bytes)
-    gen.fill_pool_ptr(cfg, pool.ptr, 0, cfg.L)
-    log("expert bank %.1f GB pinned and drawn in %.1f s" % (pool.nbytes / 1e9, time.time() - t0))
+    pool = EC.PinnedBuffer(P * cfg.E * cfg.expert_bytes)
+    gen.fill_pool_ptr(cfg, pool.ptr, 0, P, layer_period=period)
+    log("expert bank %.1f GB pinned (%d pool layers) and drawn in %.1f s" % (pool.nbytes / 1e9, P, time.time() - t0))
 
-    prefill_T = 0 if args.no_prefill else QWEN_PREFILL.T
-    ctx = EC.Context(cfg.L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype, max_tokens=1, cache_slots=cfg.slots,
-                     victim_k=cfg.K, bp=cfg.bp, bh=cfg.bh, host_pool=pool, prefill_max_tokens=prefill_T)
+    prefill_T = QWEN_PREFILL.T if (args.workload == "qwen" and not args.no_prefill) else 0
+    ctx = EC.Context(L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype, max_tokens=T, cache_slots=cfg.slots,
+                     victim_k=cfg.K, bp=cfg.bp, bh=cfg.bh, host_pool=pool, prefill_max_tokens=prefill_T,
+                     pool_layers=P)
 
-    # inputs resident in HBM
     t0 = time.time()
-    logits = torch.from_numpy(gen.decode_logits(cfg, steps=total_steps)).cuda()  # [S, L, 1, E]
-    xs = torch.empty((total_steps, cfg.L, 1, cfg.H), dtype=torch.int16, device="cuda")
+    logits = torch.from_numpy(gen.decode_logits(cfg, steps=total_steps)).cuda()  # [S, L, T, E]
+    xs = torch.empty((total_steps, L, T, cfg.H), dtype=torch.int16, device="cuda")
     for s in range(total_steps):
-        xs[s].copy_(torch.from_numpy(np.stack([gen.decode_x(cfg, s, l) for l in range(cfg.L)]).view(np.int16)))
+        xs[s].copy_(torch.from_numpy(np.stack([gen.decode_x(cfg, s, l) for l in range(L)]).view(np.int16)))
     log("decode inputs for %d steps generated in %.1f s" % (total_steps, time.time() - t0))
 
     stream = torch.cuda.current_stream()
-    x_stage = torch.empty((cfg.L, 1, cfg.H), dtype=torch.int16, device="cuda")
-    lg_stage = torch.empty((cfg.L, 1, cfg.E), dtype=torch.float32, device="cuda")
-    outs = torch.empty((cfg.L, 1, cfg.H), dtype=torch.int16, device="cuda")
+    x_stage = torch.empty((L, T, cfg.H), dtype=torch.int16, device="cuda")
+    lg_stage = torch.empty((L, T, cfg.E), dtype=torch.float32, device="cuda")
+    outs = torch.empty((L, T, cfg.H), dtype=torch.int16, device="cuda")
 
-    def token_layers(xsrc, lsrc):
-        for l in range(cfg.L):
-            EC.moe_decode_layer(ctx, l, xsrc[l], lsrc[l], 1, outs[l], stream)
+    def token_layers(xsrc, lsrc, strm):
+        for l in range(L):
+            EC.moe_decode_layer(ctx, l, xsrc[l], lsrc[l], T, outs[l], strm)
 
     graph = None
     if not args.eager:
-        # capture one token (all layers) reading fixed staging buffers
-        x_stage.copy_(xs[0]); lg_stage.copy_(logits[0])
-        torch.cuda.synchronize()
-        # warm the allocator and the first step eagerly, then capture
-        token_layers(x_stage, lg_stage)
-        torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
-        with torch.cuda.graph(graph, stream=side):
-            for l in range(cfg.L):
-                EC.moe_decode_layer(ctx, l, x_stage[l], lg_stage[l], 1, outs[l], side)
         torch.cuda.synchronize()
-        # the eager warm step and the capture did not run the graph; restart from a cold cache
-        ctx.rebuild(3000)
+        with torch.cuda.graph(graph, stream=side):
+            token_layers(x_stage, lg_stage, side)
         torch.cuda.synchronize()
 
     def run_step(s):
@@ -132,7 +169,7 @@ def main():
             x_stage.copy_(xs[s]); lg_stage.copy_(logits[s])
             graph.replay()
         else:
-            token_layers(xs[s], logits[s])
+            token_layers(xs[s], logits[s], stream)
 
     for s in range(W):
         run_step(s)
@@ -150,23 +187,24 @@ def main():
     ms_total = e0.elapsed_time(e1)
     st = ctx.stats(reset=True)
     ms_per_step = ms_total / K
-    tok_s = 1000.0 / ms_per_step
+    tok_s = 1000.0 * T / ms_per_step
     lookups = st["hits"] + st["misses"]
-    log("decode: %d steps in %.3f s (wall %.3f s): %.2f tok/s; miss rate %.3f, fills/token %.2f"
-        % (K, ms_total / 1e3, t_wall, tok_s, st["misses"] / max(lookups, 1), st["fills"] / K))
+    log("decode: %d steps in %.3f s (wall %.3f s): %.2f tok/s; miss rate %.3f, fills/step %.2f, host/step %.2f"
+        % (K, ms_total / 1e3, t_wall, tok_s, st["misses"] / max(lookups, 1), st["fills"] / K, st["host"] / K))
 
     # kernel timing pass (eager, event-bracketed kernels), continuing the same workload
     ctx.kernel_timing(True)
     for s in range(W + K, total_steps):
-        token_layers(xs[s], logits[s])
+        token_layers(xs[s], logits[s], stream)
     torch.cuda.synchronize()
     st2 = ctx.stats(reset=True)
     kt = {k: ctx.kernel_time(k) for k in ("ctl", "fill", "gate_up", "down")}
     ctx.kernel_timing(False)
     n_launch = kt["gate_up"][1]
     side_experts = st2["hits"] + st2["fills"]  # cache-side experts over the pass = sum of n_gpu per launch
-    gu_bytes = side_experts * 2 * cfg.I * cfg.H * 2 / max(n_launch, 1)
-    dn_bytes = side_experts * cfg.H * cfg.I * 2 / max(n_launch, 1)
+    gub, dnb = gemv_bytes(cfg)
+    gu_bytes = side_experts * gub / max(n_launch, 1)
+    dn_bytes = side_experts * dnb / max(n_launch, 1)
     gu_us = kt["gate_up"][0] * 1e3 / max(n_launch, 1)
     dn_us = kt["down"][0] * 1e3 / max(kt["down"][1], 1)
     ctl_us = kt["ctl"][0] * 1e3 / max(kt["ctl"][1], 1)
@@ -174,40 +212,55 @@ def main():
     dn_gbs = dn_bytes / (dn_us * 1e-6) / 1e9
     fill_ms, fill_n = kt["fill"]
     fill_gbs = st2["fills"] * cfg.expert_bytes / max(fill_ms * 1e-3, 1e-9) / 1e9
-    log("gate/up GEMV %.2f us/launch, %.1f MB -> %.0f GB/s (%.1f%% of 8 TB/s); down+merge %.2f us, %.1f MB -> %.0f GB/s; "
-        "ctl %.2f us; fill %.1f GB/s over the link" % (gu_us, gu_bytes / 1e6, gu_gbs, 100 * gu_gbs / HBM_PEAK_GBS,
-                                                     dn_us, dn_bytes / 1e6, dn_gbs, ctl_us, fill_gbs))
+    log("gate/up GEMV %.2f us/launch, %.1f MB -> %.0f GB/s (%.1f%% of 8 TB/s); down+merge %.2f us, %.1f MB -> "
+        "%.0f GB/s; ctl %.2f us; fill %.1f GB/s over the link" % (gu_us, gu_bytes / 1e6, gu_gbs,
+                                                                   100 * gu_gbs / HBM_PEAK_GBS, dn_us,
+                                                                   dn_bytes / 1e6, dn_gbs, ctl_us, fill_gbs))
 
     result = {
         "metric": "MoE decode tok/s (batch 1) + % HBM roofline; prefill s per 8192-token chunk",
         "value": round(tok_s, 3), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "Qwen3.6-35B-A3B-shaped MoE decode: 40 layers, 256 experts, top-8, hidden 2048, "
-                               "expert intermediate 512, bf16 experts (64.4 GB pinned bank), shared LRU cache of "
-                               "3072 slots (30%), batch 1, 60% step-to-step routing overlap, BP:BH 1000:1000",
-                   "global_batch": 1, "layers": cfg.L, "cache_slots": cfg.slots,
-                   "graph": graph is not None},
+        "vs_baseline": None, "dtype": "mxfp4" if cfg.wdtype == MXFP4 else "bf16", "data": "synthetic",
+        "config": {"workload": text, "global_batch": T, "layers": L, "cache_slots": cfg.slots,
+                   "host_pool_layers": P, "graph": graph is not None},
         "roofline": {"bound": "hbm", "kernel": "gate/up SwiGLU GEMV (gu_kernel)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gu_kernel"),
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("gu_kernel") if args.workload == "qwen" else None,
                      "bytes_per_launch": int(gu_bytes), "us_per_launch": round(gu_us, 3),
                      "launches": int(n_launch), "timing": "HIP events around each launch, eager pass"},
         "down_kernel": {"achieved": round(dn_gbs, 1), "unit": "GB/s", "frac": round(dn_gbs / HBM_PEAK_GBS, 4),
                         "bytes_per_launch": int(dn_bytes), "us_per_launch": round(dn_us, 3)},
         "other_kernels_us": {"ctl": round(ctl_us, 3),
                              "fill_per_expert": round(fill_ms * 1e3 / max(st2["fills"], 1), 2)},
-        "cache": {"miss_rate": round(st["misses"] / max(lookups, 1), 4), "fills_per_token": round(st["fills"] / K, 3),
-                  "host_per_token": round(st["host"] / K, 3),
-                  "fill_link_GBs": round(fill_gbs, 2)},
+        "cache": {"miss_rate": round(st["misses"] / max(lookups, 1), 4), "fills_per_step": round(st["fills"] / K, 3),
+                  "host_per_step": round(st["host"] / K, 3), "fill_link_GBs": round(fill_gbs, 2)},
     }
-
-    if not args.no_prefill:
+    if args.workload == "stress":
+        result["rebuild"] = bench_rebuild(ctx, cfg)
+    if prefill_T:
         result["prefill"] = bench_prefill(ctx, cfg, QWEN_PREFILL, args.prefill_chunks)
     if not args.no_cpu:
-        result["cpu_baseline"] = bench_cpu(cfg, logits.cpu().numpy())
+        result["cpu_baseline"] = bench_cpu(cfg, logits.cpu().numpy(), P, period)
     ctx.close()
     print(json.dumps(result), flush=True)
+
+
+def bench_rebuild(ctx, cfg):
+    """cache_rebuild latency at a safe point: 40% -> 15% -> 40% of all experts."""
+    import torch
+    from gen.configs import budget_slots
+    out = {}
+    for bp in (1500, 4000):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        C = ctx.rebuild(bp)
+        out["to_%d_bp_ms" % bp] = round((time.perf_counter() - t0) * 1e3, 3)
+        out["slots_%d_bp" % bp] = C
+    assert out["slots_4000_bp"] == budget_slots(cfg.L, cfg.E, 4000)
+    log("cache_rebuild: %s" % out)
+    return out
 
 
 def bench_prefill(ctx, cfg, pcfg, chunks):
@@ -269,39 +322,41 @@ def bench_prefill(ctx, cfg, pcfg, chunks):
             "s_per_chunk_no_double_buffer": round(t_off, 4), "tok_s": round(T / s_chunk, 1)}
 
 
-def bench_cpu(cfg, logits, budget_s=15.0):
+def bench_cpu(cfg, logits, P, period, budget_s=15.0):
     """The CPU oracle (fp64 plain-loop MoE + literal LRU simulator) on a bounded sample of the same workload."""
     import gen
     from oracle import moe
     from oracle.lru_sim import LRUSim
-    from oracle.route import route_row
+    from oracle.route import route
     cores = len(os.sched_getaffinity(0))
     sim = LRUSim(cfg.L, cfg.E, cfg.slots, cfg.K, cfg.bp, cfg.bh)
     t_moe = t_lru = 0.0
-    tokens = 0
+    steps = 0
     t_start = time.time()
-    while time.time() - t_start < budget_s or tokens == 0:
-        s = tokens
+    while time.time() - t_start < budget_s or steps == 0:
+        s = steps
         for l in range(cfg.L):
-            lg = logits[s, l]                                   # [1, E]
-            x = gen.bf16_to_f32(gen.decode_x(cfg, s, l)).astype(np.float64)
-            routed, _ = route_row(lg[0], cfg.k)
-            mats = {e: gen.expert_logical(cfg, l, e) for e in routed}  # input preparation, not timed
+            lg = logits[s, l]                                   # [T, E]
+            xw = gen.decode_x(cfg, s, l)
+            x = (xw.astype(np.float64) if cfg.wdtype == 0 else gen.bf16_to_f32(xw).astype(np.float64))
+            ids, _ = route(lg, cfg.k)
+            src_l = (l % P) % period if period else l % P  # the layer whose draws the pool holds
+            mats = {e: gen.expert_logical(cfg, src_l, e) for row in ids for e in row}  # input preparation, untimed
             t0 = time.time()
-            sim.step(l, [routed])
+            sim.step(l, ids)
             t1 = time.time()
             moe.moe_tokens(cfg.wdtype, x, lg, cfg.k, mats.__getitem__)
             t2 = time.time()
             t_lru += t1 - t0
             t_moe += t2 - t1
-        tokens += 1
+        steps += 1
     sec = t_moe + t_lru
-    log("cpu oracle: %d tokens x %d layers in %.2f s of compute (%.2f s LRU sim) on %d cores"
-        % (tokens, cfg.L, sec, t_lru, cores))
-    return {"value": round(tokens / sec, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": "first %d batch-1 decode tokens x %d layers of the same workload (fp64 C MoE layer with "
+    log("cpu oracle: %d steps x %d layers in %.2f s of compute (%.2f s LRU sim) on %d cores"
+        % (steps, cfg.L, sec, t_lru, cores))
+    return {"value": round(steps * cfg.T / sec, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": "first %d decode steps (batch %d) x %d layers of the same workload (fp64 C MoE layer with "
                       "OpenMP over rows, routing and literal LRU simulator in Python; weight generation not timed)"
-                      % (tokens, cfg.L),
+                      % (steps, cfg.T, cfg.L),
             "lru_sim_s": round(t_lru, 3), "moe_s": round(t_moe, 3)}
 
 

@@ -38,7 +38,7 @@ class ec_layout_info(ctypes.Structure):
 class ec_config(ctypes.Structure):
     _fields_ = [("shape", ec_shape), ("max_tokens", c_i32), ("cache_slots", c_i32), ("victim_k", c_i32),
                 ("bp_mbps", c_u32), ("bh_mbps", c_u32), ("host_threads", c_i32), ("prefill_max_tokens", c_i32),
-                ("reserved", c_i32 * 4)]
+                ("pool_layers", c_i32), ("reserved", c_i32 * 3)]
 
 
 class ec_step_view(ctypes.Structure):
@@ -201,12 +201,13 @@ class Context:
     """
 
     def __init__(self, L, E, k, H, I, wdtype, max_tokens, cache_slots, victim_k=0, bp=1000, bh=1000,
-                 host_pool=None, host_pool_bytes=None, slot_pool=None, host_threads=0, prefill_max_tokens=0):
+                 host_pool=None, host_pool_bytes=None, slot_pool=None, host_threads=0, prefill_max_tokens=0,
+                 pool_layers=0):
         import torch
         self.shape = make_shape(L, E, k, H, I, wdtype)
         self.layout = layout(self.shape)
         self.cfg = ec_config(self.shape, max_tokens, cache_slots, victim_k, bp, bh, host_threads,
-                             prefill_max_tokens)
+                             prefill_max_tokens, pool_layers)
         dev_b, pin_b = workspace_size(self.cfg)
         self.dev_ws = torch.empty(dev_b, dtype=torch.uint8, device="cuda")
         self.pin_ws = PinnedBuffer(pin_b)

@@ -25,6 +25,7 @@ struct ec_ctx {
     ec_config cfg{};
     ec_layout_info lay{};
     int L = 0, E = 0, k = 0, H = 0, I = 0, wdt = 0, Tmax = 0, Umax = 0, K = 0, C = 0, nmax = 0;
+    int P = 0; // layers held by the host pool (layer l reads pool layer l % P)
     uint32_t bp = 0, bh = 1;
     bool host_branch = false;
     uint64_t epoch = 1;
@@ -163,6 +164,8 @@ static ec_status check_config(const ec_config* c) {
     if (c->host_threads < 0 || c->host_threads > 256) return fail(nullptr, EC_EINVAL, "host_threads in [0, 256]");
     if (c->prefill_max_tokens < 0 || c->prefill_max_tokens > (1 << 20))
         return fail(nullptr, EC_EINVAL, "prefill_max_tokens in [0, 2^20]");
+    if (c->pool_layers < 0 || c->pool_layers > s.layers)
+        return fail(nullptr, EC_EINVAL, "pool_layers must be in [0, layers]");
     if (c->prefill_max_tokens > 0 && s.wdtype == EC_DT_F32)
         return fail(nullptr, EC_EUNSUP, "prefill needs bf16 or MXFP4 expert weights");
     return EC_OK;
@@ -217,6 +220,7 @@ static void init_dims(ec_ctx* x, const ec_config* c) {
     x->Umax = x->nmax < x->E ? x->nmax : x->E;
     x->K = c->victim_k ? c->victim_k : (x->Umax < kMaxK ? x->Umax : kMaxK);
     x->C = c->cache_slots;
+    x->P = c->pool_layers ? c->pool_layers : x->L;
     x->bp = c->bp_mbps; x->bh = c->bh_mbps;
 }
 
@@ -257,9 +261,9 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
         delete x;
         return fail(nullptr, EC_ENOSPC, "workspace too small");
     }
-    if (host_pool_bytes < x->lay.layer_bytes * x->L) {
+    if (host_pool_bytes < x->lay.layer_bytes * x->P) {
         delete x;
-        return fail(nullptr, EC_ENOSPC, "host pool smaller than layers * experts * expert_bytes");
+        return fail(nullptr, EC_ENOSPC, "host pool smaller than pool_layers * experts * expert_bytes");
     }
     if ((uint64_t)x->C * x->lay.expert_bytes > slot_pool_bytes || (x->C > 0 && !slot_pool)) {
         delete x;
@@ -383,7 +387,7 @@ static void host_branch_fn(void* p) {
     HostJob& j = x->job;
     j.n_experts = nhost;
     for (int h = 0; h < nhost; ++h)
-        j.expert_base[h] = x->host_pool + ((uint64_t)layer * x->E + mb[CNT_N + h]) * x->lay.expert_bytes;
+        j.expert_base[h] = x->host_pool + ((uint64_t)(layer % x->P) * x->E + mb[CNT_N + h]) * x->lay.expert_bytes;
     j.rewritten = mb + CNT_N + n;
     j.T = T; j.k = x->k; j.H = x->H; j.I = x->I; j.wdtype = x->wdt;
     j.x = mb + mailbox_ints(n);
@@ -427,7 +431,7 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     d.tok_pairs = x->sb.tok_pairs; d.rewritten = x->sb.rewritten; d.w = x->sb.w;
     d.x = xin; d.act = x->act; d.y_host = x->y_host_dev;
     d.out = out; d.expert_bytes = x->lay.expert_bytes;
-    d.layer = layer; d.E = x->E; d.k = x->k; d.T = T; d.H = x->H; d.I = x->I; d.wdtype = x->wdt; d.U_max = x->Umax;
+    d.layer = layer % x->P; d.E = x->E; d.k = x->k; d.T = T; d.H = x->H; d.I = x->I; d.wdtype = x->wdt; d.U_max = x->Umax;
     d.host_pairs = x->host_branch ? 1 : 0;
     if (x->C > 0) {
         tm = timer_next(x, 1);
@@ -500,6 +504,7 @@ ec_status moe_prefill_layer(ec_ctx* x, int32_t layer, const void* xin, const flo
     if (!xin || !logits || !out) return fail(x, EC_EINVAL, "NULL pointer");
     PrefillCall c{};
     c.host_pool = x->host_pool;
+    c.P = x->P;
     c.layer = layer; c.L = x->L; c.E = x->E; c.k = x->k; c.H = x->H; c.I = x->I; c.T = T; c.wdtype = x->wdt;
     c.layer_bytes = x->lay.layer_bytes; c.expert_bytes = x->lay.expert_bytes;
     c.x = xin; c.logits = logits; c.out = out;

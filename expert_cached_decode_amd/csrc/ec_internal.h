@@ -99,7 +99,7 @@ struct DecodeArgs {
     const float* y_host;   // [T_max*k][H] (device copy of host partials)
     void* out;
     uint64_t expert_bytes;
-    int32_t layer, E, k, T, H, I, wdtype, U_max;
+    int32_t layer, E, k, T, H, I, wdtype, U_max; // layer: the host-pool layer the fills read
     int32_t host_pairs; // 1 when the step can have host-side pairs (the host branch is on)
 };
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s);

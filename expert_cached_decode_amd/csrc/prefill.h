@@ -24,6 +24,7 @@ struct PrefillState {
 
 struct PrefillCall {
     const uint8_t* host_pool;
+    int P;                   // layers held by the host pool (layer l reads pool layer l % P)
     int layer, L, E, k, H, I, T, wdtype;
     uint64_t layer_bytes, expert_bytes;
     const void* x;

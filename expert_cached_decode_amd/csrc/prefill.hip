@@ -296,7 +296,7 @@ void prefill_destroy(PrefillState& p) {
 static hipError_t upload(PrefillState& p, const PrefillCall& c, int b, int layer) {
     hipError_t e;
     if (p.used[b] && (e = hipStreamWaitEvent(c.copy, p.done[b], 0)) != hipSuccess) return e;
-    e = hipMemcpyAsync(p.buf[b], c.host_pool + (uint64_t)layer * c.layer_bytes, c.layer_bytes,
+    e = hipMemcpyAsync(p.buf[b], c.host_pool + (uint64_t)(layer % c.P) * c.layer_bytes, c.layer_bytes,
                        hipMemcpyHostToDevice, c.copy);
     if (e != hipSuccess) return e;
     p.buf_layer[b] = layer;

@@ -105,7 +105,11 @@ typedef struct ec_config {
     uint32_t bh_mbps;      /* BH: host expert processing bandwidth (>= 1, same unit) */
     int32_t host_threads;  /* host branch worker threads; 0 = default (8) */
     int32_t prefill_max_tokens; /* 0 = no prefill; else T_max for moe_prefill_layer */
-    int32_t reserved[4];
+    int32_t pool_layers;   /* layers the host pool holds (0 = L). With P < L, layer l reads its
+                              experts from pool layer l mod P: the bytes moved per fill, host
+                              expert or prefill upload are unchanged, only the distinct host
+                              memory shrinks (for hosts that cannot pin all L layers). */
+    int32_t reserved[3];
 } ec_config;
 
 /* Device views returned by expert_cache_step (pointers into the context's
@@ -145,7 +149,8 @@ ec_status ec_workspace_size(const ec_config* cfg, uint64_t* dev_bytes, uint64_t*
 /* Create a context on the current HIP device (must be gfx950).
  *   dev_ws     : dev, >= dev_bytes from ec_workspace_size, 256-byte aligned
  *   pinned_ws  : pinned, >= pinned_bytes
- *   host_pool  : pinned, [L][E][expert_bytes] expert bank (source of truth)
+ *   host_pool  : pinned, [P][E][expert_bytes] expert bank (source of truth),
+ *                P = pool_layers (or L)
  *   slot_pool  : dev, >= cache_slots * expert_bytes (may be NULL if C = 0)
  * The cache starts cold (every slot empty), the LRU clock at 0. Enqueues its
  * initialisation on the null stream and waits for it. */

@@ -45,13 +45,13 @@ def make_pool(cfg, L=None, layer_period=0):
     return pb
 
 
-def make_ctx(cfg, pool, L=None, C=None, K=None, bp=None, bh=None, T=None, prefill=0, threads=8):
+def make_ctx(cfg, pool, L=None, C=None, K=None, bp=None, bh=None, T=None, prefill=0, threads=8, pool_layers=0):
     import expert_cached_decode_amd as EC
     L = cfg.L if L is None else L
     return EC.Context(L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype, max_tokens=cfg.T if T is None else T,
                       cache_slots=cfg.slots if C is None else C, victim_k=cfg.K if K is None else K,
                       bp=cfg.bp if bp is None else bp, bh=cfg.bh if bh is None else bh, host_pool=pool,
-                      host_threads=threads, prefill_max_tokens=prefill)
+                      host_threads=threads, prefill_max_tokens=prefill, pool_layers=pool_layers)
 
 
 def oracle_layer(cfg, layer, x, logits, layer_period=0, tokens=None):

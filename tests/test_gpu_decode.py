@@ -146,3 +146,16 @@ def test_qwen_decode_full_size_sampled():
     ref = sim_counts(cfg, logits, cfg.L, 1, cfg.slots, cfg.K, cfg.bp, cfg.bh)
     assert {k: st[k] for k in ref} == ref
     ctx.close()
+
+
+def test_host_pool_layer_aliasing():
+    """pool_layers = 2 for 4 layers: layer l reads pool layer l % 2 (fills and host branch)."""
+    cfg = QWEN_DECODE.with_(L=4, slots=24, bp=500, bh=1000)
+    pool = make_pool(cfg, L=2)
+    ctx = make_ctx(cfg, pool, pool_layers=2)
+    outs, logits = run_decode(cfg, ctx, 6, 4, 1, lambda s, l: s in (2, 5))
+    for (s, l), (got, x, lg) in sorted(outs.items()):
+        ref, _, _ = oracle_layer(cfg, l % 2, x, lg)
+        assert row_rel_err(got, ref) <= 1e-2, (s, l)
+    assert ctx.stats()["host"] > 0
+    ctx.close()
