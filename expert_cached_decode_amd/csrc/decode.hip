@@ -15,14 +15,23 @@ namespace ec {
 
 typedef float f2v __attribute__((ext_vector_type(2)));
 
-constexpr int kGuWaves = 4;     // 256 threads
-constexpr int kGuRowsPerWave = 1;
-constexpr int kGuRows = kGuWaves * kGuRowsPerWave;
+constexpr int kGuWaves = 4; // 256 threads
 
+// Wave-wide sum through DPP: an inclusive scan by row shifts leaves each row's
+// sum in its lane 15, two row broadcasts carry them into lane 63, which is read
+// back to every lane. No LDS round trips (a shuffle butterfly costs six).
+#define EC_DPP_ADD(V, CTRL, RMASK) \
+    V += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(V), CTRL, RMASK, 0xf, false))
 __device__ __forceinline__ float wave_sum(float v) {
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+    EC_DPP_ADD(v, 0x111, 0xf); // row_shr:1
+    EC_DPP_ADD(v, 0x112, 0xf); // row_shr:2
+    EC_DPP_ADD(v, 0x114, 0xf); // row_shr:4
+    EC_DPP_ADD(v, 0x118, 0xf); // row_shr:8: lane 15 of each row holds the row sum
+    EC_DPP_ADD(v, 0x142, 0xa); // row_bcast:15 into rows 1 and 3
+    EC_DPP_ADD(v, 0x143, 0xc); // row_bcast:31 into rows 2 and 3: lane 63 holds the total
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+#undef EC_DPP_ADD
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -112,6 +121,43 @@ __device__ __forceinline__ float chunk_dot(uint4 wv, uint32_t scale, const float
     return acc;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t w, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x), acc, false);
+}
+
+// dot of one 16-byte weight chunk with EPC bf16 activations kept packed in pairs
+// (word i holds elements 2i, low half, and 2i + 1): bf16 weight pairs feed the
+// bf16 dot2 unit directly (products are exact in fp32); MXFP4 bytes are first
+// decoded with their block scale to bf16 pairs, exact for every E2M1 code
+// times a power-of-two scale within bf16's normal range.
+template <int WDT>
+__device__ __forceinline__ float chunk_dot_packed(uint4 wv, uint32_t scale, const uint32_t* xw, float acc) {
+    if constexpr (WDT == EC_DT_BF16) {
+        acc = dot2_bf16(wv.x, xw[0], acc);
+        acc = dot2_bf16(wv.y, xw[1], acc);
+        acc = dot2_bf16(wv.z, xw[2], acc);
+        acc = dot2_bf16(wv.w, xw[3], acc);
+    } else {
+        const float sc = e8m0_scale(scale);
+        const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // byte b of the word holds elements 2b (low nibble) and 2b + 1 (high nibble)
+            const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(words[q], sc, 0);
+            const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(words[q], sc, 1);
+            const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(words[q], sc, 2);
+            const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(words[q], sc, 3);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p0, __builtin_bit_cast(bf16x2, xw[q * 4 + 0]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p1, __builtin_bit_cast(bf16x2, xw[q * 4 + 1]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p2, __builtin_bit_cast(bf16x2, xw[q * 4 + 2]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(p3, __builtin_bit_cast(bf16x2, xw[q * 4 + 3]), acc, false);
+        }
+    }
+    return acc;
+}
+
 // ---------------------------------------------------------------------------
 // Fill: copy the q filled experts from the pinned host pool (read over the
 // host link by the GPU itself: the slot addresses are decided on the device)
@@ -138,165 +184,236 @@ __global__ __launch_bounds__(256) void fill_kernel(DecodeArgs a, int chunks) {
 
 // ---------------------------------------------------------------------------
 // Gate/up GEMV: for each cache-side expert g and each token routed to it,
-// act[pair][i] = silu(W_gate[i] . x) * (W_up[i] . x), one wavefront per row
-// pair, kGuRowsPerWave row pairs in flight per wavefront. Grid: U_max x
-// (I / kGuRows); blocks past the step's cache-side count exit.
-template <int WDT, int NCH, bool T1>
+// act[pair][i] = silu(W_gate[i] . x) * (W_up[i] . x). A wavefront owns RW row
+// pairs of one expert; each lane holds NCH 16-byte chunks of every row in
+// registers, so one expert's weights are read once whatever its token count.
+// Grid: U_max x (I / (4 RW)); blocks past the step's cache-side count exit.
+// FULL: every lane owns NCH whole chunks (row bytes = 1024 NCH), no guards.
+template <int WDT, int NCH, int RW, bool T1, bool FULL>
 __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
     constexpr int EPC = Fmt<WDT>::EPC;
     const int g = blockIdx.x / chunks, ch = blockIdx.x % chunks;
+    // both loads are issued before the exit test (one round trip)
     const int n_gpu = a.counts[CNT_GPU];
     const int4 d = a.gpu_desc[g];
-    if (g >= n_gpu) return;
+    if (g >= n_gpu || d.x < 0) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H, I = a.I;
     const int rb = row_bytes<WDT>(H), n16 = rb >> 4;
     const uint8_t* base = a.slots + (uint64_t)d.x * a.expert_bytes;
-    const uint8_t* gate = base;
-    const uint8_t* up = base + (uint64_t)I * rb;
-    const uint8_t* gsc = base + 3ull * I * rb;             // MXFP4 scale rows (H/32 bytes each)
-    const uint8_t* usc = gsc + (uint64_t)I * (H / 32);
-    const int row0 = ch * kGuRows + wave * kGuRowsPerWave;
+    const uint8_t* gsc = base + 3ull * I * rb; // MXFP4 scale rows (H/32 bytes each)
+    const int row0 = (ch * kGuWaves + wave) * RW;
     const bool xbf16 = WDT != EC_DT_F32;
 
-    const int np = T1 ? 1 : d.z; // batch 1: one token per expert
-    for (int pi = 0; pi < np; ++pi) {
-        const int pair = pi == 0 ? d.w : a.tok_pairs[d.y + pi];
-        const int t = T1 ? 0 : pair / a.k;
-        uint4 wg[kGuRowsPerWave][NCH], wu[kGuRowsPerWave][NCH];
-        uint32_t sg[kGuRowsPerWave][NCH], su[kGuRowsPerWave][NCH];
+    uint4 wg[RW][NCH], wu[RW][NCH];
+    uint32_t sg[RW][NCH], su[RW][NCH];
 #pragma unroll
-        for (int rr = 0; rr < kGuRowsPerWave; ++rr) {
-            const int row = row0 + rr;
-#pragma unroll
-            for (int j = 0; j < NCH; ++j) {
-                const int c = lane + 64 * j;
-                if (row < I && c < n16) {
-                    wg[rr][j] = load_stream(gate + (uint64_t)row * rb + 16ull * c);
-                    wu[rr][j] = load_stream(up + (uint64_t)row * rb + 16ull * c);
-                    if (WDT == EC_DT_MXFP4) {
-                        sg[rr][j] = gsc[(uint64_t)row * (H / 32) + c];
-                        su[rr][j] = usc[(uint64_t)row * (H / 32) + c];
-                    }
-                }
-            }
-        }
-        float xv[NCH][EPC];
+    for (int rr = 0; rr < RW; ++rr) {
+        const uint8_t* gp = base + (uint64_t)(row0 + rr) * rb;
+        const uint8_t* up = gp + (uint64_t)I * rb;
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const int c = lane + 64 * j;
-            if (c < n16) load_vec<EPC>(a.x, (int64_t)t * H + (int64_t)c * EPC, xbf16, xv[j]);
+            if (FULL || c < n16) {
+                wg[rr][j] = load_stream(gp + 16ull * c);
+                wu[rr][j] = load_stream(up + 16ull * c);
+                if (WDT == EC_DT_MXFP4) {
+                    sg[rr][j] = gsc[(uint64_t)(row0 + rr) * (H / 32) + c];
+                    su[rr][j] = gsc[(uint64_t)(I + row0 + rr) * (H / 32) + c];
+                }
+            }
+        }
+    }
+    // keep every weight load ahead of the arithmetic (the scheduler would otherwise
+    // interleave them with the dot products and cut the loads in flight)
+    __builtin_amdgcn_sched_barrier(0);
+    const int np = T1 ? 1 : d.z;
+    for (int pi = 0; pi < np; ++pi) {
+        const int pair = (T1 || pi == 0) ? d.w : a.tok_pairs[d.y + pi];
+        const int t = T1 ? 0 : pair / a.k;
+        // x: f32 for f32 weights, else bf16 kept in packed pairs for the dot2 unit
+        constexpr bool PK = WDT != EC_DT_F32;
+        float xv[NCH][PK ? 1 : EPC];
+        uint32_t xw[NCH][PK ? EPC / 2 : 1];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int c = lane + 64 * j;
+            if (FULL || c < n16) {
+                if constexpr (PK) {
+                    const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)t * H + (int64_t)c * EPC);
+#pragma unroll
+                    for (int q = 0; q < EPC / 8; ++q) {
+                        const uint4 u = xp[q];
+                        xw[j][4 * q] = u.x; xw[j][4 * q + 1] = u.y; xw[j][4 * q + 2] = u.z; xw[j][4 * q + 3] = u.w;
+                    }
+                } else {
+                    load_vec<EPC>(a.x, (int64_t)t * H + (int64_t)c * EPC, xbf16, xv[j]);
+                }
+            }
         }
 #pragma unroll
-        for (int rr = 0; rr < kGuRowsPerWave; ++rr) {
-            const int row = row0 + rr;
+        for (int rr = 0; rr < RW; ++rr) {
             float accg = 0.f, accu = 0.f;
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
                 const int c = lane + 64 * j;
-                if (row < I && c < n16) {
-                    accg = chunk_dot<WDT>(wg[rr][j], WDT == EC_DT_MXFP4 ? sg[rr][j] : 0u, xv[j], accg);
-                    accu = chunk_dot<WDT>(wu[rr][j], WDT == EC_DT_MXFP4 ? su[rr][j] : 0u, xv[j], accu);
+                if (FULL || c < n16) {
+                    if constexpr (PK) {
+                        accg = chunk_dot_packed<WDT>(wg[rr][j], WDT == EC_DT_MXFP4 ? sg[rr][j] : 0u, xw[j], accg);
+                        accu = chunk_dot_packed<WDT>(wu[rr][j], WDT == EC_DT_MXFP4 ? su[rr][j] : 0u, xw[j], accu);
+                    } else {
+                        accg = chunk_dot<WDT>(wg[rr][j], 0u, xv[j], accg);
+                        accu = chunk_dot<WDT>(wu[rr][j], 0u, xv[j], accu);
+                    }
                 }
             }
             accg = wave_sum(accg);
             accu = wave_sum(accu);
-            if (lane == 0 && row < I) {
+            if (lane == 0) {
                 const float sv = accg / (1.f + expf(-accg));
-                a.act[(int64_t)pair * I + row] = sv * accu;
+                a.act[(int64_t)pair * I + row0 + rr] = sv * accu;
             }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Down GEMV + exact merge. One wavefront owns one output row h: for every token
-// t it computes y[t,j][h] = W_down,e(t,j)[h] . act[t,j] for the cache-side
-// pairs (the rows of up to 8 experts in flight at once, activation slices in
-// registers) and merges out[t][h] = sum_j w[t,j] y[t,j][h] in j order, taking
-// host-side pairs' partial sums from y_host. No LDS and no cross-block
-// communication; a block is 4 rows. T1: batch-1 specialisation (no token
-// loop); HOST: the step may have host-side pairs (else every pair is cache-side).
-template <int WDT, int NCH, bool HOST>
-__device__ __forceinline__ float down_group(const DecodeArgs& a, int t, int j0, int row, int lane) {
-    constexpr int EPC = Fmt<WDT>::EPC;
-    constexpr int G = 128 / (NCH * EPC) >= 8 ? 8 : (128 / (NCH * EPC) >= 1 ? 128 / (NCH * EPC) : 1);
-    const int H = a.H, I = a.I, k = a.k, last = t * k + k - 1;
+// Down GEMV + exact merge. A block of four wavefronts owns 4 R output rows h.
+// For each token t and each group of G of its pairs, the block first issues
+// the loads of its weight rows W_down,e(t,j)[h] (the group's indices come from
+// one vector load), then stages the group's activation vectors act[t,j] in LDS
+// (each is read from L2 once per block instead of once per row), and each lane
+// accumulates w[t,j] * (its slice of W_down[h] . act[t,j]) in j order; one
+// wave reduction per row gives the cache-side sum. Host-side pairs (HOST) add
+// w[t,j] * y_host[t,j][h] through a second fixed-order wave reduction, so every
+// pair of the token enters out[t][h] exactly once. A host-side pair's weight
+// row is replaced by a dummy row of the activation buffer (always allocated,
+// at least one weight row long) so that every load of a group is issued back
+// to back. LDS holds G * I floats; chunk c of a row (EPC elements, Q = EPC/4
+// float4 quads) keeps quad d at float4 slot c*Q + (d ^ (c % Q)), so the
+// wave's 16-byte reads of one quad index hit consecutive bank groups.
+template <int WDT, int NCH, int R, int G, bool T1, bool HOST, bool FULL, bool STAGE>
+__global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
+    constexpr int EPC = Fmt<WDT>::EPC, Q = EPC / 4;
+    extern __shared__ float4 s_act[]; // [G][I/4]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row0 = (blockIdx.x * 4 + wave) * R;
+    const int H = a.H, I = a.I, k = a.k, I4 = I / 4;
     const int rbi = row_bytes<WDT>(I), n16 = rbi >> 4;
-    const uint64_t down_off = 2ull * I * row_bytes<WDT>(H) + (uint64_t)row * rbi;
-    const uint64_t dsc_off = 3ull * I * row_bytes<WDT>(H) + 2ull * I * (H / 32) + (uint64_t)row * (I / 32);
-    int rw[G], pr[G];
-    float wt[G];
+    const uint64_t down_off = 2ull * I * row_bytes<WDT>(H) + (uint64_t)row0 * rbi;
+    const uint64_t dsc_off = 3ull * I * row_bytes<WDT>(H) + 2ull * I * (H / 32) + (uint64_t)row0 * (I / 32);
+    const float4* act4 = reinterpret_cast<const float4*>(a.act);
+    const int nt = T1 ? 1 : a.T;
+    for (int t = 0; t < nt; ++t) {
+        float acc[R];
 #pragma unroll
-    for (int jj = 0; jj < G; ++jj) { // pairs past k repeat the last pair with weight 0
-        pr[jj] = min(t * k + j0 + jj, last);
-        rw[jj] = a.rewritten[pr[jj]];
-        wt[jj] = a.w[pr[jj]];
-        if (j0 + jj >= k) wt[jj] = 0.f;
-    }
-    // weight rows; a host-side pair reads a dummy row of the activation buffer
-    // (always allocated, larger than one weight row) and is discarded below, so
-    // every load of the group is issued back to back
-    uint4 wd[G][NCH];
-    uint32_t sd[G][NCH];
+        for (int r = 0; r < R; ++r) acc[r] = 0.f;
+        for (int j0 = 0; j0 < k; j0 += G) {
+            const int ng = min(G, k - j0); // uniform
+            // one vector load per index array (lane j: pair j0 + j), then broadcasts
+            const int pl = t * k + min(j0 + lane, k - 1);
+            const int rw_l = a.rewritten[pl];
+            const float w_l = a.w[pl];
+            int rw[G];
+            float wt[G];
 #pragma unroll
-    for (int jj = 0; jj < G; ++jj) {
-        const uint8_t* base = a.slots + (uint64_t)(HOST && rw[jj] < 0 ? 0 : rw[jj]) * a.expert_bytes;
-        const uint8_t* rowp = base + down_off;
-        const uint8_t* scp = base + dsc_off;
-        if (HOST && rw[jj] < 0) rowp = scp = reinterpret_cast<const uint8_t*>(a.act);
+            for (int jj = 0; jj < G; ++jj) {
+                rw[jj] = __builtin_amdgcn_readlane(rw_l, jj);
+                wt[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), jj));
+            }
+            uint4 wd[G][R][NCH];
+            uint32_t sd[G][R][NCH];
 #pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-            const int c = lane + 64 * q;
-            if (c < n16) {
-                wd[jj][q] = load_stream(rowp + 16ull * c);
-                if (WDT == EC_DT_MXFP4) sd[jj][q] = scp[c];
+            for (int jj = 0; jj < G; ++jj) {
+                if (jj >= ng) break;
+                const bool hp = HOST && rw[jj] < 0;
+                const uint8_t* base = a.slots + (uint64_t)(hp ? 0 : rw[jj]) * a.expert_bytes;
+                const uint8_t* rowp = hp ? reinterpret_cast<const uint8_t*>(a.act) : base + down_off;
+                const uint8_t* scp = hp ? reinterpret_cast<const uint8_t*>(a.act) : base + dsc_off;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int q = 0; q < NCH; ++q) {
+                        const int c = lane + 64 * q;
+                        if (FULL || c < n16) {
+                            wd[jj][r][q] = load_stream(rowp + (hp ? 0 : (uint64_t)r * rbi) + 16ull * c);
+                            if (WDT == EC_DT_MXFP4) sd[jj][r][q] = scp[(hp ? 0 : r * (I / 32)) + c];
+                        }
+                    }
+            }
+            // activations: staged in LDS (the previous group's reads are done first), or,
+            // when STAGE is off, loaded into registers right behind the weights
+            float ar[STAGE ? 1 : G][NCH][STAGE ? 1 : EPC];
+            if constexpr (STAGE) {
+                __syncthreads();
+                for (int i = tid; i < ng * I4; i += 256) {
+                    const int jj = i / I4, e4 = i - jj * I4;
+                    const int c = e4 / Q, d = e4 - c * Q;
+                    s_act[jj * I4 + c * Q + (d ^ (c % Q))] = act4[(int64_t)(t * k + j0 + jj) * I4 + e4];
+                }
+                __syncthreads();
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < G; ++jj) {
+                    if (jj >= ng) break;
+#pragma unroll
+                    for (int q = 0; q < NCH; ++q) {
+                        const int c = lane + 64 * q;
+                        if (FULL || c < n16) load_vec<EPC>(a.act, (int64_t)(t * k + j0 + jj) * I + (int64_t)c * EPC, false, ar[jj][q]);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jj = 0; jj < G; ++jj) {
+                if (jj >= ng) break;
+                const bool hp = HOST && rw[jj] < 0;
+#pragma unroll
+                for (int q = 0; q < NCH; ++q) {
+                    const int c = lane + 64 * q;
+                    if (!FULL && c >= n16) continue;
+                    float av[EPC];
+                    if constexpr (STAGE) {
+#pragma unroll
+                        for (int d = 0; d < Q; ++d) {
+                            const float4 f = s_act[jj * I4 + c * Q + (d ^ (c % Q))];
+                            av[4 * d] = f.x; av[4 * d + 1] = f.y; av[4 * d + 2] = f.z; av[4 * d + 3] = f.w;
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) av[e] = ar[STAGE ? 0 : jj][q][STAGE ? 0 : e];
+                    }
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const float part = chunk_dot<WDT>(wd[jj][r][q], WDT == EC_DT_MXFP4 ? sd[jj][r][q] : 0u, av, 0.f);
+                        // a host-side pair's dummy row may decode to non-finite values: select, not multiply by 0
+                        const float nacc = fmaf(wt[jj], part, acc[r]);
+                        acc[r] = hp ? acc[r] : nacc;
+                    }
+                }
+            }
+        }
+        float hs[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) hs[r] = 0.f;
+        if (HOST) {
+            // lane j < k carries pair j's host-side term (zero for cache-side pairs)
+            const int pj = t * k + min(lane, k - 1);
+            const bool hj = lane < k && a.rewritten[pj] < 0;
+            const float wj = a.w[pj];
+#pragma unroll
+            for (int r = 0; r < R; ++r) hs[r] = hj ? wj * a.y_host[(int64_t)pj * H + row0 + r] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float y = wave_sum(acc[r]);
+            if (HOST) y += wave_sum(hs[r]);
+            if (lane == 0) {
+                if (WDT == EC_DT_F32) reinterpret_cast<float*>(a.out)[(int64_t)t * H + row0 + r] = y;
+                else reinterpret_cast<uint16_t*>(a.out)[(int64_t)t * H + row0 + r] = f32_to_bf16(y);
             }
         }
     }
-    float av[G][NCH][EPC];
-#pragma unroll
-    for (int jj = 0; jj < G; ++jj)
-#pragma unroll
-        for (int q = 0; q < NCH; ++q) {
-            const int c = lane + 64 * q;
-            if (c < n16) load_vec<EPC>(a.act, (int64_t)pr[jj] * I + (int64_t)c * EPC, false, av[jj][q]);
-        }
-    float acc = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < G; ++jj) {
-        float part = 0.f;
-#pragma unroll
-        for (int q = 0; q < NCH; ++q)
-            if (lane + 64 * q < n16)
-                part = chunk_dot<WDT>(wd[jj][q], WDT == EC_DT_MXFP4 ? sd[jj][q] : 0u, av[jj][q], part);
-        float y = wave_sum(part);
-        if (HOST) {
-            const float yh = a.y_host[(int64_t)pr[jj] * H + row];
-            y = rw[jj] >= 0 ? y : yh;
-        }
-        acc = fmaf(wt[jj], y, acc);
-    }
-    return acc;
-}
-
-template <int WDT, int NCH, bool T1, bool HOST>
-__global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
-    constexpr int EPC = Fmt<WDT>::EPC;
-    constexpr int G = 128 / (NCH * EPC) >= 8 ? 8 : (128 / (NCH * EPC) >= 1 ? 128 / (NCH * EPC) : 1);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = blockIdx.x * 4 + wave;
-    if (row >= a.H) return;
-    auto token = [&](int t) {
-        float acc = down_group<WDT, NCH, HOST>(a, t, 0, row, lane);
-        for (int j0 = G; j0 < a.k; j0 += G) acc += down_group<WDT, NCH, HOST>(a, t, j0, row, lane);
-        if (lane == 0) {
-            if (WDT == EC_DT_F32) reinterpret_cast<float*>(a.out)[(int64_t)t * a.H + row] = acc;
-            else reinterpret_cast<uint16_t*>(a.out)[(int64_t)t * a.H + row] = f32_to_bf16(acc);
-        }
-    };
-    if (T1) token(0);
-    else for (int t = 0; t < a.T; ++t) token(t);
 }
 
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s) {
@@ -304,61 +421,108 @@ void launch_fill(const DecodeArgs& a, int K, hipStream_t s) {
     hipLaunchKernelGGL(fill_kernel, dim3(K * chunks), dim3(256), 0, s, a, chunks);
 }
 
-template <int WDT> static int nch_for(int n) {
-    const int rb = WDT == EC_DT_F32 ? n * 4 : WDT == EC_DT_BF16 ? n * 2 : n / 2;
-    return (rb + 1023) / 1024;
+template <int WDT> static int row16(int n) { return (WDT == EC_DT_F32 ? n * 4 : WDT == EC_DT_BF16 ? n * 2 : n / 2) / 16; }
+
+// 16-byte chunks per lane, rounded up to 1, 2, 4 or 8; FULL when they tile the row exactly.
+static int nch_of(int n16) { const int c = (n16 + 63) / 64; return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 8; }
+
+template <int WDT, int NCH, int RW>
+static void gu_go(const DecodeArgs& a, bool full, hipStream_t s) {
+    const int chunks = a.I / (kGuWaves * RW);
+    const dim3 grid(a.U_max * chunks), blk(256);
+    if (full) {
+        if (a.T == 1) hipLaunchKernelGGL((gu_kernel<WDT, NCH, RW, true, true>), grid, blk, 0, s, a, chunks);
+        else hipLaunchKernelGGL((gu_kernel<WDT, NCH, RW, false, true>), grid, blk, 0, s, a, chunks);
+    } else {
+        if (a.T == 1) hipLaunchKernelGGL((gu_kernel<WDT, NCH, RW, true, false>), grid, blk, 0, s, a, chunks);
+        else hipLaunchKernelGGL((gu_kernel<WDT, NCH, RW, false, false>), grid, blk, 0, s, a, chunks);
+    }
 }
 
-#define EC_DISPATCH_NCH(KERNEL, WDT, NCH, GRID, ...)                                              \
-    switch (NCH) {                                                                                \
-    case 1: hipLaunchKernelGGL((KERNEL<WDT, 1>), GRID, dim3(256), 0, s, __VA_ARGS__); break;      \
-    case 2: hipLaunchKernelGGL((KERNEL<WDT, 2>), GRID, dim3(256), 0, s, __VA_ARGS__); break;      \
-    case 3: case 4: hipLaunchKernelGGL((KERNEL<WDT, 4>), GRID, dim3(256), 0, s, __VA_ARGS__); break; \
-    default: hipLaunchKernelGGL((KERNEL<WDT, 8>), GRID, dim3(256), 0, s, __VA_ARGS__); break;     \
+template <int WDT, int RW>
+static void gu_nch(const DecodeArgs& a, hipStream_t s) {
+    const int n16 = row16<WDT>(a.H), nch = nch_of(n16);
+    const bool full = n16 == 64 * nch;
+    switch (nch) {
+    case 1: gu_go<WDT, 1, RW>(a, full, s); break;
+    case 2: gu_go<WDT, 2, RW>(a, full, s); break;
+    case 4: gu_go<WDT, 4, RW>(a, full, s); break;
+    default: gu_go<WDT, 8, RW>(a, full, s); break;
     }
+}
 
+// I is a multiple of 64, so I / (4 RW) blocks cover every row exactly.
 void launch_gu(const DecodeArgs& a, hipStream_t s) {
-    const int chunks = (a.I + kGuRows - 1) / kGuRows;
-    const dim3 grid(a.U_max * chunks);
-#define EC_GU(WDT, NCH)                                                                            \
-    do {                                                                                           \
-        if (a.T == 1) hipLaunchKernelGGL((gu_kernel<WDT, NCH, true>), grid, dim3(256), 0, s, a, chunks); \
-        else hipLaunchKernelGGL((gu_kernel<WDT, NCH, false>), grid, dim3(256), 0, s, a, chunks);  \
-    } while (0)
-#define EC_GU_NCH(WDT, N)                                                                          \
-    switch (N) {                                                                                   \
-    case 1: EC_GU(WDT, 1); break;                                                                  \
-    case 2: EC_GU(WDT, 2); break;                                                                  \
-    case 3: case 4: EC_GU(WDT, 4); break;                                                          \
-    default: EC_GU(WDT, 8); break;                                                                 \
-    }
-    if (a.wdtype == EC_DT_F32) { EC_GU_NCH(EC_DT_F32, nch_for<EC_DT_F32>(a.H)) }
-    else if (a.wdtype == EC_DT_BF16) { EC_GU_NCH(EC_DT_BF16, nch_for<EC_DT_BF16>(a.H)) }
-    else { EC_GU_NCH(EC_DT_MXFP4, nch_for<EC_DT_MXFP4>(a.H)) }
-#undef EC_GU_NCH
-#undef EC_GU
+    if (a.wdtype == EC_DT_F32) gu_nch<EC_DT_F32, 1>(a, s);
+    else if (a.wdtype == EC_DT_BF16) gu_nch<EC_DT_BF16, 1>(a, s);
+    else gu_nch<EC_DT_MXFP4, 2>(a, s);
 }
 
-void launch_down(const DecodeArgs& a, hipStream_t s) {
-    const dim3 grid((a.H + 3) / 4);
-#define EC_DOWN(WDT, NCH)                                                                          \
-    do {                                                                                           \
-        if (a.T == 1 && !a.host_pairs) hipLaunchKernelGGL((down_kernel<WDT, NCH, true, false>), grid, dim3(256), 0, s, a); \
-        else if (a.T == 1) hipLaunchKernelGGL((down_kernel<WDT, NCH, true, true>), grid, dim3(256), 0, s, a); \
-        else hipLaunchKernelGGL((down_kernel<WDT, NCH, false, true>), grid, dim3(256), 0, s, a);  \
-    } while (0)
-#define EC_DOWN_NCH(WDT, N)                                                                        \
-    switch (N) {                                                                                   \
-    case 1: EC_DOWN(WDT, 1); break;                                                                \
-    case 2: EC_DOWN(WDT, 2); break;                                                                \
-    case 3: case 4: EC_DOWN(WDT, 4); break;                                                        \
-    default: EC_DOWN(WDT, 8); break;                                                               \
+template <int WDT, int NCH, int R, int G, bool STAGE>
+static void down_go2(const DecodeArgs& a, bool full, hipStream_t s) {
+    const dim3 blk(256), grid(a.H / (4 * R));
+    const size_t lds = STAGE ? (size_t)G * a.I * sizeof(float) : 0;
+    if (a.T == 1) {
+#define EC_D1(HOST, FULL) hipLaunchKernelGGL((down_kernel<WDT, NCH, R, G, true, HOST, FULL, STAGE>), grid, blk, lds, s, a)
+        if constexpr (WDT != EC_DT_F32) { // f32 (small test shapes) only takes the guarded form
+            if (full) {
+                if (a.host_pairs) EC_D1(true, true); else EC_D1(false, true);
+                return;
+            }
+        }
+        if (a.host_pairs) EC_D1(true, false); else EC_D1(false, false);
+#undef EC_D1
+    } else if constexpr (STAGE) {
+        if constexpr (WDT != EC_DT_F32) {
+            if (full) {
+                hipLaunchKernelGGL((down_kernel<WDT, NCH, R, G, false, true, true, true>), grid, blk, lds, s, a);
+                return;
+            }
+        }
+        hipLaunchKernelGGL((down_kernel<WDT, NCH, R, G, false, true, false, true>), grid, blk, lds, s, a);
     }
-    if (a.wdtype == EC_DT_F32) { EC_DOWN_NCH(EC_DT_F32, nch_for<EC_DT_F32>(a.I)) }
-    else if (a.wdtype == EC_DT_BF16) { EC_DOWN_NCH(EC_DT_BF16, nch_for<EC_DT_BF16>(a.I)) }
-    else { EC_DOWN_NCH(EC_DT_MXFP4, nch_for<EC_DT_MXFP4>(a.I)) }
-#undef EC_DOWN_NCH
-#undef EC_DOWN
+}
+
+// Activations go through LDS when each lane's slice is wide (MXFP4: 32 floats per
+// 16-byte chunk) or the step has several tokens; batch-1 bf16/f32 rows keep them
+// in registers, issued with the weights (no block barrier on the path).
+template <int WDT, int NCH, int R, int G>
+static void down_go(const DecodeArgs& a, bool full, hipStream_t s) {
+    if constexpr (WDT == EC_DT_MXFP4) down_go2<WDT, NCH, R, G, true>(a, full, s);
+    else if (a.T != 1) down_go2<WDT, NCH, R, G, true>(a, full, s);
+    else down_go2<WDT, NCH, R, G, false>(a, full, s);
+}
+
+// Pairs per group: up to 8 (fewer for small top-k), G * I floats of LDS at most
+// 64 KiB, and at most 32 weight chunks in registers per lane (G * R * NCH).
+template <int WDT, int NCH, int R>
+static void down_g(const DecodeArgs& a, bool full, hipStream_t s) {
+    int g = a.k <= 2 ? 2 : a.k <= 4 ? 4 : 8;
+    while (g > 2 && (g * a.I > 16384 || g * R * NCH > 32)) g >>= 1;
+    static_assert(2 * R * NCH <= 32, "weight chunks per lane");
+    if (g == 8 && 8 * R * NCH <= 32) down_go<WDT, NCH, R, (8 * R * NCH <= 32 ? 8 : 2)>(a, full, s);
+    else if (g >= 4 && 4 * R * NCH <= 32) down_go<WDT, NCH, R, (4 * R * NCH <= 32 ? 4 : 2)>(a, full, s);
+    else down_go<WDT, NCH, R, 2>(a, full, s);
+}
+
+template <int WDT, int R>
+static void down_nch(const DecodeArgs& a, hipStream_t s) {
+    const int n16 = row16<WDT>(a.I), nch = nch_of(n16);
+    const bool full = n16 == 64 * nch;
+    switch (nch) {
+    case 1: down_g<WDT, 1, R>(a, full, s); break;
+    case 2: down_g<WDT, 2, R>(a, full, s); break;
+    case 4: down_g<WDT, 4, R>(a, full, s); break;
+    default: down_g<WDT, 8, (R > 2 ? 2 : R)>(a, full, s); break;
+    }
+}
+
+// H is a multiple of 64, so H / (4 R) blocks cover every row exactly. MXFP4 rows
+// are short in bytes, so more of them share one staging of the activations.
+void launch_down(const DecodeArgs& a, hipStream_t s) {
+    if (a.wdtype == EC_DT_F32) down_nch<EC_DT_F32, 1>(a, s);
+    else if (a.wdtype == EC_DT_BF16) down_nch<EC_DT_BF16, 2>(a, s);
+    else down_nch<EC_DT_MXFP4, 4>(a, s);
 }
 
 } // namespace ec
