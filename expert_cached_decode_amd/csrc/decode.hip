@@ -184,7 +184,9 @@ __global__ __launch_bounds__(256) void fill_kernel(DecodeArgs a, int chunks) {
 
 // ---------------------------------------------------------------------------
 // Gate/up GEMV: for each cache-side expert g and each token routed to it,
-// act[pair][i] = silu(W_gate[i] . x) * (W_up[i] . x). A wavefront owns RW row
+// act[pair][i] = silu(W_gate[i] . x) * (W_up[i] . x), stored as f32 for f32
+// weights and rounded to bf16 otherwise (the precision the down projection
+// consumes on the matrix-core prefill path as well). A wavefront owns RW row
 // pairs of one expert; each lane holds NCH 16-byte chunks of every row in
 // registers, so one expert's weights are read once whatever its token count.
 // Grid: U_max x (I / (4 RW)); blocks past the step's cache-side count exit.
@@ -270,8 +272,9 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
             accg = wave_sum(accg);
             accu = wave_sum(accu);
             if (lane == 0) {
-                const float sv = accg / (1.f + expf(-accg));
-                a.act[(int64_t)pair * I + row0 + rr] = sv * accu;
+                const float h = accg / (1.f + expf(-accg)) * accu;
+                if constexpr (WDT == EC_DT_F32) a.act[(int64_t)pair * I + row0 + rr] = h;
+                else reinterpret_cast<uint16_t*>(a.act)[(int64_t)pair * I + row0 + rr] = f32_to_bf16(h);
             }
         }
     }
@@ -281,28 +284,32 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
 // Down GEMV + exact merge. A block of four wavefronts owns 4 R output rows h.
 // For each token t and each group of G of its pairs, the block first issues
 // the loads of its weight rows W_down,e(t,j)[h] (the group's indices come from
-// one vector load), then stages the group's activation vectors act[t,j] in LDS
-// (each is read from L2 once per block instead of once per row), and each lane
-// accumulates w[t,j] * (its slice of W_down[h] . act[t,j]) in j order; one
-// wave reduction per row gives the cache-side sum. Host-side pairs (HOST) add
+// one vector load), then the group's activation vectors act[t,j]: staged in
+// LDS (STAGE: each is read from L2 once per block instead of once per row) or
+// loaded into registers right behind the weights. Each lane accumulates
+// w[t,j] * (its slice of W_down[h] . act[t,j]) in j order; one wave reduction
+// per row gives the cache-side sum. Host-side pairs (HOST) add
 // w[t,j] * y_host[t,j][h] through a second fixed-order wave reduction, so every
 // pair of the token enters out[t][h] exactly once. A host-side pair's weight
 // row is replaced by a dummy row of the activation buffer (always allocated,
 // at least one weight row long) so that every load of a group is issued back
-// to back. LDS holds G * I floats; chunk c of a row (EPC elements, Q = EPC/4
-// float4 quads) keeps quad d at float4 slot c*Q + (d ^ (c % Q)), so the
-// wave's 16-byte reads of one quad index hit consecutive bank groups.
+// to back. Activations are f32 (f32 weights) or bf16 (else, through the dot2
+// unit). In LDS, chunk c of a row (EPC elements, QB 16-byte quads) keeps quad
+// d at slot c*QB + (d ^ (c % QB)), so the wave's 16-byte reads of one quad
+// index hit consecutive bank groups.
 template <int WDT, int NCH, int R, int G, bool T1, bool HOST, bool FULL, bool STAGE>
 __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
-    constexpr int EPC = Fmt<WDT>::EPC, Q = EPC / 4;
-    extern __shared__ float4 s_act[]; // [G][I/4]
+    constexpr int EPC = Fmt<WDT>::EPC;
+    constexpr int AB = WDT == EC_DT_F32 ? 4 : 2; // bytes per activation element
+    constexpr int QB = EPC * AB / 16;            // 16-byte quads per chunk
+    extern __shared__ uint4 s_q[];               // [G][I * AB / 16]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row0 = (blockIdx.x * 4 + wave) * R;
-    const int H = a.H, I = a.I, k = a.k, I4 = I / 4;
+    const int H = a.H, I = a.I, k = a.k, IQ = I * AB / 16;
     const int rbi = row_bytes<WDT>(I), n16 = rbi >> 4;
     const uint64_t down_off = 2ull * I * row_bytes<WDT>(H) + (uint64_t)row0 * rbi;
     const uint64_t dsc_off = 3ull * I * row_bytes<WDT>(H) + 2ull * I * (H / 32) + (uint64_t)row0 * (I / 32);
-    const float4* act4 = reinterpret_cast<const float4*>(a.act);
+    const uint4* actq = reinterpret_cast<const uint4*>(a.act);
     const int nt = T1 ? 1 : a.T;
     for (int t = 0; t < nt; ++t) {
         float acc[R];
@@ -341,15 +348,13 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
                         }
                     }
             }
-            // activations: staged in LDS (the previous group's reads are done first), or,
-            // when STAGE is off, loaded into registers right behind the weights
-            float ar[STAGE ? 1 : G][NCH][STAGE ? 1 : EPC];
+            uint4 ar[STAGE ? 1 : G][NCH][QB];
             if constexpr (STAGE) {
-                __syncthreads();
-                for (int i = tid; i < ng * I4; i += 256) {
-                    const int jj = i / I4, e4 = i - jj * I4;
-                    const int c = e4 / Q, d = e4 - c * Q;
-                    s_act[jj * I4 + c * Q + (d ^ (c % Q))] = act4[(int64_t)(t * k + j0 + jj) * I4 + e4];
+                __syncthreads(); // the previous group's reads are done
+                for (int i = tid; i < ng * IQ; i += 256) {
+                    const int jj = i / IQ, e = i - jj * IQ;
+                    const int c = e / QB, d = e - c * QB;
+                    s_q[jj * IQ + c * QB + (d ^ (c % QB))] = actq[(int64_t)(t * k + j0 + jj) * IQ + e];
                 }
                 __syncthreads();
             } else {
@@ -359,7 +364,9 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
                         const int c = lane + 64 * q;
-                        if (FULL || c < n16) load_vec<EPC>(a.act, (int64_t)(t * k + j0 + jj) * I + (int64_t)c * EPC, false, ar[jj][q]);
+                        if (FULL || c < n16)
+#pragma unroll
+                            for (int d = 0; d < QB; ++d) ar[jj][q][d] = actq[(int64_t)(t * k + j0 + jj) * IQ + c * QB + d];
                     }
                 }
             }
@@ -372,20 +379,21 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
                 for (int q = 0; q < NCH; ++q) {
                     const int c = lane + 64 * q;
                     if (!FULL && c >= n16) continue;
-                    float av[EPC];
-                    if constexpr (STAGE) {
+                    uint32_t aw[QB * 4];
 #pragma unroll
-                        for (int d = 0; d < Q; ++d) {
-                            const float4 f = s_act[jj * I4 + c * Q + (d ^ (c % Q))];
-                            av[4 * d] = f.x; av[4 * d + 1] = f.y; av[4 * d + 2] = f.z; av[4 * d + 3] = f.w;
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < EPC; ++e) av[e] = ar[STAGE ? 0 : jj][q][STAGE ? 0 : e];
+                    for (int d = 0; d < QB; ++d) {
+                        const uint4 u = STAGE ? s_q[jj * IQ + c * QB + (d ^ (c % QB))] : ar[STAGE ? 0 : jj][q][d];
+                        aw[4 * d] = u.x; aw[4 * d + 1] = u.y; aw[4 * d + 2] = u.z; aw[4 * d + 3] = u.w;
                     }
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        const float part = chunk_dot<WDT>(wd[jj][r][q], WDT == EC_DT_MXFP4 ? sd[jj][r][q] : 0u, av, 0.f);
+                        float part;
+                        if constexpr (WDT == EC_DT_F32) {
+                            const float av[4] = {__uint_as_float(aw[0]), __uint_as_float(aw[1]), __uint_as_float(aw[2]), __uint_as_float(aw[3])};
+                            part = chunk_dot<WDT>(wd[jj][r][q], 0u, av, 0.f);
+                        } else {
+                            part = chunk_dot_packed<WDT>(wd[jj][r][q], WDT == EC_DT_MXFP4 ? sd[jj][r][q] : 0u, aw, 0.f);
+                        }
                         // a host-side pair's dummy row may decode to non-finite values: select, not multiply by 0
                         const float nacc = fmaf(wt[jj], part, acc[r]);
                         acc[r] = hp ? acc[r] : nacc;
@@ -461,7 +469,7 @@ void launch_gu(const DecodeArgs& a, hipStream_t s) {
 template <int WDT, int NCH, int R, int G, bool STAGE>
 static void down_go2(const DecodeArgs& a, bool full, hipStream_t s) {
     const dim3 blk(256), grid(a.H / (4 * R));
-    const size_t lds = STAGE ? (size_t)G * a.I * sizeof(float) : 0;
+    const size_t lds = STAGE ? (size_t)G * a.I * (WDT == EC_DT_F32 ? 4 : 2) : 0;
     if (a.T == 1) {
 #define EC_D1(HOST, FULL) hipLaunchKernelGGL((down_kernel<WDT, NCH, R, G, true, HOST, FULL, STAGE>), grid, blk, lds, s, a)
         if constexpr (WDT != EC_DT_F32) { // f32 (small test shapes) only takes the guarded form
@@ -483,9 +491,9 @@ static void down_go2(const DecodeArgs& a, bool full, hipStream_t s) {
     }
 }
 
-// Activations go through LDS when each lane's slice is wide (MXFP4: 32 floats per
-// 16-byte chunk) or the step has several tokens; batch-1 bf16/f32 rows keep them
-// in registers, issued with the weights (no block barrier on the path).
+// Activations go through LDS when each lane's slice is wide (MXFP4: 32 elements
+// per 16-byte chunk) or the step has several tokens; batch-1 bf16/f32 rows keep
+// them in registers, issued with the weights (no block barrier on the path).
 template <int WDT, int NCH, int R, int G>
 static void down_go(const DecodeArgs& a, bool full, hipStream_t s) {
     if constexpr (WDT == EC_DT_MXFP4) down_go2<WDT, NCH, R, G, true>(a, full, s);
@@ -493,12 +501,13 @@ static void down_go(const DecodeArgs& a, bool full, hipStream_t s) {
     else down_go2<WDT, NCH, R, G, false>(a, full, s);
 }
 
-// Pairs per group: up to 8 (fewer for small top-k), G * I floats of LDS at most
-// 64 KiB, and at most 32 weight chunks in registers per lane (G * R * NCH).
+// Pairs per group: up to 8 (fewer for small top-k), G activation rows of LDS at
+// most 64 KiB, and at most 32 weight chunks in registers per lane (G * R * NCH).
 template <int WDT, int NCH, int R>
 static void down_g(const DecodeArgs& a, bool full, hipStream_t s) {
+    const int ab = WDT == EC_DT_F32 ? 4 : 2;
     int g = a.k <= 2 ? 2 : a.k <= 4 ? 4 : 8;
-    while (g > 2 && (g * a.I > 16384 || g * R * NCH > 32)) g >>= 1;
+    while (g > 2 && (g * a.I * ab > 65536 || g * R * NCH > 32)) g >>= 1;
     static_assert(2 * R * NCH <= 32, "weight chunks per lane");
     if (g == 8 && 8 * R * NCH <= 32) down_go<WDT, NCH, R, (8 * R * NCH <= 32 ? 8 : 2)>(a, full, s);
     else if (g >= 4 && 4 * R * NCH <= 32) down_go<WDT, NCH, R, (4 * R * NCH <= 32 ? 4 : 2)>(a, full, s);
