@@ -65,15 +65,14 @@ def workload(args):
     else:
         cfg = STRESS.with_(T=args.tokens or 16)
         text = ("stress: DeepSeek-V4-Flash shapes (MXFP4), 4096-slot cache, K = 64")
-    if args.bpbh:
+    if args.bpbh and args.bpbh != "calibrate":
         bp, bh = (int(v) for v in args.bpbh.split(":"))
         cfg = cfg.with_(bp=bp, bh=bh)
     if args.p is not None:
         cfg = cfg.with_(p=args.p)
     if args.tokens and args.workload != "stress":
         cfg = cfg.with_(T=args.tokens)
-    text += ", batch %d, %d%% step-to-step routing overlap, BP:BH %d:%d" % (cfg.T, round(100 * cfg.p), cfg.bp,
-                                                                             cfg.bh)
+    text += ", batch %d, %d%% step-to-step routing overlap" % (cfg.T, round(100 * cfg.p))
     return cfg, text
 
 
@@ -92,7 +91,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", choices=["qwen", "dsv4", "stress"], default="qwen")
-    ap.add_argument("--bpbh", default=None, help="BP:BH integers, e.g. 300:1000")
+    ap.add_argument("--bpbh", default=None,
+                    help="BP:BH integers, e.g. 300:1000, or 'calibrate' (measured on this machine and applied)")
     ap.add_argument("--p", type=float, default=None, help="step-to-step routing overlap")
     ap.add_argument("--tokens", type=int, default=0, help="decode batch T")
     ap.add_argument("--eager", action="store_true", help="no graph capture")
@@ -138,6 +138,12 @@ def main():
     ctx = EC.Context(L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype, max_tokens=T, cache_slots=cfg.slots,
                      victim_k=cfg.K, bp=cfg.bp, bh=cfg.bh, host_pool=pool, prefill_max_tokens=prefill_T,
                      pool_layers=P)
+    # measured BP and BH (MB/s): applied with --bpbh calibrate, else reported only
+    bp_meas, bh_meas = ctx.calibrate_bandwidth(8, apply=(args.bpbh == "calibrate"))
+    log("calibration: BP %d MB/s over the link, BH %d MB/s on the host branch%s"
+        % (bp_meas, bh_meas, " (applied)" if args.bpbh == "calibrate" else ""))
+    bp_used, bh_used = (bp_meas, bh_meas) if args.bpbh == "calibrate" else (cfg.bp, cfg.bh)
+    text += ", BP:BH %d:%d%s" % (bp_used, bh_used, " (measured)" if args.bpbh == "calibrate" else "")
 
     t0 = time.time()
     logits = torch.from_numpy(gen.decode_logits(cfg, steps=total_steps)).cuda()  # [S, L, T, E]
@@ -234,6 +240,7 @@ def main():
                         "bytes_per_launch": int(dn_bytes), "us_per_launch": round(dn_us, 3)},
         "other_kernels_us": {"ctl": round(ctl_us, 3),
                              "fill_per_expert": round(fill_ms * 1e3 / max(st2["fills"], 1), 2)},
+        "bandwidth_mbps": {"bp_measured": bp_meas, "bh_measured": bh_meas, "bp_used": bp_used, "bh_used": bh_used},
         "cache": {"miss_rate": round(st["misses"] / max(lookups, 1), 4), "fills_per_step": round(st["fills"] / K, 3),
                   "host_per_step": round(st["host"] / K, 3), "fill_link_GBs": round(fill_gbs, 2)},
     }

@@ -48,14 +48,15 @@ class ec_step_view(ctypes.Structure):
 
 class ec_stats(ctypes.Structure):
     _fields_ = [("steps", c_u64), ("hits", c_u64), ("misses", c_u64), ("fills", c_u64), ("host", c_u64),
-                ("evictions", c_u64), ("device_error", c_i32), ("slots", c_i32), ("clock", c_u64)]
+                ("evictions", c_u64), ("device_error", c_i32), ("slots", c_i32), ("clock", c_u64),
+                ("host_only", c_i32), ("reserved", c_i32)]
 
 
 _lib = None
 EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec_create", "ec_destroy",
            "ec_set_bandwidth", "moe_route", "expert_cache_step", "moe_decode_layer", "moe_prefill_layer",
            "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
-           "ec_kernel_timing", "ec_kernel_time"]
+           "ec_kernel_timing", "ec_kernel_time", "ec_calibrate_bandwidth"]
 KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
@@ -89,6 +90,7 @@ def lib():
         L.ec_debug_state.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp]
         L.ec_kernel_timing.argtypes = [c_vp, c_i32]
         L.ec_kernel_time.argtypes = [c_vp, c_i32, ctypes.POINTER(ctypes.c_double), P(c_u64), c_i32]
+        L.ec_calibrate_bandwidth.argtypes = [c_vp, c_i32, c_i32, P(ctypes.c_uint32), P(ctypes.c_uint32)]
         for f in EXPORTS:
             getattr(L, f).restype = getattr(L, f).restype or c_i32
         L.ec_strerror.restype = ctypes.c_char_p
@@ -226,6 +228,13 @@ class Context:
 
     def set_bandwidth(self, bp, bh, stream=None):
         check(lib().ec_set_bandwidth(self.handle, bp, bh, _stream(stream)), self.handle)
+
+    def calibrate_bandwidth(self, probe_experts=8, apply=True):
+        """Measure (BP, BH) in MB/s on this machine; apply them when `apply`."""
+        bp, bh = ctypes.c_uint32(), ctypes.c_uint32()
+        check(lib().ec_calibrate_bandwidth(self.handle, probe_experts, 1 if apply else 0, ctypes.byref(bp),
+                                           ctypes.byref(bh)), self.handle)
+        return bp.value, bh.value
 
     def set_prefill_overlap(self, on):
         check(lib().ec_set_prefill_overlap(self.handle, 1 if on else 0), self.handle)

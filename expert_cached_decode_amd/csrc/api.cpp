@@ -3,6 +3,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <algorithm>
+#include <thread>
+#include <mutex>
+#include <atomic>
+#include <chrono>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -19,6 +24,8 @@ thread_local std::string g_err; // last error of calls that have no context
 
 uint64_t mailbox_ints(int n) { return 8 + 3ull * n + (4 - (3ull * n) % 4) % 4; }
 
+constexpr int kDone = 32; // doorbell word the host writes (own 128-byte line)
+
 } // namespace
 
 struct ec_ctx {
@@ -28,6 +35,8 @@ struct ec_ctx {
     int P = 0; // layers held by the host pool (layer l reads pool layer l % P)
     uint32_t bp = 0, bh = 1;
     bool host_branch = false;
+    bool host_only = false;  // host pool not device-accessible: no fills, every miss on the host
+    uint32_t* probe_sink = nullptr; // never written (link probe of the BP calibration)
     uint64_t epoch = 1;
     const uint8_t* host_pool = nullptr;     // host address
     const uint8_t* host_pool_dev = nullptr; // device address of the same memory
@@ -37,12 +46,18 @@ struct ec_ctx {
     DevState st{};
     StepBufs sb{};
     float* act = nullptr;
-    float* y_host_dev = nullptr;
+    // host branch: pinned mailbox, partial sums and doorbell, with their device-visible addresses
     int32_t* mb_pinned = nullptr;
     float* y_host_pinned = nullptr;
+    uint32_t* doorbell = nullptr; // [0] mailbox sequence (GPU writes), [kDone] finished sequence (host writes)
+    int32_t* mb_dev = nullptr;
+    float* y_host_dev = nullptr;
+    uint32_t* doorbell_dev = nullptr;
     hipStream_t side = nullptr;
-    hipEvent_t ev_ctl = nullptr, ev_side = nullptr;
     HostPool* pool = nullptr;
+    std::mutex pool_mu;           // one host job at a time (poller, calibration)
+    std::thread poller;
+    std::atomic<bool> stop{false};
     std::vector<float> host_act;
     HostJob job{};
     PrefillState pf{};
@@ -60,6 +75,8 @@ struct ec_ctx {
 };
 
 static constexpr int kTimerPairs = 1024;
+
+static void host_branch_poll(ec_ctx* x);
 
 static void timers_free(ec_ctx* x);
 
@@ -181,6 +198,7 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     x->st.clock = d.take<uint64_t>(1);
     x->st.bw = d.take<uint32_t>(2);
     x->st.err = d.take<int32_t>(1);
+    x->probe_sink = d.take<uint32_t>(4);
     x->st.stats = d.take<unsigned long long>((uint64_t)x->L * ST_N);
     const int n = x->nmax, U = x->Umax;
     x->sb.ids = d.take<int32_t>(n);
@@ -197,14 +215,14 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     x->sb.rewritten = d.take<int32_t>(n);
     x->sb.gpu_desc = d.take<int4>(U);
     x->sb.tok_pairs = d.take<int32_t>(n);
+    x->st.hseq = d.take<uint32_t>(1);
     const uint64_t xbytes = (uint64_t)x->Tmax * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
     const uint64_t mb_bytes = mailbox_ints(n) * 4 + xbytes;
-    x->sb.mailbox = d.take<int32_t>((mb_bytes + 3) / 4);
     x->act = d.take<float>((uint64_t)n * x->I);
-    x->y_host_dev = d.take<float>((uint64_t)n * x->H);
     prefill_carve(x->pf, d, x->cfg.prefill_max_tokens, x->E, x->k, x->H, x->I, x->lay.layer_bytes);
     *dev_bytes = (d.off + 255) & ~255ull;
     Carve p(pin);
+    x->doorbell = p.take<uint32_t>(2 * kDone);
     x->mb_pinned = p.take<int32_t>((mb_bytes + 3) / 4);
     x->y_host_pinned = p.take<float>((uint64_t)n * x->H);
     *pin_bytes = (p.off + 255) & ~255ull;
@@ -226,8 +244,12 @@ static void init_dims(ec_ctx* x, const ec_config* c) {
 
 static bool needs_host_branch(const ec_ctx* x) {
     // q = min(m, floor(m*BP/BH), K, C - h) equals m for every step iff BP >= BH, K >= U_max and C >= U_max
-    return !(x->bp >= x->bh && x->K >= x->Umax && x->C >= x->Umax);
+    return x->host_only || !(x->bp >= x->bh && x->K >= x->Umax && x->C >= x->Umax);
 }
+
+// BP as the device sees it: without a device-accessible host pool nothing can be
+// filled, so the fill count is pinned to 0 (q = floor(m * 0 / BH)).
+static uint32_t device_bp(const ec_ctx* x, uint32_t bp) { return x->host_only ? 0u : bp; }
 
 ec_status ec_workspace_size(const ec_config* c, uint64_t* dev_bytes, uint64_t* pinned_bytes) {
     ec_status st = check_config(c);
@@ -270,10 +292,27 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
         return fail(nullptr, EC_ENOSPC, "slot pool smaller than cache_slots * expert_bytes");
     }
     carve(x, (uint8_t*)dev_ws, (uint8_t*)pinned_ws, &need_dev, &need_pin);
+    void* ws_dev = nullptr;
+    if (hipHostGetDevicePointer(&ws_dev, pinned_ws, 0) != hipSuccess || !ws_dev) {
+        (void)hipGetLastError();
+        delete x;
+        return fail(nullptr, EC_EINVAL, "pinned_ws must be pinned, device-accessible memory (hipHostMalloc)");
+    }
+    {
+        auto dev_of = [&](const void* hp) {
+            return (uint8_t*)ws_dev + ((const uint8_t*)hp - (const uint8_t*)pinned_ws);
+        };
+        x->mb_dev = (int32_t*)dev_of(x->mb_pinned);
+        x->y_host_dev = (float*)dev_of(x->y_host_pinned);
+        x->doorbell_dev = (uint32_t*)dev_of(x->doorbell);
+        std::memset(x->doorbell, 0, 2 * kDone * sizeof(uint32_t));
+    }
     void* pdev = nullptr;
     if (hipHostGetDevicePointer(&pdev, const_cast<void*>(host_pool), 0) != hipSuccess || !pdev) {
-        delete x;
-        return fail(nullptr, EC_EINVAL, "host_pool must be pinned, device-accessible memory (hipHostMalloc)");
+        // ordinary (pageable) memory, e.g. when pinning the bank failed: run host-only
+        (void)hipGetLastError();
+        pdev = nullptr;
+        x->host_only = true;
     }
     x->host_pool = (const uint8_t*)host_pool;
     x->host_pool_dev = (const uint8_t*)pdev;
@@ -281,11 +320,9 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
     x->slot_pool = (uint8_t*)slot_pool;
     x->slot_pool_bytes = slot_pool_bytes;
     x->host_branch = needs_host_branch(x);
-    if (hipStreamCreateWithFlags(&x->side, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&x->ev_ctl, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&x->ev_side, hipEventDisableTiming) != hipSuccess) {
+    if (hipStreamCreateWithFlags(&x->side, hipStreamNonBlocking) != hipSuccess) {
         delete x;
-        return fail(nullptr, EC_EHIP, "stream/event creation failed");
+        return fail(nullptr, EC_EHIP, "stream creation failed");
     }
     if (prefill_init(x->pf) != hipSuccess) {
         delete x;
@@ -298,8 +335,9 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
     launch_fill_i32((int32_t*)x->st.stats, 0, 2ll * x->L * ST_N, s);
     launch_fill_i32((int32_t*)x->sb.gpu_desc, 0, 4ll * x->Umax, s);
     launch_fill_i32(x->sb.counts, 0, CNT_N, s);
+    launch_fill_i32((int32_t*)x->st.hseq, 0, 1, s);
     launch_reset_cache(x->st, x->L, x->E, x->C, s);
-    launch_set_bw(x->st.bw, x->bp, x->bh, s);
+    launch_set_bw(x->st.bw, device_bp(x, x->bp), x->bh, s);
     prefill_reset_device(x->pf, s);
     hipError_t e = hipStreamSynchronize(s);
     if (e == hipSuccess) e = hipGetLastError();
@@ -310,6 +348,7 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
     }
     x->pool = host_pool_create(c->host_threads ? c->host_threads : 8);
     x->host_act.resize((size_t)x->nmax * x->I);
+    x->poller = std::thread(host_branch_poll, x);
     *out = x;
     return EC_OK;
 }
@@ -317,11 +356,11 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
 ec_status ec_destroy(ec_ctx* x) {
     if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
     (void)hipDeviceSynchronize();
+    x->stop.store(true);
+    if (x->poller.joinable()) x->poller.join();
     if (x->pool) host_pool_destroy(x->pool);
     timers_free(x);
     prefill_destroy(x->pf);
-    if (x->ev_ctl) (void)hipEventDestroy(x->ev_ctl);
-    if (x->ev_side) (void)hipEventDestroy(x->ev_side);
     if (x->side) (void)hipStreamDestroy(x->side);
     delete x;
     return EC_OK;
@@ -330,7 +369,7 @@ ec_status ec_destroy(ec_ctx* x) {
 ec_status ec_set_bandwidth(ec_ctx* x, uint32_t bp, uint32_t bh, void* stream) {
     if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
     if (bh < 1) return fail(x, EC_EINVAL, "BH must be >= 1");
-    launch_set_bw(x->st.bw, bp, bh, (hipStream_t)stream);
+    launch_set_bw(x->st.bw, device_bp(x, bp), bh, (hipStream_t)stream);
     HIPCHK(x, hipGetLastError());
     x->bp = bp;
     x->bh = bh;
@@ -379,8 +418,14 @@ ec_status expert_cache_step(ec_ctx* x, int32_t layer, const int32_t* ids, int32_
     return EC_OK;
 }
 
-static void host_branch_fn(void* p) {
-    ec_ctx* x = (ec_ctx*)p;
+// Host branch ("Bandwidth-adaptive execution": misses left to the host are computed
+// there in place). The cache-control kernel writes a mailbox into pinned memory and
+// rings the doorbell with a new sequence number; this thread polls the doorbell,
+// computes the host-list experts from the host pool, writes their partial sums into
+// pinned memory and publishes the finished sequence number, which the down GEMV
+// waits for before merging. No runtime callbacks or copies are on the step's path,
+// so a captured step is kernels only.
+static void host_branch_run(ec_ctx* x) {
     const int32_t* mb = x->mb_pinned;
     const int T = mb[6], layer = mb[7], nhost = mb[CNT_HOST];
     const int n = T * x->k;
@@ -394,6 +439,32 @@ static void host_branch_fn(void* p) {
     j.y = x->y_host_pinned;
     j.act = x->host_act.data();
     host_pool_run(x->pool, j);
+}
+
+static inline void cpu_relax() { __builtin_ia32_pause(); }
+
+static void host_branch_poll(ec_ctx* x) {
+    uint32_t last = 0;
+    auto active = std::chrono::steady_clock::now();
+    while (!x->stop.load(std::memory_order_relaxed)) {
+        const uint32_t sq = __atomic_load_n(&x->doorbell[0], __ATOMIC_ACQUIRE);
+        if (sq != last) {
+            {
+                std::lock_guard<std::mutex> lk(x->pool_mu);
+                host_branch_run(x);
+            }
+            __atomic_store_n(&x->doorbell[kDone], sq, __ATOMIC_RELEASE);
+            last = sq;
+            active = std::chrono::steady_clock::now();
+            continue;
+        }
+        // spin while steps are arriving, back off when idle
+        if (std::chrono::steady_clock::now() - active < std::chrono::milliseconds(20)) {
+            for (int i = 0; i < 64; ++i) cpu_relax();
+        } else {
+            std::this_thread::sleep_for(std::chrono::microseconds(50));
+        }
+    }
 }
 
 ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
@@ -410,21 +481,13 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     a.x = xin;
     a.x_bytes = (int32_t)xbytes;
     a.host_branch = x->host_branch ? 1 : 0;
+    a.sb.mailbox = x->mb_dev;
+    a.doorbell = x->doorbell_dev;
     hipEvent_t* tm = timer_next(x, 0);
     if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
     launch_ctl(a, s);
     if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
     HIPCHK(x, hipGetLastError());
-    if (x->host_branch) {
-        HIPCHK(x, hipEventRecord(x->ev_ctl, s));
-        HIPCHK(x, hipStreamWaitEvent(x->side, x->ev_ctl, 0));
-        HIPCHK(x, hipMemcpyAsync(x->mb_pinned, x->sb.mailbox, mailbox_ints(n) * 4 + xbytes, hipMemcpyDeviceToHost,
-                                 x->side));
-        HIPCHK(x, hipLaunchHostFunc(x->side, host_branch_fn, x));
-        HIPCHK(x, hipMemcpyAsync(x->y_host_dev, x->y_host_pinned, (uint64_t)n * x->H * 4, hipMemcpyHostToDevice,
-                                 x->side));
-        HIPCHK(x, hipEventRecord(x->ev_side, x->side));
-    }
     DecodeArgs d{};
     d.pool = x->host_pool_dev; d.slots = x->slot_pool; d.counts = x->sb.counts; d.fills = x->sb.fills;
     d.victims = x->sb.victims; d.gpu_desc = x->sb.gpu_desc;
@@ -433,7 +496,8 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     d.out = out; d.expert_bytes = x->lay.expert_bytes;
     d.layer = layer % x->P; d.E = x->E; d.k = x->k; d.T = T; d.H = x->H; d.I = x->I; d.wdtype = x->wdt; d.U_max = x->Umax;
     d.host_pairs = x->host_branch ? 1 : 0;
-    if (x->C > 0) {
+    d.host_done = x->doorbell_dev + kDone; d.hseq = x->st.hseq; d.err = x->st.err;
+    if (x->C > 0 && !x->host_only) {
         tm = timer_next(x, 1);
         if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
         launch_fill(d, x->K, s);
@@ -444,7 +508,6 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     launch_gu(d, s);
     if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
     HIPCHK(x, hipGetLastError());
-    if (x->host_branch) HIPCHK(x, hipStreamWaitEvent(s, x->ev_side, 0));
     tm = timer_next(x, 3);
     if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
     launch_down(d, s);
@@ -533,6 +596,74 @@ ec_status cache_rebuild(ec_ctx* x, int32_t budget_bp, void* new_slot_pool, uint6
     return EC_OK;
 }
 
+ec_status ec_calibrate_bandwidth(ec_ctx* x, int32_t probe_experts, int32_t apply, uint32_t* bp_out,
+                                 uint32_t* bh_out) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    constexpr int kReps = 3; // timed passes after one warm-up; every pass reads different experts
+    if (probe_experts < 1 || probe_experts * (kReps + 1) > x->E || probe_experts > x->nmax)
+        return fail(x, EC_EINVAL, "need 1 <= probe_experts <= min(experts / 4, max_tokens * top_k)");
+    HIPCHK(x, hipDeviceSynchronize()); // safe point
+    const uint64_t eb = x->lay.expert_bytes, bytes = (uint64_t)probe_experts * eb;
+    // BP: the fill path's source side, experts of pool layer 0 read over the link
+    double bp = 0.0;
+    if (!x->host_only) {
+        hipEvent_t e0, e1;
+        HIPCHK(x, hipEventCreate(&e0));
+        if (hipEventCreate(&e1) != hipSuccess) {
+            (void)hipEventDestroy(e0);
+            return fail(x, EC_EHIP, "event creation failed");
+        }
+        double best_ms = 1e30;
+        hipError_t e = hipSuccess;
+        for (int r = 0; r <= kReps && e == hipSuccess; ++r) { // pass 0 warms the mapping up
+            const uint8_t* src = x->host_pool_dev + (uint64_t)r * bytes; // experts [r n, (r+1) n) of layer 0
+            e = hipEventRecord(e0, x->side);
+            if (e == hipSuccess) { launch_link_probe(src, bytes, x->probe_sink, x->side); e = hipGetLastError(); }
+            if (e == hipSuccess) e = hipEventRecord(e1, x->side);
+            if (e == hipSuccess) e = hipEventSynchronize(e1);
+            float ms = 0.f;
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+            if (e == hipSuccess && r > 0 && ms > 0.f && ms < best_ms) best_ms = ms;
+        }
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(e1);
+        if (e != hipSuccess) return fail(x, EC_EHIP, std::string("link probe: ") + hipGetErrorString(e));
+        bp = bytes / (best_ms * 1e-3) / 1e6;
+    }
+    // BH: the host branch itself on experts of the last pool layer (each pass on experts
+    // not read before, so they come from memory, not from the host's caches), zero input
+    double bh = 0.0;
+    {
+        HostJob j{};
+        const int n = probe_experts;
+        const uint8_t* layer_base = x->host_pool + (uint64_t)(x->P - 1) * x->lay.layer_bytes;
+        std::vector<int32_t> rw(n);
+        for (int i = 0; i < n; ++i) rw[i] = -(1 + i);
+        std::vector<uint8_t> xz((size_t)x->H * 4, 0);
+        j.n_experts = n; j.rewritten = rw.data(); j.T = 1; j.k = n; j.H = x->H; j.I = x->I; j.wdtype = x->wdt;
+        j.x = xz.data(); j.y = x->y_host_pinned; j.act = x->host_act.data();
+        double best_s = 1e30;
+        std::lock_guard<std::mutex> lk(x->pool_mu);
+        for (int r = 0; r <= kReps; ++r) {
+            for (int i = 0; i < n; ++i) j.expert_base[i] = layer_base + (uint64_t)(x->E - 1 - r * n - i) * eb;
+            const auto t0 = std::chrono::steady_clock::now();
+            host_pool_run(x->pool, j);
+            const double sec = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+            if (r > 0 && sec > 0.0 && sec < best_s) best_s = sec;
+        }
+        bh = bytes / best_s / 1e6;
+    }
+    const uint32_t bpi = (uint32_t)std::min(bp, 4.0e9), bhi = (uint32_t)std::max(1.0, std::min(bh, 4.0e9));
+    if (bp_out) *bp_out = bpi;
+    if (bh_out) *bh_out = bhi;
+    if (apply) {
+        ec_status st = ec_set_bandwidth(x, bpi, bhi, x->side);
+        if (st) return st;
+        HIPCHK(x, hipStreamSynchronize(x->side));
+    }
+    return EC_OK;
+}
+
 uint64_t ec_epoch(const ec_ctx* x) { return x ? x->epoch : 0; }
 
 ec_status ec_get_stats(ec_ctx* x, ec_stats* o, int32_t reset) {
@@ -553,10 +684,12 @@ ec_status ec_get_stats(ec_ctx* x, ec_stats* o, int32_t reset) {
     o->device_error = err;
     o->slots = x->C;
     o->clock = clk;
+    o->host_only = x->host_only ? 1 : 0;
     if (reset) {
         launch_fill_i32((int32_t*)x->st.stats, 0, 2ll * x->L * ST_N, x->side);
         HIPCHK(x, hipStreamSynchronize(x->side));
     }
+    if (err & 2) return fail(x, EC_EDEVICE, "the host branch did not deliver its partial sums in time");
     return err ? fail(x, EC_EDEVICE, "an expert id outside [0, E) was passed to expert_cache_step") : EC_OK;
 }
 

@@ -239,7 +239,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     }
     __syncthreads();
     if (s_misc[0]) { // invalid expert id: flag it, do nothing else
-        if (tid == 0) atomicExch(a.st.err, 1);
+        if (tid == 0) atomicOr(a.st.err, 1);
         if (tid < CNT_N) a.sb.counts[tid] = 0;
         return;
     }
@@ -414,8 +414,10 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
         st[ST_HOST] += m - q; st[ST_EVICT] += n_ev;
         *a.st.clock = clk + 1;
     }
-    if (a.host_branch) {
-        // mailbox: [counts 8][host_list n][rewritten n][w n][x bytes], n = T*k
+    if (a.host_branch && m - q > 0) {
+        // mailbox in pinned host memory: [counts 8][host_list n][rewritten n][w n][x bytes], n = T*k.
+        // The host branch polls the doorbell; every writer makes its stores visible system-wide
+        // before the block barrier, then one thread publishes the new sequence number.
         int32_t* mb = a.sb.mailbox;
         if (tid == 0) {
             mb[CNT_U] = U; mb[CNT_H] = h; mb[CNT_M] = m; mb[CNT_Q] = q; mb[CNT_HOST] = m - q; mb[CNT_GPU] = n_gpu;
@@ -429,6 +431,13 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
         const uint4* xs = reinterpret_cast<const uint4*>(a.x);
         uint4* xd = reinterpret_cast<uint4*>(mb + CNT_N + 3 * n + ((4 - (3 * n) % 4) % 4));
         for (int i = tid; i < a.x_bytes / 16; i += kCtlThreads) xd[i] = xs[i];
+        __threadfence_system();
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t sq = *a.st.hseq + 1;
+            *a.st.hseq = sq;
+            __hip_atomic_store(a.doorbell, sq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
     }
 }
 

@@ -281,6 +281,31 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
 }
 
 // ---------------------------------------------------------------------------
+// Wait (block-wide) until the host branch has published the partial sums of this
+// step's mailbox: thread 0 polls the pinned "finished" sequence number until it
+// equals the step's sequence, then acquires at system scope so that the partial
+// sums the host wrote before it are seen. The wait is bounded: past the limit the
+// device error flag gets bit 1 and the kernel goes on (the output is then wrong,
+// and ec_get_stats reports it), so no wave can spin forever.
+constexpr uint32_t kHostWaitPolls = 1u << 22;
+
+__device__ __noinline__ void wait_host_branch(const DecodeArgs& a) {
+    if (threadIdx.x == 0) {
+        const uint32_t want = *a.hseq;
+        uint32_t it = 0;
+        while (__hip_atomic_load(a.host_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != want) {
+            if (++it > kHostWaitPolls) {
+                atomicOr(a.err, 2);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // Down GEMV + exact merge. A block of four wavefronts owns 4 R output rows h.
 // For each token t and each group of G of its pairs, the block first issues
 // the loads of its weight rows W_down,e(t,j)[h] (the group's indices come from
@@ -405,6 +430,7 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) hs[r] = 0.f;
         if (HOST) {
+            if (t == 0 && a.counts[CNT_HOST] > 0) wait_host_branch(a);
             // lane j < k carries pair j's host-side term (zero for cache-side pairs)
             const int pj = t * k + min(lane, k - 1);
             const bool hj = lane < k && a.rewritten[pj] < 0;
@@ -422,6 +448,31 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
             }
         }
     }
+}
+
+// Link probe for the BP calibration: reads `bytes` of the pinned host pool over
+// the host link with the fill kernel's access pattern (256 KiB per block, four
+// 16-byte loads per thread in flight) and discards them. The sink is written
+// only for an impossible checksum, so no device memory is changed.
+__global__ __launch_bounds__(256) void link_probe_kernel(const uint8_t* src, uint64_t bytes, uint32_t* sink) {
+    const uint64_t n16 = bytes / 16;
+    const uint4* p = reinterpret_cast<const uint4*>(src);
+    const uint64_t b0 = (uint64_t)blockIdx.x * (kFillChunk / 16);
+    uint64_t b1 = b0 + kFillChunk / 16;
+    if (b1 > n16) b1 = n16;
+    uint32_t acc = 0;
+    uint64_t idx = b0 + threadIdx.x;
+    for (; idx + 768 < b1; idx += 1024) {
+        const uint4 r0 = p[idx], r1 = p[idx + 256], r2 = p[idx + 512], r3 = p[idx + 768];
+        acc ^= r0.x ^ r1.y ^ r2.z ^ r3.w;
+    }
+    for (; idx < b1; idx += 256) acc ^= p[idx].x;
+    if (acc == 0x9e3779b9u && bytes == 1) sink[0] = acc;
+}
+
+void launch_link_probe(const uint8_t* src_dev, uint64_t bytes, uint32_t* sink, hipStream_t s) {
+    const uint64_t blocks = (bytes + kFillChunk - 1) / kFillChunk;
+    hipLaunchKernelGGL(link_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src_dev, bytes, sink);
 }
 
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s) {

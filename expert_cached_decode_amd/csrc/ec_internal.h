@@ -42,8 +42,9 @@ struct DevState {
     uint64_t* slot_lru;// [L*E] LRU key
     uint64_t* clock;   // [1]
     uint32_t* bw;      // [2] BP, BH
-    int32_t* err;      // [1] device error flag
+    int32_t* err;      // [1] device error flags (bit 0 bad expert id, bit 1 host branch timeout)
     unsigned long long* stats; // [L][ST_N]
+    uint32_t* hseq;    // [1] sequence number of the last mailbox handed to the host branch
 };
 
 // Per-step work buffers (fixed shape, reused by every layer).
@@ -63,7 +64,8 @@ struct StepBufs {
     int4* gpu_desc;     // [U_max] cache-side experts in uniq order: {slot, first entry in tok_pairs,
                         //          number of pairs, first pair}
     int32_t* tok_pairs; // [T_max*k] pair index t*k+j, grouped by unique expert, ascending inside
-    int32_t* mailbox;   // device staging copied to the host for the host branch (layout in host code)
+    int32_t* mailbox;   // pinned host mailbox (device-visible address) read by the host branch
+                        // (layout in host code)
 };
 
 struct CtlArgs {
@@ -74,7 +76,8 @@ struct CtlArgs {
     const void* x;       // layer input, copied into the mailbox when host_branch
     int32_t x_bytes;     // bytes of x (T*H*elem)
     int32_t layer, E, k, T, C, K;
-    int32_t host_branch; // 1: write the mailbox for the host branch
+    int32_t host_branch; // 1: hand steps with host-list experts to the host branch
+    uint32_t* doorbell;  // pinned (device-visible): [0] sequence of the last mailbox written
 };
 
 // Launchers (defined in the .hip files).
@@ -96,13 +99,17 @@ struct DecodeArgs {
     const float* w;
     const void* x;
     float* act;            // [T_max*k][I] SwiGLU activations of cache-side pairs
-    const float* y_host;   // [T_max*k][H] (device copy of host partials)
+    const float* y_host;   // [T_max*k][H] host partials, pinned (device-visible address)
     void* out;
     uint64_t expert_bytes;
     int32_t layer, E, k, T, H, I, wdtype, U_max; // layer: the host-pool layer the fills read
     int32_t host_pairs; // 1 when the step can have host-side pairs (the host branch is on)
+    const uint32_t* host_done; // pinned (device-visible): sequence of the last mailbox the host finished
+    const uint32_t* hseq;      // device: sequence of this step's mailbox
+    int32_t* err;              // device error flags
 };
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s);
+void launch_link_probe(const uint8_t* src_dev, uint64_t bytes, uint32_t* sink, hipStream_t s);
 void launch_gu(const DecodeArgs& a, hipStream_t s);
 void launch_down(const DecodeArgs& a, hipStream_t s);
 

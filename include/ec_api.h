@@ -133,6 +133,8 @@ typedef struct ec_stats {
     int32_t device_error; /* nonzero: a bad expert id was seen (EC_EDEVICE) */
     int32_t slots;        /* current C */
     uint64_t clock;       /* LRU clock: expert_cache_step calls so far */
+    int32_t host_only;    /* 1: the host pool is not device-accessible (see ec_create) */
+    int32_t reserved;
 } ec_stats;
 
 typedef struct ec_ctx ec_ctx;
@@ -149,8 +151,14 @@ ec_status ec_workspace_size(const ec_config* cfg, uint64_t* dev_bytes, uint64_t*
 /* Create a context on the current HIP device (must be gfx950).
  *   dev_ws     : dev, >= dev_bytes from ec_workspace_size, 256-byte aligned
  *   pinned_ws  : pinned, >= pinned_bytes
- *   host_pool  : pinned, [P][E][expert_bytes] expert bank (source of truth),
- *                P = pool_layers (or L)
+ *   host_pool  : [P][E][expert_bytes] expert bank (source of truth),
+ *                P = pool_layers (or L); pinned (device-accessible). Ordinary
+ *                pageable memory (a host where pinning the bank failed) is
+ *                accepted and selects host-only mode: the device sees BP = 0,
+ *                so q = 0 and every miss is computed on the host threads
+ *                ("Implementation notes": platforms that cannot pin or DMA
+ *                fall back to a CPU MoE backend); prefill uploads still work,
+ *                through staged copies. ec_stats.host_only reports the mode.
  *   slot_pool  : dev, >= cache_slots * expert_bytes (may be NULL if C = 0)
  * The cache starts cold (every slot empty), the LRU clock at 0. Enqueues its
  * initialisation on the null stream and waits for it. */
@@ -164,6 +172,25 @@ ec_status ec_destroy(ec_ctx* ctx);
  * on `stream` (capturable). Bumps the epoch when the host branch is switched
  * on or off. */
 ec_status ec_set_bandwidth(ec_ctx* ctx, uint32_t bp, uint32_t bh, void* stream);
+
+/* Measure BP and BH on this machine at a safe point ("Bandwidth-adaptive
+ * execution": the split follows the two measured bandwidths; "Elastic edge
+ * resource management": resources change at run time, so this may be
+ * repeated at later safe points). Synchronises the device; not capturable.
+ *   BP: bytes/s the fill path moves over the host link, timed by reading
+ *       probe_experts experts of pool layer 0 from the pinned pool with the
+ *       fill kernel's access pattern (read only: no slot is touched);
+ *       0 in host-only mode.
+ *   BH: bytes/s of expert weights the host branch's worker threads turn into
+ *       partial sums, timed by running that branch on probe_experts experts
+ *       of the last pool layer (zero input).
+ * One warm-up and three timed passes each, every pass on experts not read
+ * before; the best timed pass counts. Results in MB/s (10^6 bytes/s) in
+ * *bp_mbps and *bh_mbps (either may be NULL). apply != 0 also sets them as
+ * ec_set_bandwidth would (BH at least 1).
+ * 1 <= probe_experts <= min(experts / 4, max_tokens * top_k). */
+ec_status ec_calibrate_bandwidth(ec_ctx* ctx, int32_t probe_experts, int32_t apply, uint32_t* bp_mbps,
+                                 uint32_t* bh_mbps);
 
 /* Router top-k ("Why personal MoE is hard": k of E routed experts per token).
  *   logits : dev f32 [T][E], finite values

@@ -79,3 +79,8 @@ def test_route_argument_checks_enqueue_nothing():
     assert lib.moe_route(None, 1, 16, 2, None, None, None) == -1  # NULL pointers
     assert lib.ec_destroy(None) == -1
     assert lib.ec_epoch(None) == 0
+
+
+def test_calibration_rejects_a_null_context():
+    lib = E.lib()
+    assert lib.ec_calibrate_bandwidth(None, 8, 1, None, None) == -1

@@ -159,3 +159,75 @@ def test_host_pool_layer_aliasing():
         assert row_rel_err(got, ref) <= 1e-2, (s, l)
     assert ctx.stats()["host"] > 0
     ctx.close()
+
+
+def test_budget_zero_runs_every_expert_on_the_host():
+    """C = 0: q = 0 at every step, every routed expert is computed by the host branch."""
+    cfg = QWEN_DECODE.with_(L=3, slots=0, bp=1000, bh=1000)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool)
+    outs, logits = run_decode(cfg, ctx, 5, 3, 1, lambda s, l: True)
+    check_against_oracle(cfg, outs, 1e-2)
+    st = ctx.stats()
+    ref = sim_counts(cfg, logits, 3, 1, 0, cfg.K, 1000, 1000)
+    assert {k: st[k] for k in ref} == ref
+    assert st["fills"] == 0 and st["hits"] == 0 and st["host"] == st["misses"] == 5 * 3 * cfg.k
+    assert st["host_only"] == 0
+    ctx.close()
+
+
+def test_pageable_pool_selects_host_only_mode():
+    """A host pool in ordinary pageable memory (pinning failed): BP is 0 on the device,
+    nothing is filled, every expert runs on the host, outputs still match the oracle."""
+    import expert_cached_decode_amd as EC
+    cfg = QWEN_DECODE.with_(L=2, slots=32, bp=2000, bh=1000)
+    pinned = make_pool(cfg)
+    pageable = np.array(pinned.numpy(), copy=True)  # same bytes, ordinary memory
+    pinned.close()
+    ctx = EC.Context(cfg.L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype, max_tokens=1, cache_slots=cfg.slots,
+                     victim_k=cfg.K, bp=cfg.bp, bh=cfg.bh, host_pool=pageable.ctypes.data,
+                     host_pool_bytes=pageable.nbytes, host_threads=8)
+    outs, logits = run_decode(cfg, ctx, 4, 2, 1, lambda s, l: True)
+    check_against_oracle(cfg, outs, 1e-2)
+    st = ctx.stats()
+    assert st["host_only"] == 1
+    assert st["fills"] == 0 and st["hits"] == 0 and st["host"] == st["misses"] == 4 * 2 * cfg.k
+    ctx.set_bandwidth(5000, 1000)  # still no fills: the device keeps BP = 0
+    run_decode(cfg, ctx, 2, 2, 1, lambda s, l: False)
+    assert ctx.stats()["fills"] == 0
+    ctx.close()
+    del pageable
+
+
+def test_bandwidth_calibration_drives_the_split():
+    """Measured BP and BH (MB/s) are applied on the device; the step decisions then follow
+    the oracle simulator run with the same integers."""
+    cfg = QWEN_DECODE.with_(L=2, slots=24)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool, bp=1000, bh=1000)
+    bp, bh = ctx.calibrate_bandwidth(probe_experts=4, apply=True)
+    print("calibrated BP %d MB/s, BH %d MB/s" % (bp, bh))
+    assert bp > 1000 and bh >= 1
+    outs, logits = run_decode(cfg, ctx, 4, 2, 1, lambda s, l: s == 3)
+    check_against_oracle(cfg, outs, 1e-2)
+    st = ctx.stats()
+    ref = sim_counts(cfg, logits, 2, 1, cfg.slots, cfg.K, bp, bh)
+    assert {k: st[k] for k in ref} == ref
+    bp2, bh2 = ctx.calibrate_bandwidth(probe_experts=2, apply=False)  # a later safe point
+    assert bp2 > 0 and bh2 >= 1
+    ctx.close()
+
+
+def test_calibration_in_host_only_mode_reports_no_link():
+    import expert_cached_decode_amd as EC
+    cfg = TINY.with_(L=1)
+    pinned = make_pool(cfg)
+    pageable = np.array(pinned.numpy(), copy=True)
+    pinned.close()
+    ctx = EC.Context(cfg.L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype, max_tokens=1, cache_slots=cfg.slots,
+                     victim_k=cfg.K, bp=cfg.bp, bh=cfg.bh, host_pool=pageable.ctypes.data,
+                     host_pool_bytes=pageable.nbytes)
+    bp, bh = ctx.calibrate_bandwidth(probe_experts=2, apply=True)
+    assert bp == 0 and bh >= 1
+    ctx.close()
+    del pageable
