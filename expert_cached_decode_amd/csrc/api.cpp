@@ -216,6 +216,7 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     x->sb.gpu_desc = d.take<int4>(U);
     x->sb.tok_pairs = d.take<int32_t>(n);
     x->st.hseq = d.take<uint32_t>(1);
+    x->st.hseen = d.take<uint32_t>(1);
     const uint64_t xbytes = (uint64_t)x->Tmax * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
     const uint64_t mb_bytes = mailbox_ints(n) * 4 + xbytes;
     x->act = d.take<float>((uint64_t)n * x->I);
@@ -336,6 +337,7 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
     launch_fill_i32((int32_t*)x->sb.gpu_desc, 0, 4ll * x->Umax, s);
     launch_fill_i32(x->sb.counts, 0, CNT_N, s);
     launch_fill_i32((int32_t*)x->st.hseq, 0, 1, s);
+    launch_fill_i32((int32_t*)x->st.hseen, 0, 1, s);
     launch_reset_cache(x->st, x->L, x->E, x->C, s);
     launch_set_bw(x->st.bw, device_bp(x, x->bp), x->bh, s);
     prefill_reset_device(x->pf, s);
@@ -496,7 +498,7 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     d.out = out; d.expert_bytes = x->lay.expert_bytes;
     d.layer = layer % x->P; d.E = x->E; d.k = x->k; d.T = T; d.H = x->H; d.I = x->I; d.wdtype = x->wdt; d.U_max = x->Umax;
     d.host_pairs = x->host_branch ? 1 : 0;
-    d.host_done = x->doorbell_dev + kDone; d.hseq = x->st.hseq; d.err = x->st.err;
+    d.host_done = x->doorbell_dev + kDone; d.hseq = x->st.hseq; d.hseen = x->st.hseen; d.err = x->st.err;
     if (x->C > 0 && !x->host_only) {
         tm = timer_next(x, 1);
         if (tm) HIPCHK(x, hipEventRecord(tm[0], s));

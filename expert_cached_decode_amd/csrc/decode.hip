@@ -282,18 +282,23 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
 
 // ---------------------------------------------------------------------------
 // Wait (block-wide) until the host branch has published the partial sums of this
-// step's mailbox: thread 0 polls the pinned "finished" sequence number until it
-// equals the step's sequence, then acquires at system scope so that the partial
-// sums the host wrote before it are seen. The wait is bounded: past the limit the
-// device error flag gets bit 1 and the kernel goes on (the output is then wrong,
+// step's mailbox. Only block 0 polls the pinned "finished" sequence number over the
+// host link (hundreds of pollers would load the host's memory while it computes);
+// once it equals the step's sequence, block 0 relays it to a device word that the
+// other blocks poll. Every block then acquires at system scope, so the partial sums
+// the host wrote before publishing are seen. The waits are bounded: past the limit
+// the device error flag gets bit 1 and the kernel goes on (the output is then wrong,
 // and ec_get_stats reports it), so no wave can spin forever.
 constexpr uint32_t kHostWaitPolls = 1u << 22;
 
 __device__ __noinline__ void wait_host_branch(const DecodeArgs& a) {
     if (threadIdx.x == 0) {
         const uint32_t want = *a.hseq;
+        const bool relay = blockIdx.x == 0;
+        const uint32_t* flag = relay ? a.host_done : a.hseen;
         uint32_t it = 0;
-        while (__hip_atomic_load(a.host_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != want) {
+        while (relay ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != want
+                     : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
             if (++it > kHostWaitPolls) {
                 atomicOr(a.err, 2);
                 break;
@@ -301,6 +306,7 @@ __device__ __noinline__ void wait_host_branch(const DecodeArgs& a) {
             __builtin_amdgcn_s_sleep(8);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+        if (relay) __hip_atomic_store(a.hseen, want, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
 }
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
             const bool hj = lane < k && a.rewritten[pj] < 0;
             const float wj = a.w[pj];
 #pragma unroll
-            for (int r = 0; r < R; ++r) hs[r] = hj ? wj * a.y_host[(int64_t)pj * H + row0 + r] : 0.f;
+            for (int r = 0; r < R; ++r) hs[r] = hj ? wj * a.y_host[((int64_t)t * H + row0 + r) * k + min(lane, k - 1)] : 0.f;
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {

@@ -45,6 +45,7 @@ struct DevState {
     int32_t* err;      // [1] device error flags (bit 0 bad expert id, bit 1 host branch timeout)
     unsigned long long* stats; // [L][ST_N]
     uint32_t* hseq;    // [1] sequence number of the last mailbox handed to the host branch
+    uint32_t* hseen;   // [1] last finished sequence as relayed on the device
 };
 
 // Per-step work buffers (fixed shape, reused by every layer).
@@ -99,13 +100,14 @@ struct DecodeArgs {
     const float* w;
     const void* x;
     float* act;            // [T_max*k][I] SwiGLU activations of cache-side pairs
-    const float* y_host;   // [T_max*k][H] host partials, pinned (device-visible address)
+    const float* y_host;   // [T_max][H][k] host partials, pinned (device-visible address)
     void* out;
     uint64_t expert_bytes;
     int32_t layer, E, k, T, H, I, wdtype, U_max; // layer: the host-pool layer the fills read
     int32_t host_pairs; // 1 when the step can have host-side pairs (the host branch is on)
     const uint32_t* host_done; // pinned (device-visible): sequence of the last mailbox the host finished
     const uint32_t* hseq;      // device: sequence of this step's mailbox
+    uint32_t* hseen;           // device: last finished sequence, relayed by block 0 of the down GEMV
     int32_t* err;              // device error flags
 };
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s);

@@ -116,7 +116,7 @@ struct HostPool {
             const uint8_t* dsc = base + 3ull * I * rbH + 2ull * I * (H / 32);
             for (int h = r0; h < r0 + kRows && h < H; ++h)
                 for (int p : pairs_of[e])
-                    j.y[(uint64_t)p * H + h] =
+                    j.y[((uint64_t)(p / j.k) * H + h) * j.k + p % j.k] =
                         dot_row(j.wdtype, d + h * rbI, dsc + (uint64_t)h * (I / 32), j.act + (uint64_t)p * I, I);
             done2.fetch_add(1, std::memory_order_release);
         }

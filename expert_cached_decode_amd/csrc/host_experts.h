@@ -13,7 +13,8 @@ struct HostJob {
     const int32_t* rewritten; // [T*k] slot or -(1 + host index)
     int T, k, H, I, wdtype;
     const void* x;            // [T][H] f32 (wdtype f32) or bf16
-    float* y;                 // [T*k][H] written for host-side pairs only
+    float* y;                 // [T][H][k] written for host-side pairs (t, j) only (the k partial
+                              // sums of one output element are adjacent for the merge)
     float* act;               // scratch [T*k][I]
 };
 
