@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--timing-steps", type=int, default=64)
+    ap.add_argument("--measured-split-steps", type=int, default=128,
+                    help="extra decode run with the measured BP:BH applied (0 = skip)")
     ap.add_argument("--prefill-chunks", type=int, default=4)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc runs)")
@@ -244,6 +246,9 @@ def main():
         "cache": {"miss_rate": round(st["misses"] / max(lookups, 1), 4), "fills_per_step": round(st["fills"] / K, 3),
                   "host_per_step": round(st["host"] / K, 3), "fill_link_GBs": round(fill_gbs, 2)},
     }
+    if args.bpbh != "calibrate" and args.measured_split_steps > 0:
+        result["measured_split"] = bench_measured_split(ctx, cfg, token_layers, xs, logits, x_stage, lg_stage,
+                                                        total_steps, args.measured_split_steps)
     if args.workload == "stress":
         result["rebuild"] = bench_rebuild(ctx, cfg)
     if prefill_T:
@@ -252,6 +257,40 @@ def main():
         result["cpu_baseline"] = bench_cpu(cfg, logits.cpu().numpy(), P, period)
     ctx.close()
     print(json.dumps(result), flush=True)
+
+
+def bench_measured_split(ctx, cfg, token_layers, xs, logits, x_stage, lg_stage, n_inputs, steps):
+    """Extra run: the same decode continued with the measured BP and BH applied (the pages split the
+    misses by the two measured bandwidths); the graph is captured again for the new split."""
+    import torch
+    bp, bh = ctx.calibrate_bandwidth(8, apply=True)
+    graph, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        token_layers(x_stage, lg_stage, side)
+    torch.cuda.synchronize()
+
+    def step(i):
+        s = i % n_inputs
+        x_stage.copy_(xs[s]); lg_stage.copy_(logits[s])
+        graph.replay()
+
+    for i in range(16):
+        step(i)
+    torch.cuda.synchronize()
+    ctx.stats(reset=True)
+    t0 = time.perf_counter()
+    for i in range(16, 16 + steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = ctx.stats(reset=True)
+    out = {"bp_mbps": bp, "bh_mbps": bh, "steps": steps, "tok_s": round(steps * cfg.T / dt, 3),
+           "miss_rate": round(st["misses"] / max(st["hits"] + st["misses"], 1), 4),
+           "fills_per_step": round(st["fills"] / steps, 3), "host_per_step": round(st["host"] / steps, 3)}
+    log("measured split BP:BH %d:%d: %.2f tok/s, fills/step %.2f, host/step %.2f"
+        % (bp, bh, out["tok_s"], out["fills_per_step"], out["host_per_step"]))
+    return out
 
 
 def bench_rebuild(ctx, cfg):

@@ -56,7 +56,8 @@ _lib = None
 EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec_create", "ec_destroy",
            "ec_set_bandwidth", "moe_route", "expert_cache_step", "moe_decode_layer", "moe_prefill_layer",
            "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
-           "ec_kernel_timing", "ec_kernel_time", "ec_calibrate_bandwidth"]
+           "ec_kernel_timing", "ec_kernel_time", "ec_calibrate_bandwidth", "moe_gate_logits",
+           "moe_decode_block"]
 KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
@@ -91,6 +92,8 @@ def lib():
         L.ec_kernel_timing.argtypes = [c_vp, c_i32]
         L.ec_kernel_time.argtypes = [c_vp, c_i32, ctypes.POINTER(ctypes.c_double), P(c_u64), c_i32]
         L.ec_calibrate_bandwidth.argtypes = [c_vp, c_i32, c_i32, P(ctypes.c_uint32), P(ctypes.c_uint32)]
+        L.moe_gate_logits.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
+        L.moe_decode_block.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]
         for f in EXPORTS:
             getattr(L, f).restype = getattr(L, f).restype or c_i32
         L.ec_strerror.restype = ctypes.c_char_p
@@ -180,6 +183,15 @@ def expert_cache_step(ctx, layer, ids, T, stream=None):
 
 def moe_decode_layer(ctx, layer, x, logits, T, out, stream=None):
     check(lib().moe_decode_layer(ctx.handle, layer, _ptr(x), _ptr(logits), T, _ptr(out), _stream(stream)),
+          ctx.handle)
+
+
+def moe_gate_logits(w_router, x, x_dtype, T, E, H, logits, stream=None):
+    check(lib().moe_gate_logits(_ptr(w_router), _ptr(x), x_dtype, T, E, H, _ptr(logits), _stream(stream)))
+
+
+def moe_decode_block(ctx, layer, x, w_router, T, out, stream=None):
+    check(lib().moe_decode_block(ctx.handle, layer, _ptr(x), _ptr(w_router), T, _ptr(out), _stream(stream)),
           ctx.handle)
 
 

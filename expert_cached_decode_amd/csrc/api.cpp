@@ -46,6 +46,7 @@ struct ec_ctx {
     DevState st{};
     StepBufs sb{};
     float* act = nullptr;
+    float* gate_logits = nullptr; // [T_max][E] router logits of moe_decode_block
     // host branch: pinned mailbox, partial sums and doorbell, with their device-visible addresses
     int32_t* mb_pinned = nullptr;
     float* y_host_pinned = nullptr;
@@ -217,6 +218,7 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     x->sb.tok_pairs = d.take<int32_t>(n);
     x->st.hseq = d.take<uint32_t>(1);
     x->st.hseen = d.take<uint32_t>(1);
+    x->gate_logits = d.take<float>((uint64_t)x->Tmax * x->E);
     const uint64_t xbytes = (uint64_t)x->Tmax * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
     const uint64_t mb_bytes = mailbox_ints(n) * 4 + xbytes;
     x->act = d.take<float>((uint64_t)n * x->I);
@@ -469,13 +471,45 @@ static void host_branch_poll(ec_ctx* x) {
     }
 }
 
+static ec_status decode_layer(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
+                              hipStream_t s, int residual);
+
 ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
                            void* stream) {
     if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
     if (layer < 0 || layer >= x->L) return fail(x, EC_EINVAL, "layer out of range");
     if (T < 1 || T > x->Tmax) return fail(x, EC_EINVAL, "need 1 <= T <= max_tokens");
     if (!xin || !logits || !out) return fail(x, EC_EINVAL, "NULL pointer");
+    return decode_layer(x, layer, xin, logits, T, out, (hipStream_t)stream, 0);
+}
+
+ec_status moe_gate_logits(const void* w_router, const void* xin, int32_t x_dtype, int32_t T, int32_t E, int32_t H,
+                          float* logits, void* stream) {
+    if (!w_router || !xin || !logits) return fail(nullptr, EC_EINVAL, "NULL pointer");
+    if (x_dtype != EC_DT_F32 && x_dtype != EC_DT_BF16) return fail(nullptr, EC_EINVAL, "x_dtype must be f32 or bf16");
+    const int maxh = x_dtype == EC_DT_F32 ? 2048 : 4096;
+    if (T < 0 || E < 1 || E > kMaxExperts || H < 64 || H % 64 || H > maxh)
+        return fail(nullptr, EC_EINVAL, "need T >= 0, 1 <= E <= 4096, H a multiple of 64 within the dtype's limit");
+    launch_gate(w_router, xin, x_dtype == EC_DT_F32, T, E, H, logits, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? EC_OK : fail(nullptr, EC_EHIP, hipGetErrorString(e));
+}
+
+ec_status moe_decode_block(ec_ctx* x, int32_t layer, const void* xin, const void* w_router, int32_t T, void* out,
+                           void* stream) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    if (layer < 0 || layer >= x->L) return fail(x, EC_EINVAL, "layer out of range");
+    if (T < 1 || T > x->Tmax) return fail(x, EC_EINVAL, "need 1 <= T <= max_tokens");
+    if (!xin || !w_router || !out) return fail(x, EC_EINVAL, "NULL pointer");
+    if (out == xin) return fail(x, EC_EINVAL, "out must not alias x");
     hipStream_t s = (hipStream_t)stream;
+    launch_gate(w_router, xin, x->wdt == EC_DT_F32, T, x->E, x->H, x->gate_logits, s);
+    HIPCHK(x, hipGetLastError());
+    return decode_layer(x, layer, xin, x->gate_logits, T, out, s, 1);
+}
+
+static ec_status decode_layer(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
+                              hipStream_t s, int residual) {
     const int n = T * x->k;
     const uint64_t xbytes = (uint64_t)T * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
     CtlArgs a = ctl_args(x, layer, T);
@@ -499,6 +533,7 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     d.layer = layer % x->P; d.E = x->E; d.k = x->k; d.T = T; d.H = x->H; d.I = x->I; d.wdtype = x->wdt; d.U_max = x->Umax;
     d.host_pairs = x->host_branch ? 1 : 0;
     d.host_done = x->doorbell_dev + kDone; d.hseq = x->st.hseq; d.hseen = x->st.hseen; d.err = x->st.err;
+    d.residual = residual;
     if (x->C > 0 && !x->host_only) {
         tm = timer_next(x, 1);
         if (tm) HIPCHK(x, hipEventRecord(tm[0], s));

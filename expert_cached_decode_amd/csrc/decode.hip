@@ -65,6 +65,11 @@ template <int WDT> __device__ __forceinline__ int row_bytes(int n) {
     return WDT == EC_DT_F32 ? n * 4 : WDT == EC_DT_BF16 ? n * 2 : n / 2;
 }
 
+template <int WDT> static int row16(int n) { return (WDT == EC_DT_F32 ? n * 4 : WDT == EC_DT_BF16 ? n * 2 : n / 2) / 16; }
+
+// 16-byte chunks per lane, rounded up to 1, 2, 4 or 8; FULL when they tile the row exactly.
+static int nch_of(int n16) { const int c = (n16 + 63) / 64; return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 8; }
+
 // Load EPC activation values (elements c*EPC ...) as float.
 // act_bf16: x is bf16 (decode input) else float32.
 template <int EPC>
@@ -327,7 +332,8 @@ __device__ __noinline__ void wait_host_branch(const DecodeArgs& a) {
 // to back. Activations are f32 (f32 weights) or bf16 (else, through the dot2
 // unit). In LDS, chunk c of a row (EPC elements, QB 16-byte quads) keeps quad
 // d at slot c*QB + (d ^ (c % QB)), so the wave's 16-byte reads of one quad
-// index hit consecutive bank groups.
+// index hit consecutive bank groups. With `residual` set, the layer input is
+// added to each merged output row before rounding (a chained MoE block).
 template <int WDT, int NCH, int R, int G, bool T1, bool HOST, bool FULL, bool STAGE>
 __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
     constexpr int EPC = Fmt<WDT>::EPC;
@@ -449,8 +455,14 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
             float y = wave_sum(acc[r]);
             if (HOST) y += wave_sum(hs[r]);
             if (lane == 0) {
-                if (WDT == EC_DT_F32) reinterpret_cast<float*>(a.out)[(int64_t)t * H + row0 + r] = y;
-                else reinterpret_cast<uint16_t*>(a.out)[(int64_t)t * H + row0 + r] = f32_to_bf16(y);
+                const int64_t o = (int64_t)t * H + row0 + r;
+                if (WDT == EC_DT_F32) {
+                    if (a.residual) y += reinterpret_cast<const float*>(a.x)[o];
+                    reinterpret_cast<float*>(a.out)[o] = y;
+                } else {
+                    if (a.residual) y += bf16_lo(reinterpret_cast<const uint16_t*>(a.x)[o]);
+                    reinterpret_cast<uint16_t*>(a.out)[o] = f32_to_bf16(y);
+                }
             }
         }
     }
@@ -481,15 +493,76 @@ void launch_link_probe(const uint8_t* src_dev, uint64_t bytes, uint32_t* sink, h
     hipLaunchKernelGGL(link_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src_dev, bytes, sink);
 }
 
+// ---------------------------------------------------------------------------
+// Router GEMV: logits[t][e] = W_r[e] . x[t], one wavefront per expert row, the
+// row's NCH 16-byte chunks per lane kept in registers across the tokens. bf16
+// rows meet bf16 tokens in the dot2 unit; f32 rows use FMA. fp32 accumulation.
+template <bool F32, int NCH, bool FULL>
+__global__ __launch_bounds__(256) void gate_kernel(const uint8_t* wr, const void* x, int T, int E, int H,
+                                                   float* logits) {
+    const int lane = threadIdx.x & 63, e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    const int rb = F32 ? H * 4 : H * 2, n16 = rb >> 4;
+    uint4 w[NCH];
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+        const int c = lane + 64 * q;
+        if (FULL || c < n16) w[q] = load_stream(wr + (uint64_t)e * rb + 16ull * c);
+    }
+    for (int t = 0; t < T; ++t) {
+        const uint4* xr = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) + (uint64_t)t * rb);
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < NCH; ++q) {
+            const int c = lane + 64 * q;
+            if (FULL || c < n16) {
+                const uint4 u = xr[c];
+                if constexpr (F32) {
+                    const float xv[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                         __uint_as_float(u.w)};
+                    acc = chunk_dot<EC_DT_F32>(w[q], 0u, xv, acc);
+                } else {
+                    const uint32_t xw[4] = {u.x, u.y, u.z, u.w};
+                    acc = chunk_dot_packed<EC_DT_BF16>(w[q], 0u, xw, acc);
+                }
+            }
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) logits[(int64_t)t * E + e] = acc;
+    }
+}
+
+template <bool F32, int NCH>
+static void gate_go(const uint8_t* wr, const void* x, int T, int E, int H, float* logits, bool full, hipStream_t s) {
+    const dim3 grid((E + 3) / 4), blk(256);
+    if (full) hipLaunchKernelGGL((gate_kernel<F32, NCH, true>), grid, blk, 0, s, wr, x, T, E, H, logits);
+    else hipLaunchKernelGGL((gate_kernel<F32, NCH, false>), grid, blk, 0, s, wr, x, T, E, H, logits);
+}
+
+template <bool F32>
+static void gate_nch(const uint8_t* wr, const void* x, int T, int E, int H, float* logits, hipStream_t s) {
+    const int n16 = (F32 ? H * 4 : H * 2) / 16, nch = nch_of(n16);
+    const bool full = n16 == 64 * nch;
+    switch (nch) {
+    case 1: gate_go<F32, 1>(wr, x, T, E, H, logits, full, s); break;
+    case 2: gate_go<F32, 2>(wr, x, T, E, H, logits, full, s); break;
+    case 4: gate_go<F32, 4>(wr, x, T, E, H, logits, full, s); break;
+    default: gate_go<F32, 8>(wr, x, T, E, H, logits, full, s); break;
+    }
+}
+
+void launch_gate(const void* wr, const void* x, bool f32, int T, int E, int H, float* logits, hipStream_t s) {
+    if (T <= 0) return;
+    if (f32) gate_nch<true>(reinterpret_cast<const uint8_t*>(wr), x, T, E, H, logits, s);
+    else gate_nch<false>(reinterpret_cast<const uint8_t*>(wr), x, T, E, H, logits, s);
+}
+
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s) {
     const int chunks = (int)((a.expert_bytes + kFillChunk - 1) / kFillChunk);
     hipLaunchKernelGGL(fill_kernel, dim3(K * chunks), dim3(256), 0, s, a, chunks);
 }
 
-template <int WDT> static int row16(int n) { return (WDT == EC_DT_F32 ? n * 4 : WDT == EC_DT_BF16 ? n * 2 : n / 2) / 16; }
 
-// 16-byte chunks per lane, rounded up to 1, 2, 4 or 8; FULL when they tile the row exactly.
-static int nch_of(int n16) { const int c = (n16 + 63) / 64; return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 8; }
 
 template <int WDT, int NCH, int RW>
 static void gu_go(const DecodeArgs& a, bool full, hipStream_t s) {

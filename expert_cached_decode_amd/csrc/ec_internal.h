@@ -109,9 +109,11 @@ struct DecodeArgs {
     const uint32_t* hseq;      // device: sequence of this step's mailbox
     uint32_t* hseen;           // device: last finished sequence, relayed by block 0 of the down GEMV
     int32_t* err;              // device error flags
+    int32_t residual;          // 1: out = x + merged output (chained MoE block)
 };
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s);
 void launch_link_probe(const uint8_t* src_dev, uint64_t bytes, uint32_t* sink, hipStream_t s);
+void launch_gate(const void* wr, const void* x, bool f32, int T, int E, int H, float* logits, hipStream_t s);
 void launch_gu(const DecodeArgs& a, hipStream_t s);
 void launch_down(const DecodeArgs& a, hipStream_t s);
 

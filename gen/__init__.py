@@ -17,7 +17,7 @@ _SO = os.path.join(_HERE, "libecgen.so")
 _lib = None
 
 TAG_GATE, TAG_UP, TAG_DOWN = 0, 1, 2
-TAG_X, TAG_PLOGIT, TAG_PX, TAG_VEC = 11, 12, 13, 14
+TAG_X, TAG_PLOGIT, TAG_PX, TAG_VEC, TAG_ROUTER = 11, 12, 13, 14, 15
 
 
 def build(force=True):
@@ -138,6 +138,14 @@ def prefill_x(cfg: Workload, layer, T=None):
     """Prefill hidden states [T, H] ~ N(0,1) in bf16 bits."""
     T = cfg.T if T is None else T
     return normals(cfg, TAG_PX, layer, 0, 0, T * cfg.H, bf16=True).reshape(T, cfg.H)
+
+
+def router_weights(cfg: Workload, layer):
+    """Router matrix W_r [E, H] of one layer ~ N(0, 1/sqrt(H)) (logits of N(0,1) inputs are then
+    about N(0,1)): float32 for f32 workloads, else bf16 bits."""
+    n = cfg.E * cfg.H
+    return normals(cfg, TAG_ROUTER, layer, 0, 0, n, sigma=1.0 / np.sqrt(cfg.H),
+                   bf16=cfg.act_bf16).reshape(cfg.E, cfg.H)
 
 
 def bf16_to_f32(a):

@@ -124,7 +124,7 @@ static inline uint16_t f32_to_bf16_rne(float f) {
 
 /* ---- tensor tags ---------------------------------------------------------- */
 enum { TAG_GATE = 0, TAG_UP = 1, TAG_DOWN = 2, TAG_LOGIT = 10, TAG_X = 11, TAG_PLOGIT = 12,
-       TAG_PX = 13, TAG_VEC = 14 };
+       TAG_PX = 13, TAG_VEC = 14, TAG_ROUTER = 15 };
 enum { DT_F32 = 0, DT_BF16 = 1, DT_MXFP4 = 2 };
 
 /* Fill n normals N(0, sigma) of stream (seed, tag, a, b, c), starting at index i0. */

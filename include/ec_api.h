@@ -229,6 +229,28 @@ ec_status expert_cache_step(ec_ctx* ctx, int32_t layer, const int32_t* ids, int3
 ec_status moe_decode_layer(ec_ctx* ctx, int32_t layer, const void* x, const float* logits, int32_t T,
                            void* out, void* stream);
 
+/* Router logits, the step before top-k ("Why personal MoE is hard": a router
+ * scores the E experts of a layer for each token):
+ *   logits[t][e] = sum_h w_router[e][h] * x[t][h], fp32 accumulation.
+ *   w_router : dev [E][H], row-major, x_dtype (EC_DT_F32 or EC_DT_BF16)
+ *   x        : dev [T][H], x_dtype
+ *   logits   : dev f32 [T][E]
+ * H a multiple of 64, at most 2048 (f32) or 4096 (bf16); 1 <= E <= 4096;
+ * T >= 0 (T = 0 enqueues nothing). Capturable. */
+ec_status moe_gate_logits(const void* w_router, const void* x, int32_t x_dtype, int32_t T, int32_t E, int32_t H,
+                          float* logits, void* stream);
+
+/* One MoE block of a chained decode: logits = w_router x (moe_gate_logits
+ * into the context's workspace), moe_decode_layer on them, and the residual:
+ *   out[t] = x[t] + sum_j w[t,j] f_e(t,j)(x[t]), rounded once to x's dtype,
+ * so out is the next layer's input and routing follows the data ("Semantic-
+ * aware caching": the cache sees the locality of real routing).
+ *   w_router : dev [E][H] in x's dtype (f32 when wdtype is EC_DT_F32, else bf16)
+ *   x, out   : dev [T][H], distinct buffers
+ * 1 <= T <= T_max. Capturable. */
+ec_status moe_decode_block(ec_ctx* ctx, int32_t layer, const void* x, const void* w_router, int32_t T, void* out,
+                           void* stream);
+
 /* One prefill MoE layer ("Bandwidth-adaptive execution", prefill: full-layer
  * double buffering). Ensures the layer's whole expert set is in one of two
  * device buffers (uploading it on `copy_stream` if it is not), makes
