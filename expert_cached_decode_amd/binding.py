@@ -57,7 +57,7 @@ EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec
            "ec_set_bandwidth", "moe_route", "expert_cache_step", "moe_decode_layer", "moe_prefill_layer",
            "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
            "ec_kernel_timing", "ec_kernel_time", "ec_calibrate_bandwidth", "moe_gate_logits",
-           "moe_decode_block"]
+           "moe_decode_block", "ec_bank_write", "ec_bank_read"]
 KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
@@ -94,6 +94,9 @@ def lib():
         L.ec_calibrate_bandwidth.argtypes = [c_vp, c_i32, c_i32, P(ctypes.c_uint32), P(ctypes.c_uint32)]
         L.moe_gate_logits.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
         L.moe_decode_block.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]
+        L.ec_bank_write.argtypes = [ctypes.c_char_p, P(ec_shape), c_i32, c_vp, c_u64]
+        L.ec_bank_read.argtypes = [ctypes.c_char_p, P(ec_shape), c_i32, c_vp, c_u64, c_i32, P(c_i32),
+                                   ctypes.POINTER(ctypes.c_double)]
         for f in EXPORTS:
             getattr(L, f).restype = getattr(L, f).restype or c_i32
         L.ec_strerror.restype = ctypes.c_char_p
@@ -184,6 +187,19 @@ def expert_cache_step(ctx, layer, ids, T, stream=None):
 def moe_decode_layer(ctx, layer, x, logits, T, out, stream=None):
     check(lib().moe_decode_layer(ctx.handle, layer, _ptr(x), _ptr(logits), T, _ptr(out), _stream(stream)),
           ctx.handle)
+
+
+def bank_write(path, shape, pool_layers, ptr, nbytes):
+    """Write an expert-bank file (no GPU involved)."""
+    check(lib().ec_bank_write(os.fsencode(path), ctypes.byref(shape), pool_layers, c_vp(ptr), nbytes))
+
+
+def bank_read(path, shape, pool_layers, ptr, nbytes, threads=0):
+    """Fill host memory at ptr from an expert-bank file; returns (seconds, direct_io)."""
+    sec, direct = ctypes.c_double(), c_i32()
+    check(lib().ec_bank_read(os.fsencode(path), ctypes.byref(shape), pool_layers, c_vp(ptr), nbytes, threads,
+                             ctypes.byref(direct), ctypes.byref(sec)))
+    return sec.value, bool(direct.value)
 
 
 def moe_gate_logits(w_router, x, x_dtype, T, E, H, logits, stream=None):

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "ec_internal.h"
+#include "bank_io.h"
 #include "host_experts.h"
 #include "prefill.h"
 
@@ -698,6 +699,50 @@ ec_status ec_calibrate_bandwidth(ec_ctx* x, int32_t probe_experts, int32_t apply
         if (st) return st;
         HIPCHK(x, hipStreamSynchronize(x->side));
     }
+    return EC_OK;
+}
+
+static ec_status bank_args(const ec_shape* shape, int32_t pool_layers, uint64_t* expert_bytes, uint64_t* bank_bytes,
+                           int32_t dims[6]) {
+    ec_status st = check_shape(shape);
+    if (st) return st;
+    if (pool_layers < 1 || pool_layers > shape->layers)
+        return fail(nullptr, EC_EINVAL, "need 1 <= pool_layers <= layers");
+    ec_layout_info lay;
+    ec_layout(shape, &lay);
+    *expert_bytes = lay.expert_bytes;
+    *bank_bytes = lay.layer_bytes * (uint64_t)pool_layers;
+    dims[0] = shape->layers; dims[1] = shape->experts; dims[2] = shape->top_k;
+    dims[3] = shape->hidden; dims[4] = shape->inter; dims[5] = shape->wdtype;
+    return EC_OK;
+}
+
+ec_status ec_bank_write(const char* path, const ec_shape* shape, int32_t pool_layers, const void* bank, uint64_t bytes) {
+    if (!path || !bank) return fail(nullptr, EC_EINVAL, "NULL argument");
+    uint64_t eb = 0, need = 0;
+    int32_t dims[6];
+    ec_status st = bank_args(shape, pool_layers, &eb, &need, dims);
+    if (st) return st;
+    if (bytes < need) return fail(nullptr, EC_ENOSPC, "bank smaller than pool_layers * experts * expert_bytes");
+    std::string err;
+    if (bank_write(path, dims, pool_layers, eb, bank, need, &err) != 0) return fail(nullptr, EC_EINVAL, err);
+    return EC_OK;
+}
+
+ec_status ec_bank_read(const char* path, const ec_shape* shape, int32_t pool_layers, void* dst, uint64_t dst_bytes,
+                       int32_t threads, int32_t* direct_io, double* seconds) {
+    if (!path || !dst) return fail(nullptr, EC_EINVAL, "NULL argument");
+    uint64_t eb = 0, need = 0;
+    int32_t dims[6];
+    ec_status st = bank_args(shape, pool_layers, &eb, &need, dims);
+    if (st) return st;
+    if (dst_bytes < need) return fail(nullptr, EC_ENOSPC, "destination smaller than the bank");
+    std::string err;
+    int direct = 0;
+    const int r = bank_read(path, dims, pool_layers, eb, dst, need, threads > 0 ? threads : 16, &direct, seconds, &err);
+    if (r == -2) return fail(nullptr, EC_ESHAPE, err);
+    if (r != 0) return fail(nullptr, EC_EINVAL, err);
+    if (direct_io) *direct_io = direct;
     return EC_OK;
 }
 

@@ -278,6 +278,27 @@ ec_status ec_set_prefill_overlap(ec_ctx* ctx, int32_t on);
  * Bumps the epoch. */
 ec_status cache_rebuild(ec_ctx* ctx, int32_t budget_bp, void* new_slot_pool, uint64_t bytes);
 
+/* Expert-bank files ("Implementation notes": weights stored ahead of time in the
+ * runtime's expert-bank layout are loaded without discovery or repacking, with
+ * parallel direct I/O of aligned blocks; "Elastic edge resource management":
+ * reading straight into the final host layout keeps the cold start short).
+ * A file is a 4096-byte header (magic "ECBANK01", version, shape, pool layers,
+ * expert and bank byte counts, header checksum) followed by the
+ * [P][E][expert_bytes] bank, padded to a multiple of 4096 bytes.
+ * Neither call touches the GPU.
+ *
+ * ec_bank_write: writes `bank` (host memory, >= P * E * expert_bytes bytes)
+ *   to `path` and syncs it to storage.
+ * ec_bank_read: fills `dst` (host memory, typically the pinned pool later
+ *   given to ec_create) from a file written for the same shape and P
+ *   (EC_ESHAPE otherwise), with `threads` readers (0 = 16) over 32 MiB
+ *   chunks; O_DIRECT when dst is 4096-byte aligned and the file system allows
+ *   it (*direct_io = 1), else buffered reads. *seconds (may be NULL) is the
+ *   wall time. EC_EINVAL on I/O errors or a truncated file. */
+ec_status ec_bank_write(const char* path, const ec_shape* shape, int32_t pool_layers, const void* bank, uint64_t bytes);
+ec_status ec_bank_read(const char* path, const ec_shape* shape, int32_t pool_layers, void* dst, uint64_t dst_bytes,
+                       int32_t threads, int32_t* direct_io, double* seconds);
+
 /* Changes whenever captured graphs of this context must be re-captured. */
 uint64_t ec_epoch(const ec_ctx* ctx);
 
