@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--timing-steps", type=int, default=64)
+    ap.add_argument("--cold-start-gb", type=float, default=0.0,
+                    help="time a cold start: write about this many GB of the bank as a bank file and read it "
+                         "back into pinned memory with parallel direct I/O (0 = skip)")
     ap.add_argument("--measured-split-steps", type=int, default=128,
                     help="extra decode run with the measured BP:BH applied (0 = skip)")
     ap.add_argument("--prefill-chunks", type=int, default=4)
@@ -116,6 +119,7 @@ def main():
 
     cfg, text = workload(args)
     torch.cuda.set_device(0)
+    cold = bench_cold_start(cfg, args.cold_start_gb) if args.cold_start_gb > 0 else None
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -249,6 +253,8 @@ def main():
     if args.bpbh != "calibrate" and args.measured_split_steps > 0:
         result["measured_split"] = bench_measured_split(ctx, cfg, token_layers, xs, logits, x_stage, lg_stage,
                                                         total_steps, args.measured_split_steps)
+    if cold:
+        result["cold_start"] = cold
     if args.workload == "stress":
         result["rebuild"] = bench_rebuild(ctx, cfg)
     if prefill_T:
@@ -290,6 +296,42 @@ def bench_measured_split(ctx, cfg, token_layers, xs, logits, x_stage, lg_stage, 
            "fills_per_step": round(st["fills"] / steps, 3), "host_per_step": round(st["host"] / steps, 3)}
     log("measured split BP:BH %d:%d: %.2f tok/s, fills/step %.2f, host/step %.2f"
         % (bp, bh, out["tok_s"], out["fills_per_step"], out["host_per_step"]))
+    return out
+
+
+def bench_cold_start(cfg, gb):
+    """Fast start: write the first layers of the expert bank (about `gb` GB) as a bank file,
+    then time reading it with parallel direct I/O into freshly pinned host memory (the final
+    host-pool layout, no repacking); the rate is extrapolated to the whole bank."""
+    import shutil
+    import tempfile
+    import gen
+    import expert_cached_decode_amd as EC
+    layer_bytes = cfg.E * cfg.expert_bytes
+    P = max(1, min(cfg.L, int(gb * 1e9 // layer_bytes)))
+    shape = EC.make_shape(cfg.L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype)
+    src = np.empty(P * layer_bytes, np.uint8)
+    gen.fill_pool_ptr(cfg, src.ctypes.data, 0, P)
+    d = tempfile.mkdtemp(prefix="ecbank_", dir=os.environ.get("TMPDIR", "/tmp"))
+    try:
+        path = os.path.join(d, "bank.ecb")
+        t0 = time.perf_counter()
+        EC.bank_write(path, shape, P, src.ctypes.data, src.nbytes)
+        t_write = time.perf_counter() - t0
+        pinned = EC.PinnedBuffer(src.nbytes)
+        sec, direct = EC.bank_read(path, shape, P, pinned.ptr, pinned.nbytes, threads=16)
+        ok = bool(np.array_equal(pinned.numpy()[::4096], src[::4096]) and
+                  np.array_equal(pinned.numpy()[-1 << 20:], src[-1 << 20:]))
+        pinned.close()
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    rate = src.nbytes / sec / 1e9
+    full = cfg.L * layer_bytes
+    out = {"bytes": int(src.nbytes), "layers": P, "read_s": round(sec, 3), "read_GBs": round(rate, 2),
+           "direct_io": direct, "threads": 16, "write_s": round(t_write, 2), "verified": ok,
+           "full_bank_bytes": int(full), "full_bank_read_s_extrapolated": round(full / 1e9 / rate, 2)}
+    log("cold start: %.2f GB bank file read in %.2f s (%.2f GB/s, direct I/O %s); the %.1f GB bank would take %.1f s"
+        % (src.nbytes / 1e9, sec, rate, direct, full / 1e9, out["full_bank_read_s_extrapolated"]))
     return out
 
 

@@ -195,11 +195,12 @@ def bank_write(path, shape, pool_layers, ptr, nbytes):
 
 
 def bank_read(path, shape, pool_layers, ptr, nbytes, threads=0):
-    """Fill host memory at ptr from an expert-bank file; returns (seconds, direct_io)."""
+    """Fill host memory at ptr from an expert-bank file; returns (seconds, mode) with mode 1 direct
+    I/O into ptr, 2 direct I/O through bounce buffers, 0 buffered."""
     sec, direct = ctypes.c_double(), c_i32()
     check(lib().ec_bank_read(os.fsencode(path), ctypes.byref(shape), pool_layers, c_vp(ptr), nbytes, threads,
                              ctypes.byref(direct), ctypes.byref(sec)))
-    return sec.value, bool(direct.value)
+    return sec.value, int(direct.value)
 
 
 def moe_gate_logits(w_router, x, x_dtype, T, E, H, logits, stream=None):

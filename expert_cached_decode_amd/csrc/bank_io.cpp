@@ -25,6 +25,7 @@
 #include <cerrno>
 #include <chrono>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <thread>
@@ -112,22 +113,38 @@ int bank_read(const char* path, const int32_t shape[6], int32_t P, uint64_t expe
     if (std::memcmp(h.data(), kMagic, 8) != 0) { *err = "not an expert-bank file"; return -2; }
     if (std::memcmp(h.data(), want.data(), 64) != 0) { *err = "bank file holds another shape, layer count or size"; return -2; }
 
-    // direct I/O needs aligned destinations, offsets and lengths: the bank is read in
-    // whole 4096-byte blocks where the destination allows it, else through the page cache
-    const bool aligned = ((uintptr_t)dst % kAlign) == 0;
-    int dfd = aligned ? open(path, O_RDONLY | O_DIRECT) : -1;
-    const bool direct = dfd >= 0;
-    if (!direct) dfd = open(path, O_RDONLY);
+    // Direct I/O needs aligned destinations, offsets and lengths. The bank is read in
+    // whole 4096-byte blocks: straight into dst when the kernel can pin dst's pages for
+    // the transfer (checked on the first block), else into per-reader aligned bounce
+    // buffers copied to dst (memory handed out by a GPU driver may refuse direct
+    // transfers); without O_DIRECT support, or for an unaligned dst, through the page
+    // cache. The tail below 4096 bytes is always read buffered.
+    enum Mode { kBuffered = 0, kDirect = 1, kBounce = 2 };
+    int dfd = open(path, O_RDONLY | O_DIRECT);
+    Mode mode = dfd >= 0 ? kDirect : kBuffered;
+    if (mode == kDirect && (((uintptr_t)dst % kAlign) != 0 || bytes < kAlign ||
+                            !read_full(dfd, (uint8_t*)dst, kAlign, kHeader)))
+        mode = kBounce;
+    if (mode == kBuffered) dfd = open(path, O_RDONLY);
     if (dfd < 0) { *err = std::string("open failed: ") + std::strerror(errno); return -1; }
-    const uint64_t whole = direct ? bytes / kAlign * kAlign : bytes; // the tail is read buffered
+    const uint64_t whole = mode == kBuffered ? bytes : bytes / kAlign * kAlign;
     const uint64_t nchunks = (whole + kChunk - 1) / kChunk;
     std::atomic<uint64_t> next{0};
     std::atomic<bool> failed{false};
     auto worker = [&] {
+        uint8_t* bounce = nullptr;
+        if (mode == kBounce && posix_memalign((void**)&bounce, kAlign, kChunk) != 0) { failed = true; return; }
         for (uint64_t c; (c = next.fetch_add(1)) < nchunks && !failed.load();) {
             const uint64_t off = c * kChunk, n = std::min(kChunk, whole - off);
-            if (!read_full(dfd, (uint8_t*)dst + off, n, kHeader + off)) failed = true;
+            uint8_t* to = (uint8_t*)dst + off;
+            if (mode == kBounce) {
+                if (!read_full(dfd, bounce, n, kHeader + off)) failed = true;
+                else std::memcpy(to, bounce, n);
+            } else if (!read_full(dfd, to, n, kHeader + off)) {
+                failed = true;
+            }
         }
+        std::free(bounce);
     };
     const int nt = std::max(1, std::min(threads, 64));
     std::vector<std::thread> pool;
@@ -141,7 +158,7 @@ int bank_read(const char* path, const int32_t shape[6], int32_t P, uint64_t expe
         if (bfd >= 0) close(bfd);
     }
     if (failed) { *err = "read failed or file truncated"; return -1; }
-    if (direct_used) *direct_used = direct ? 1 : 0;
+    if (direct_used) *direct_used = (int)mode;
     if (seconds) *seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
     return 0;
 }

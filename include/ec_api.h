@@ -292,9 +292,12 @@ ec_status cache_rebuild(ec_ctx* ctx, int32_t budget_bp, void* new_slot_pool, uin
  * ec_bank_read: fills `dst` (host memory, typically the pinned pool later
  *   given to ec_create) from a file written for the same shape and P
  *   (EC_ESHAPE otherwise), with `threads` readers (0 = 16) over 32 MiB
- *   chunks; O_DIRECT when dst is 4096-byte aligned and the file system allows
- *   it (*direct_io = 1), else buffered reads. *seconds (may be NULL) is the
- *   wall time. EC_EINVAL on I/O errors or a truncated file. */
+ *   chunks. *direct_io (may be NULL) tells how: 1 O_DIRECT straight into dst
+ *   (dst 4096-byte aligned and its pages accept direct transfers), 2 O_DIRECT
+ *   into per-reader aligned bounce buffers copied to dst (e.g. pinned memory
+ *   from the GPU driver, which refuses direct transfers), 0 buffered reads
+ *   (no O_DIRECT on the file system). *seconds (may be NULL) is the wall
+ *   time. EC_EINVAL on I/O errors or a truncated file. */
 ec_status ec_bank_write(const char* path, const ec_shape* shape, int32_t pool_layers, const void* bank, uint64_t bytes);
 ec_status ec_bank_read(const char* path, const ec_shape* shape, int32_t pool_layers, void* dst, uint64_t dst_bytes,
                        int32_t threads, int32_t* direct_io, double* seconds);
