@@ -243,7 +243,8 @@ def main():
                      "bytes_per_launch": int(gu_bytes), "us_per_launch": round(gu_us, 3),
                      "launches": int(n_launch), "timing": "HIP events around each launch, eager pass"},
         "down_kernel": {"achieved": round(dn_gbs, 1), "unit": "GB/s", "frac": round(dn_gbs / HBM_PEAK_GBS, 4),
-                        "bytes_per_launch": int(dn_bytes), "us_per_launch": round(dn_us, 3)},
+                        "bytes_per_launch": int(dn_bytes), "us_per_launch": round(dn_us, 3),
+                        "traffic": measured_traffic("down_kernel") if args.workload == "qwen" else None},
         "other_kernels_us": {"ctl": round(ctl_us, 3),
                              "fill_per_expert": round(fill_ms * 1e3 / max(st2["fills"], 1), 2)},
         "bandwidth_mbps": {"bp_measured": bp_meas, "bh_measured": bh_meas, "bp_used": bp_used, "bh_used": bh_used},
