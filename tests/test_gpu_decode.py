@@ -148,6 +148,23 @@ def test_qwen_decode_full_size_sampled():
     ctx.close()
 
 
+def test_dsv4_decode_full_size_sampled():
+    """The full MXFP4 workload as the bench runs it: 43 layers, 2752 slots (25%), BP:BH 300:1000 (most
+    misses on the host branch), host pool of 16 layers (layer l reads pool layer l % 16, all drawn as
+    layer 0), sampled outputs against the oracle and every decision against the simulator."""
+    cfg = DSV4_DECODE
+    pool = make_pool(cfg, L=16, layer_period=1)
+    ctx = make_ctx(cfg, pool, pool_layers=16)
+    steps = 20
+    outs, logits = run_decode(cfg, ctx, steps, cfg.L, 1, lambda s, l: (s * 11 + l) % 89 == 0)
+    check_against_oracle(cfg, outs, 1e-2, layer_period=1, max_checks=8)
+    st = ctx.stats()
+    ref = sim_counts(cfg, logits, cfg.L, 1, cfg.slots, cfg.K, cfg.bp, cfg.bh)
+    assert {k: st[k] for k in ref} == ref
+    assert st["host"] > 0 and st["fills"] > 0
+    ctx.close()
+
+
 def test_host_pool_layer_aliasing():
     """pool_layers = 2 for 4 layers: layer l reads pool layer l % 2 (fills and host branch)."""
     cfg = QWEN_DECODE.with_(L=4, slots=24, bp=500, bh=1000)
