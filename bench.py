@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--timing-steps", type=int, default=64)
+    ap.add_argument("--sweep-locality", action="store_true",
+                    help="stress workload: tok/s and miss rate against routing overlap at batch 1 and 16")
     ap.add_argument("--cold-start-gb", type=float, default=0.0,
                     help="time a cold start: write about this many GB of the bank as a bank file and read it "
                          "back into pinned memory with parallel direct I/O (0 = skip)")
@@ -258,6 +260,8 @@ def main():
         result["cold_start"] = cold
     if args.workload == "stress":
         result["rebuild"] = bench_rebuild(ctx, cfg)
+        if args.sweep_locality:
+            result["locality_sweep"] = bench_locality_sweep(ctx, cfg)
     if prefill_T:
         result["prefill"] = bench_prefill(ctx, cfg, QWEN_PREFILL, args.prefill_chunks)
     if not args.no_cpu:
@@ -333,6 +337,60 @@ def bench_cold_start(cfg, gb):
            "full_bank_bytes": int(full), "full_bank_read_s_extrapolated": round(full / 1e9 / rate, 2)}
     log("cold start: %.2f GB bank file read in %.2f s (%.2f GB/s, direct I/O %s); the %.1f GB bank would take %.1f s"
         % (src.nbytes / 1e9, sec, rate, direct, full / 1e9, out["full_bank_read_s_extrapolated"]))
+    return out
+
+
+def bench_locality_sweep(ctx, cfg, ps=(0.0, 0.3, 0.6, 0.9), warm=16, steps=48):
+    """tok/s and miss rate against step-to-step routing overlap p at batch 1 and 16 (cold cache at
+    each point through cache_rebuild to the configured slot count, one graph per point)."""
+    import torch
+    import gen
+    import expert_cached_decode_amd as EC
+    L, E, H = cfg.L, cfg.E, cfg.H
+    budget = -(-cfg.slots * 10000 // (L * E))  # smallest budget giving at least cfg.slots slots
+    if budget * L * E // 10000 > cfg.slots:
+        budget -= 1
+    out = []
+    for T in (1, cfg.T):
+        x_stage = torch.empty((L, T, H), dtype=torch.int16, device="cuda")
+        lg_stage = torch.empty((L, T, E), dtype=torch.float32, device="cuda")
+        outs = torch.empty((L, T, H), dtype=torch.int16, device="cuda")
+        for p in ps:
+            c = cfg.with_(T=T, p=p)
+            lg = torch.from_numpy(gen.decode_logits(c, steps=warm + steps)).cuda()
+            xs = torch.from_numpy(np.stack([np.stack([gen.decode_x(c, s, l) for l in range(L)])
+                                            for s in range(4)]).view(np.int16)).cuda()
+            ctx.rebuild(budget)
+            graph, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=side):
+                for l in range(L):
+                    EC.moe_decode_layer(ctx, l, x_stage[l], lg_stage[l], T, outs[l], side)
+            torch.cuda.synchronize()
+
+            def step(i):
+                x_stage.copy_(xs[i % 4]); lg_stage.copy_(lg[i])
+                graph.replay()
+
+            for i in range(warm):
+                step(i)
+            torch.cuda.synchronize()
+            ctx.stats(reset=True)
+            t0 = time.perf_counter()
+            for i in range(warm, warm + steps):
+                step(i)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            st = ctx.stats(reset=True)
+            r = {"T": T, "p": p, "tok_s": round(steps * T / dt, 2),
+                 "miss_rate": round(st["misses"] / max(st["hits"] + st["misses"], 1), 4),
+                 "unique_per_layer_step": round((st["hits"] + st["misses"]) / (steps * L), 2),
+                 "fills_per_step": round(st["fills"] / steps, 2), "host_per_step": round(st["host"] / steps, 2)}
+            log("locality sweep T=%d p=%.1f: %.2f tok/s, miss rate %.3f, %.1f unique experts per layer step"
+                % (T, p, r["tok_s"], r["miss_rate"], r["unique_per_layer_step"]))
+            out.append(r)
+            del graph
+    ctx.rebuild(budget)
     return out
 
 
