@@ -147,7 +147,7 @@ def main():
                      victim_k=cfg.K, bp=cfg.bp, bh=cfg.bh, host_pool=pool, prefill_max_tokens=prefill_T,
                      pool_layers=P)
     # measured BP and BH (MB/s): applied with --bpbh calibrate, else reported only
-    bp_meas, bh_meas = ctx.calibrate_bandwidth(8, apply=(args.bpbh == "calibrate"))
+    bp_meas, bh_meas = ctx.calibrate_bandwidth(min(8, T * cfg.k, cfg.E // 4), apply=(args.bpbh == "calibrate"))
     log("calibration: BP %d MB/s over the link, BH %d MB/s on the host branch%s"
         % (bp_meas, bh_meas, " (applied)" if args.bpbh == "calibrate" else ""))
     bp_used, bh_used = (bp_meas, bh_meas) if args.bpbh == "calibrate" else (cfg.bp, cfg.bh)
@@ -274,7 +274,7 @@ def bench_measured_split(ctx, cfg, token_layers, xs, logits, x_stage, lg_stage, 
     """Extra run: the same decode continued with the measured BP and BH applied (the pages split the
     misses by the two measured bandwidths); the graph is captured again for the new split."""
     import torch
-    bp, bh = ctx.calibrate_bandwidth(8, apply=True)
+    bp, bh = ctx.calibrate_bandwidth(min(8, cfg.T * cfg.k, cfg.E // 4), apply=True)
     graph, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=side):

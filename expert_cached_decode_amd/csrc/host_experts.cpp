@@ -9,6 +9,8 @@
 // down rows, so each weight byte is read from host memory once per step.
 #include "host_experts.h"
 
+#include <immintrin.h>
+
 #include <atomic>
 #include <cmath>
 #include <condition_variable>
@@ -51,15 +53,32 @@ float dot_row(int wdt, const uint8_t* row, const uint8_t* srow, const float* v, 
         for (int i = 0; i < n; i += 16)
             for (int q = 0; q < 16; ++q) acc[q] += bf16f(w[i + q]) * v[i + q];
     } else {
+        // 32 codes per block: nibbles in element order (low nibble = even element), looked up
+        // eight at a time in the E2M1 magnitude table with the sign bit applied separately,
+        // times the activations, then the block sum times its E8M0 scale
+        const __m256 lut = _mm256_loadu_ps(kE2M1);
+        const __m256i seven = _mm256_set1_epi32(7), eight = _mm256_set1_epi32(8);
+        const __m128i lo_mask = _mm_set1_epi8(0x0f);
+        __m256 tot = _mm256_setzero_ps();
         for (int b = 0; b < n / 32; ++b) {
-            float blk[16] = {0};
-            const uint8_t* c = row + b * 16;
+            const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(row + b * 16));
+            const __m128i lo = _mm_and_si128(raw, lo_mask), hi = _mm_and_si128(_mm_srli_epi16(raw, 4), lo_mask);
+            const __m128i e0 = _mm_unpacklo_epi8(lo, hi), e1 = _mm_unpackhi_epi8(lo, hi); // elements 0..15, 16..31
             const float* vb = v + b * 32;
-            for (int q = 0; q < 16; ++q) blk[q] = kE2M1[c[q] & 15] * vb[2 * q] + kE2M1[c[q] >> 4] * vb[2 * q + 1];
-            float s = 0.f;
-            for (int q = 0; q < 16; ++q) s += blk[q];
-            acc[b & 15] += s * e8m0(srow[b]);
+            __m256 blk = _mm256_setzero_ps();
+            const __m128i parts[4] = {e0, _mm_srli_si128(e0, 8), e1, _mm_srli_si128(e1, 8)};
+            for (int g = 0; g < 4; ++g) {
+                const __m256i idx = _mm256_cvtepu8_epi32(parts[g]);
+                __m256 w = _mm256_permutevar8x32_ps(lut, _mm256_and_si256(idx, seven));
+                const __m256i sgn = _mm256_slli_epi32(_mm256_and_si256(idx, eight), 28);
+                w = _mm256_xor_ps(w, _mm256_castsi256_ps(sgn));
+                blk = _mm256_fmadd_ps(w, _mm256_loadu_ps(vb + 8 * g), blk);
+            }
+            tot = _mm256_fmadd_ps(blk, _mm256_set1_ps(e8m0(srow[b])), tot);
         }
+        alignas(32) float t8[8];
+        _mm256_store_ps(t8, tot);
+        for (int q = 0; q < 8; ++q) acc[q] += t8[q];
     }
     float s = 0.f;
     for (int q = 0; q < 16; ++q) s += acc[q];
