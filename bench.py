@@ -99,6 +99,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--timing-steps", type=int, default=64)
+    ap.add_argument("--host-threads", type=int, default=0, help="host-branch worker threads (0 = library default)")
     ap.add_argument("--sweep-locality", action="store_true",
                     help="stress workload: tok/s and miss rate against routing overlap at batch 1 and 16")
     ap.add_argument("--cold-start-gb", type=float, default=0.0,
@@ -145,9 +146,10 @@ def main():
     prefill_T = QWEN_PREFILL.T if (args.workload == "qwen" and not args.no_prefill) else 0
     ctx = EC.Context(L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype, max_tokens=T, cache_slots=cfg.slots,
                      victim_k=cfg.K, bp=cfg.bp, bh=cfg.bh, host_pool=pool, prefill_max_tokens=prefill_T,
+                     host_threads=args.host_threads,
                      pool_layers=P)
     # measured BP and BH (MB/s): applied with --bpbh calibrate, else reported only
-    bp_meas, bh_meas = ctx.calibrate_bandwidth(min(8, T * cfg.k, cfg.E // 4), apply=(args.bpbh == "calibrate"))
+    bp_meas, bh_meas = ctx.calibrate_bandwidth(min(32, cfg.E // 4), apply=(args.bpbh == "calibrate"))
     log("calibration: BP %d MB/s over the link, BH %d MB/s on the host branch%s"
         % (bp_meas, bh_meas, " (applied)" if args.bpbh == "calibrate" else ""))
     bp_used, bh_used = (bp_meas, bh_meas) if args.bpbh == "calibrate" else (cfg.bp, cfg.bh)
@@ -274,7 +276,7 @@ def bench_measured_split(ctx, cfg, token_layers, xs, logits, x_stage, lg_stage, 
     """Extra run: the same decode continued with the measured BP and BH applied (the pages split the
     misses by the two measured bandwidths); the graph is captured again for the new split."""
     import torch
-    bp, bh = ctx.calibrate_bandwidth(min(8, cfg.T * cfg.k, cfg.E // 4), apply=True)
+    bp, bh = ctx.calibrate_bandwidth(min(32, cfg.E // 4), apply=True)
     graph, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=side):

@@ -80,6 +80,13 @@ static constexpr int kTimerPairs = 1024;
 
 static void host_branch_poll(ec_ctx* x);
 
+// Host-branch workers by default: the host's hardware threads less two (the polling thread
+// and the caller), 1 to 32.
+static int default_host_threads() {
+    const int hw = (int)std::thread::hardware_concurrency();
+    return std::max(1, std::min(32, hw > 2 ? hw - 2 : 1));
+}
+
 static void timers_free(ec_ctx* x);
 
 static hipError_t timer_drain(ec_ctx::Timer& t) {
@@ -351,7 +358,7 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
         delete x;
         return fail(nullptr, EC_EHIP, m);
     }
-    x->pool = host_pool_create(c->host_threads ? c->host_threads : 8);
+    x->pool = host_pool_create(c->host_threads ? c->host_threads : default_host_threads());
     x->host_act.resize((size_t)x->nmax * x->I);
     x->poller = std::thread(host_branch_poll, x);
     *out = x;
@@ -638,8 +645,8 @@ ec_status ec_calibrate_bandwidth(ec_ctx* x, int32_t probe_experts, int32_t apply
                                  uint32_t* bh_out) {
     if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
     constexpr int kReps = 3; // timed passes after one warm-up; every pass reads different experts
-    if (probe_experts < 1 || probe_experts * (kReps + 1) > x->E || probe_experts > x->nmax)
-        return fail(x, EC_EINVAL, "need 1 <= probe_experts <= min(experts / 4, max_tokens * top_k)");
+    if (probe_experts < 1 || probe_experts * (kReps + 1) > x->E)
+        return fail(x, EC_EINVAL, "need 1 <= probe_experts <= experts / 4");
     HIPCHK(x, hipDeviceSynchronize()); // safe point
     const uint64_t eb = x->lay.expert_bytes, bytes = (uint64_t)probe_experts * eb;
     // BP: the fill path's source side, experts of pool layer 0 read over the link
@@ -672,20 +679,26 @@ ec_status ec_calibrate_bandwidth(ec_ctx* x, int32_t probe_experts, int32_t apply
     // not read before, so they come from memory, not from the host's caches), zero input
     double bh = 0.0;
     {
+        // a pass runs the host branch on probe_experts experts, as host jobs of at most
+        // max_tokens * top_k experts (the most one step can hand over)
         HostJob j{};
-        const int n = probe_experts;
+        const int per = std::min(probe_experts, x->nmax);
         const uint8_t* layer_base = x->host_pool + (uint64_t)(x->P - 1) * x->lay.layer_bytes;
-        std::vector<int32_t> rw(n);
-        for (int i = 0; i < n; ++i) rw[i] = -(1 + i);
+        std::vector<int32_t> rw(per);
+        for (int i = 0; i < per; ++i) rw[i] = -(1 + i);
         std::vector<uint8_t> xz((size_t)x->H * 4, 0);
-        j.n_experts = n; j.rewritten = rw.data(); j.T = 1; j.k = n; j.H = x->H; j.I = x->I; j.wdtype = x->wdt;
+        j.rewritten = rw.data(); j.T = 1; j.k = per; j.H = x->H; j.I = x->I; j.wdtype = x->wdt;
         j.x = xz.data(); j.y = x->y_host_pinned; j.act = x->host_act.data();
         double best_s = 1e30;
         std::lock_guard<std::mutex> lk(x->pool_mu);
         for (int r = 0; r <= kReps; ++r) {
-            for (int i = 0; i < n; ++i) j.expert_base[i] = layer_base + (uint64_t)(x->E - 1 - r * n - i) * eb;
             const auto t0 = std::chrono::steady_clock::now();
-            host_pool_run(x->pool, j);
+            for (int done = 0; done < probe_experts; done += per) {
+                j.n_experts = std::min(per, probe_experts - done);
+                for (int i = 0; i < j.n_experts; ++i)
+                    j.expert_base[i] = layer_base + (uint64_t)(x->E - 1 - r * probe_experts - done - i) * eb;
+                host_pool_run(x->pool, j);
+            }
             const double sec = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
             if (r > 0 && sec > 0.0 && sec < best_s) best_s = sec;
         }

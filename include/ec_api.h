@@ -103,7 +103,7 @@ typedef struct ec_config {
     int32_t victim_k;      /* K victim candidates per step (1..64); 0 = min(64, U_max) */
     uint32_t bp_mbps;      /* BP: expert transfer bandwidth (integer, any unit) */
     uint32_t bh_mbps;      /* BH: host expert processing bandwidth (>= 1, same unit) */
-    int32_t host_threads;  /* host branch worker threads; 0 = default (8) */
+    int32_t host_threads;  /* host branch worker threads; 0 = the host's hardware threads less 2 (1..32) */
     int32_t prefill_max_tokens; /* 0 = no prefill; else T_max for moe_prefill_layer */
     int32_t pool_layers;   /* layers the host pool holds (0 = L). With P < L, layer l reads its
                               experts from pool layer l mod P: the bytes moved per fill, host
@@ -188,7 +188,8 @@ ec_status ec_set_bandwidth(ec_ctx* ctx, uint32_t bp, uint32_t bh, void* stream);
  * before; the best timed pass counts. Results in MB/s (10^6 bytes/s) in
  * *bp_mbps and *bh_mbps (either may be NULL). apply != 0 also sets them as
  * ec_set_bandwidth would (BH at least 1).
- * 1 <= probe_experts <= min(experts / 4, max_tokens * top_k). */
+ * A pass hands the host branch probe_experts experts in jobs of at most
+ * max_tokens * top_k. 1 <= probe_experts <= experts / 4. */
 ec_status ec_calibrate_bandwidth(ec_ctx* ctx, int32_t probe_experts, int32_t apply, uint32_t* bp_mbps,
                                  uint32_t* bh_mbps);
 
