@@ -248,3 +248,57 @@ def test_calibration_in_host_only_mode_reports_no_link():
     assert bp == 0 and bh >= 1
     ctx.close()
     del pageable
+
+
+def test_stress_decode_full_size_sampled():
+    """Stress shapes as the bench runs them: 43 MXFP4 layers, 4096 slots, K = 64, batch 16 (up to 96
+    unique experts a layer step, so misses beyond K go to the host branch), 16-layer host pool;
+    sampled token rows against the oracle and every decision against the simulator."""
+    cfg = STRESS
+    pool = make_pool(cfg, L=16, layer_period=1)
+    ctx = make_ctx(cfg, pool, pool_layers=16)
+    steps = 4
+    outs, logits = run_decode(cfg, ctx, steps, cfg.L, cfg.T, lambda s, l: (s, l) in ((1, 7), (3, 42)))
+    for (s, l), (got, x, lg) in sorted(outs.items()):
+        toks = [0, 9, 15]
+        ref, _, _ = oracle_layer(cfg, l, x, lg, layer_period=1, tokens=toks)
+        assert row_rel_err(got[toks], ref) <= 1e-2, (s, l)
+    st = ctx.stats()
+    ref = sim_counts(cfg, logits, cfg.L, cfg.T, cfg.slots, cfg.K, cfg.bp, cfg.bh)
+    assert {k: st[k] for k in ref} == ref
+    ctx.close()
+
+
+def test_decode_outputs_across_rebuilds():
+    """cache_rebuild at safe points (40% -> 15% -> 40% of the experts, cold each time, clock going
+    on): outputs keep matching the oracle and decisions the simulator rebuilt at the same steps."""
+    import torch
+    import expert_cached_decode_amd as EC
+    from gen.configs import budget_slots
+    cfg = QWEN_DECODE.with_(L=3, slots=budget_slots(3, 256, 4000), bp=700, bh=1000)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool)
+    steps, L = 12, 3
+    logits = gen.decode_logits(cfg, steps=steps, T=1, L=L)
+    lg_dev = torch.from_numpy(logits).cuda()
+    out = empty_out(cfg, 1)
+    sim = LRUSim(L, cfg.E, cfg.slots, cfg.K, cfg.bp, cfg.bh)
+    plan = {4: 1500, 8: 4000}
+    for s in range(steps):
+        if s in plan:
+            C = ctx.rebuild(plan[s])
+            assert C == budget_slots(L, cfg.E, plan[s])
+            sim.rebuild(C)
+        for l in range(L):
+            x = gen.decode_x(cfg, s, l, 1)
+            EC.moe_decode_layer(ctx, l, x_to_device(cfg, x), lg_dev[s, l], 1, out)
+            r = sim.step(l, route_ids(logits[s, l], cfg.k).tolist())
+            if (s + l) % 3 == 0:
+                torch.cuda.synchronize()
+                ref, _, _ = oracle_layer(cfg, l, x, logits[s, l])
+                assert row_rel_err(out_to_host(cfg, out), ref) <= 1e-2, (s, l)
+    resid, sk, lru, clk = ctx.debug_state()
+    assert clk == steps * L
+    occ = sorted((int(k) for k in sk if k >= 0))
+    assert occ == sorted(l * cfg.E + e for (l, e) in sim.resid.keys())
+    ctx.close()
