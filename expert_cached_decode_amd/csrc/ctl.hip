@@ -7,12 +7,13 @@
 // recently used candidate slots, and the rewrite of logical routing ids to
 // cache slots), writing fixed-shape buffers plus device-resident counts.
 //
-// The control work is tiny and latency-bound, so it runs in ONE workgroup of
-// 16 wavefronts: bitmap dedup and prefix popcounts in LDS, ballot/popcount
-// block scans for the miss and cache-side lists, and a wave-wide bitonic
-// top-64 for the victims (each wave keeps its 64 oldest candidate slots
-// sorted across its lanes while streaming the slot table once; the 16 wave
-// lists are then merged pairwise in LDS).
+// The control work is tiny and latency-bound, so it runs in ONE workgroup (4
+// wavefronts when the step has at most 256 routed pairs, else 16): register
+// top-k with DPP wave reductions, bitmap dedup and prefix popcounts in LDS,
+// ballot/popcount block scans for the miss and cache-side lists, and the
+// victims from the slot table read once into registers (issued before the
+// routing, whose latency it then hides): q rounds of block-wide argmin over
+// the unique LRU keys.
 #include "ec_internal.h"
 
 namespace ec {
@@ -165,6 +166,28 @@ __device__ int block_scan_flag(bool f, int* s_wtot, int* total) {
     return wpre + __popcll(b & ((1ull << lane) - 1ull));
 }
 
+// Exclusive block scan of flag f plus the block-wide count of a second flag e (one pair
+// of barriers for both).
+template <int NT>
+__device__ int block_scan_flag2(bool f, bool e, int* s_wtot, int* total_f, int* total_e) {
+    constexpr int kCtlWaves = NT / 64;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint64_t bf = __ballot(f), be = __ballot(e);
+    if (lane == 0) { s_wtot[wave] = __popcll(bf); s_wtot[kCtlWaves + wave] = __popcll(be); }
+    __syncthreads();
+    int wpre = 0, tf = 0, te = 0;
+    for (int w2 = 0; w2 < kCtlWaves; ++w2) {
+        const int c = s_wtot[w2];
+        wpre += w2 < wave ? c : 0;
+        tf += c;
+        te += s_wtot[kCtlWaves + w2];
+    }
+    __syncthreads();
+    *total_f = tf;
+    *total_e = te;
+    return wpre + __popcll(bf & ((1ull << lane) - 1ull));
+}
+
 // Exclusive block scan of one int per thread (NT threads).
 template <int NT>
 __device__ int block_scan(int v, int* s_wtot, int* total) {
@@ -210,7 +233,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     __shared__ uint64_t s_wmin[2][kCtlWaves];
     __shared__ int32_t s_vslot[kMaxK];
     __shared__ int32_t s_vocc[kMaxK];
-    __shared__ int32_t s_wtot[kCtlWaves];
+    __shared__ int32_t s_wtot[2 * kCtlWaves];
     __shared__ int32_t s_misc[4];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -218,6 +241,17 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     const int n = T * k;
     const int nwords = (E + 31) >> 5;
     const uint64_t clk = *a.st.clock;
+
+    // 0. the slot table for the victim scan (LRU key + occupant of each slot), read
+    //    first: nothing before the victim rounds changes it
+    uint64_t pk[kSlotRegs];
+    int po[kSlotRegs];
+#pragma unroll
+    for (int p = 0; p < kSlotRegs; ++p) {
+        const int s = tid + kCtlThreads * p;
+        pk[p] = s < C ? a.st.slot_lru[s] : ~0ull;
+        po[p] = s < C ? a.st.slot_key[s] : -1;
+    }
 
     // 1. routing (fused) or routed ids from the caller
     if (a.logits) {
@@ -273,20 +307,11 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     }
     __syncthreads();
 
-    // 3. one round of global reads: residency of the unique experts, and the
-    //    slot table for the victim scan (LRU key + occupant of each slot)
+    // 3. residency of the unique experts
     const int r = tid;
     const bool valid = r < U;
     const int u = valid ? s_uniq[r] : 0;
     const int sl = valid ? a.st.resid[(int64_t)l * E + u] : -1;
-    uint64_t pk[kSlotRegs];
-    int po[kSlotRegs];
-#pragma unroll
-    for (int p = 0; p < kSlotRegs; ++p) {
-        const int s = tid + kCtlThreads * p;
-        pk[p] = s < C ? a.st.slot_lru[s] : ~0ull;
-        po[p] = s < C ? a.st.slot_key[s] : -1;
-    }
 
     // 4. classify, fill count q = min(m, floor(m*BP/BH), K, C - h)
     const bool miss = valid && sl < 0;
@@ -373,34 +398,46 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
         a.sb.cls[r] = cls;
         a.sb.slot[r] = slot_r;
     }
-    int n_gpu;
-    const int g = block_scan_flag<NT>(valid && cls != CLS_HOST, s_wtot, &n_gpu);
+    int n_gpu, n_ev;
+    const int g = block_scan_flag2<NT>(valid && cls != CLS_HOST, ev != 0, s_wtot, &n_gpu, &n_ev);
     if (valid) s_g[r] = cls != CLS_HOST ? g : -1;
-    int n_ev;
-    (void)block_scan_flag<NT>(ev != 0, s_wtot, &n_ev);
 
     // 7. rewrite (t, j) -> slot or -(1 + host index); pair lists per unique expert
-    if (tid <= U) s_off[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kCtlThreads) {
-        a.sb.rewritten[i] = s_slot[s_pos[i]];
-        a.sb.pos[i] = s_pos[i];
-        atomicAdd(&s_off[s_pos[i]], 1);
+    int cnt, off;
+    if (U == n) { // every unique expert has one pair (e.g. one token: its k ids are distinct)
+        for (int i = tid; i < n; i += kCtlThreads) {
+            const int pr = s_pos[i];
+            a.sb.rewritten[i] = s_slot[pr];
+            a.sb.pos[i] = pr;
+            a.sb.tok_pairs[pr] = i;
+            s_first[pr] = i;
+        }
+        __syncthreads();
+        cnt = valid ? 1 : 0;
+        off = r;
+    } else {
+        if (tid <= U) s_off[tid] = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += kCtlThreads) {
+            a.sb.rewritten[i] = s_slot[s_pos[i]];
+            a.sb.pos[i] = s_pos[i];
+            atomicAdd(&s_off[s_pos[i]], 1);
+        }
+        __syncthreads();
+        int ntot;
+        cnt = valid ? s_off[r] : 0;
+        off = block_scan<NT>(cnt, s_wtot, &ntot);
+        if (valid) s_off[r] = off;
+        __syncthreads();
+        for (int i = tid; i < n; i += kCtlThreads) {
+            const int pr = s_pos[i];
+            int within = 0;
+            for (int i2 = 0; i2 < i; ++i2) within += (s_pos[i2] == pr);
+            a.sb.tok_pairs[s_off[pr] + within] = i;
+            if (within == 0) s_first[pr] = i;
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    int ntot;
-    const int cnt = valid ? s_off[r] : 0;
-    const int off = block_scan<NT>(cnt, s_wtot, &ntot);
-    if (valid) s_off[r] = off;
-    __syncthreads();
-    for (int i = tid; i < n; i += kCtlThreads) {
-        const int pr = s_pos[i];
-        int within = 0;
-        for (int i2 = 0; i2 < i; ++i2) within += (s_pos[i2] == pr);
-        a.sb.tok_pairs[s_off[pr] + within] = i;
-        if (within == 0) s_first[pr] = i;
-    }
-    __syncthreads();
     // work descriptor of each cache-side expert: slot, first entry in tok_pairs, pair count, first pair
     if (valid && s_g[r] >= 0) a.sb.gpu_desc[s_g[r]] = make_int4(slot_r, off, cnt, s_first[r]);
 
