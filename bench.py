@@ -249,6 +249,11 @@ def main():
         "down_kernel": {"achieved": round(dn_gbs, 1), "unit": "GB/s", "frac": round(dn_gbs / HBM_PEAK_GBS, 4),
                         "bytes_per_launch": int(dn_bytes), "us_per_launch": round(dn_us, 3),
                         "traffic": measured_traffic("down_kernel") if args.workload == "qwen" else None},
+        "expert_streaming": {"kernels": "gate/up + down GEMV of one layer step (D9)",
+                             "bytes": int(gu_bytes + dn_bytes), "us": round(gu_us + dn_us, 3),
+                             "achieved": round((gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9, 1),
+                             "unit": "GB/s",
+                             "frac": round((gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "other_kernels_us": {"ctl": round(ctl_us, 3),
                              "fill_per_expert": round(fill_ms * 1e3 / max(st2["fills"], 1), 2)},
         "bandwidth_mbps": {"bp_measured": bp_meas, "bh_measured": bh_meas, "bp_used": bp_used, "bh_used": bh_used},

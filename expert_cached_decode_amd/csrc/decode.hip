@@ -299,7 +299,7 @@ constexpr uint32_t kHostWaitPolls = 1u << 22;
 __device__ __noinline__ void wait_host_branch(const DecodeArgs& a) {
     if (threadIdx.x == 0) {
         const uint32_t want = *a.hseq;
-        const bool relay = blockIdx.x == 0;
+        const bool relay = blockIdx.x == 0 && blockIdx.y == 0;
         const uint32_t* flag = relay ? a.host_done : a.hseen;
         uint32_t it = 0;
         while (relay ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != want
@@ -317,8 +317,9 @@ __device__ __noinline__ void wait_host_branch(const DecodeArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// Down GEMV + exact merge. A block of four wavefronts owns 4 R output rows h.
-// For each token t and each group of G of its pairs, the block first issues
+// Down GEMV + exact merge. A block of four wavefronts owns 4 R output rows h of
+// one token t (grid: H / (4 R) x T). For each group of G of the token's pairs,
+// the block first issues
 // the loads of its weight rows W_down,e(t,j)[h] (the group's indices come from
 // one vector load), then the group's activation vectors act[t,j]: staged in
 // LDS (STAGE: each is read from L2 once per block instead of once per row) or
@@ -334,7 +335,7 @@ __device__ __noinline__ void wait_host_branch(const DecodeArgs& a) {
 // d at slot c*QB + (d ^ (c % QB)), so the wave's 16-byte reads of one quad
 // index hit consecutive bank groups. With `residual` set, the layer input is
 // added to each merged output row before rounding (a chained MoE block).
-template <int WDT, int NCH, int R, int G, bool T1, bool HOST, bool FULL, bool STAGE>
+template <int WDT, int NCH, int R, int G, bool HOST, bool FULL, bool STAGE>
 __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
     constexpr int EPC = Fmt<WDT>::EPC;
     constexpr int AB = WDT == EC_DT_F32 ? 4 : 2; // bytes per activation element
@@ -347,8 +348,8 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
     const uint64_t down_off = 2ull * I * row_bytes<WDT>(H) + (uint64_t)row0 * rbi;
     const uint64_t dsc_off = 3ull * I * row_bytes<WDT>(H) + 2ull * I * (H / 32) + (uint64_t)row0 * (I / 32);
     const uint4* actq = reinterpret_cast<const uint4*>(a.act);
-    const int nt = T1 ? 1 : a.T;
-    for (int t = 0; t < nt; ++t) {
+    {
+        const int t = blockIdx.y; // one token per grid row: tokens run in parallel
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) hs[r] = 0.f;
         if (HOST) {
-            if (t == 0 && a.counts[CNT_HOST] > 0) wait_host_branch(a);
+            if (a.counts[CNT_HOST] > 0) wait_host_branch(a);
             // lane j < k carries pair j's host-side term (zero for cache-side pairs)
             const int pj = t * k + min(lane, k - 1);
             const bool hj = lane < k && a.rewritten[pj] < 0;
@@ -598,37 +599,25 @@ void launch_gu(const DecodeArgs& a, hipStream_t s) {
 
 template <int WDT, int NCH, int R, int G, bool STAGE>
 static void down_go2(const DecodeArgs& a, bool full, hipStream_t s) {
-    const dim3 blk(256), grid(a.H / (4 * R));
+    const dim3 blk(256), grid(a.H / (4 * R), a.T);
     const size_t lds = STAGE ? (size_t)G * a.I * (WDT == EC_DT_F32 ? 4 : 2) : 0;
-    if (a.T == 1) {
-#define EC_D1(HOST, FULL) hipLaunchKernelGGL((down_kernel<WDT, NCH, R, G, true, HOST, FULL, STAGE>), grid, blk, lds, s, a)
-        if constexpr (WDT != EC_DT_F32) { // f32 (small test shapes) only takes the guarded form
-            if (full) {
-                if (a.host_pairs) EC_D1(true, true); else EC_D1(false, true);
-                return;
-            }
+#define EC_D1(HOST, FULL) hipLaunchKernelGGL((down_kernel<WDT, NCH, R, G, HOST, FULL, STAGE>), grid, blk, lds, s, a)
+    if constexpr (WDT != EC_DT_F32) { // f32 (small test shapes) only takes the guarded form
+        if (full) {
+            if (a.host_pairs) EC_D1(true, true); else EC_D1(false, true);
+            return;
         }
-        if (a.host_pairs) EC_D1(true, false); else EC_D1(false, false);
-#undef EC_D1
-    } else if constexpr (STAGE) {
-        if constexpr (WDT != EC_DT_F32) {
-            if (full) {
-                hipLaunchKernelGGL((down_kernel<WDT, NCH, R, G, false, true, true, true>), grid, blk, lds, s, a);
-                return;
-            }
-        }
-        hipLaunchKernelGGL((down_kernel<WDT, NCH, R, G, false, true, false, true>), grid, blk, lds, s, a);
     }
+    if (a.host_pairs) EC_D1(true, false); else EC_D1(false, false);
+#undef EC_D1
 }
 
 // Activations go through LDS when each lane's slice is wide (MXFP4: 32 elements
-// per 16-byte chunk) or the step has several tokens; batch-1 bf16/f32 rows keep
-// them in registers, issued with the weights (no block barrier on the path).
+// per 16-byte chunk); bf16/f32 rows keep them in registers, issued with the
+// weights (no block barrier on the path).
 template <int WDT, int NCH, int R, int G>
 static void down_go(const DecodeArgs& a, bool full, hipStream_t s) {
-    if constexpr (WDT == EC_DT_MXFP4) down_go2<WDT, NCH, R, G, true>(a, full, s);
-    else if (a.T != 1) down_go2<WDT, NCH, R, G, true>(a, full, s);
-    else down_go2<WDT, NCH, R, G, false>(a, full, s);
+    down_go2<WDT, NCH, R, G, WDT == EC_DT_MXFP4>(a, full, s);
 }
 
 // Pairs per group: up to 8 (fewer for small top-k), G activation rows of LDS at
@@ -661,7 +650,7 @@ static void down_nch(const DecodeArgs& a, hipStream_t s) {
 void launch_down(const DecodeArgs& a, hipStream_t s) {
     if (a.wdtype == EC_DT_F32) down_nch<EC_DT_F32, 1>(a, s);
     else if (a.wdtype == EC_DT_BF16) down_nch<EC_DT_BF16, 2>(a, s);
-    else down_nch<EC_DT_MXFP4, 4>(a, s);
+    else down_nch<EC_DT_MXFP4, 2>(a, s);
 }
 
 } // namespace ec
