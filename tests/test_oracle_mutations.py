@@ -110,8 +110,50 @@ def _load_mutant(fname, old, new):
     src = open(os.path.join(ROOT, "oracle", fname)).read()
     assert old in src, (fname, old)
     mod = types.ModuleType("mutant_" + fname.replace(".", "_"))
+    mod.__dict__["__package__"] = "oracle"  # relative imports of the oracle package resolve
     exec(compile(src.replace(old, new), fname, "exec"), mod.__dict__)
     return mod
+
+
+CHAIN_MUTANTS = {
+    "bf16_truncate": ("up = (rem > half) | ((rem == half) & ((keep & np.uint64(1)) == np.uint64(1)))",
+                      "up = rem > rem"),
+    "bf16_ties_away": ("up = (rem > half) | ((rem == half) & ((keep & np.uint64(1)) == np.uint64(1)))",
+                       "up = rem >= half"),
+    "no_residual": ("nxt = xv + out", "nxt = out"),
+    "logits_transposed": ("return x @ w.T", "return x @ w"),
+    "margin_shifted": ("margin = srt[:, k - 1] - srt[:, k]", "margin = srt[:, k] - srt[:, k + 1]"),
+    "widen_low_half": ("b = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)",
+                       "b = np.asarray(bits, np.uint16).astype(np.uint32)"),
+}
+
+
+def _chain_pins_pass(mod, tmp_path):
+    """The pins of tests/test_oracle_chain.py against a given copy of oracle/chain.py."""
+    import tests.test_oracle_chain as T
+    saved = T.chain
+    T.chain = mod
+    try:
+        for f in (T.test_bf16_rounding_matches_hand_derived_values, T.test_bf16_round_trip_of_representable_values,
+                  T.test_rounding_is_to_the_nearest_bf16, T.test_gate_logits_exact_on_integers_and_brute_force_dot,
+                  T.test_gate_logits_linear_in_x, T.test_block_with_zero_down_weights_returns_its_input,
+                  T.test_block_routes_on_the_data_and_adds_the_residual):
+            f()
+        return True
+    except Exception:  # a failed pin or a crash both reject the copy
+        return False
+    finally:
+        T.chain = saved
+
+
+def test_unmutated_chain_oracle_passes(tmp_path):
+    assert _chain_pins_pass(_load_mutant("chain.py", "import numpy as np", "import numpy as np"), tmp_path)
+
+
+@pytest.mark.parametrize("name", sorted(CHAIN_MUTANTS))
+def test_chain_mutant_is_caught(name, tmp_path):
+    old, new = CHAIN_MUTANTS[name]
+    assert not _chain_pins_pass(_load_mutant("chain.py", old, new), tmp_path)
 
 
 def _lru_pins_pass(mod):
