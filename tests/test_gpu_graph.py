@@ -1,5 +1,6 @@
 """A decode step captured as one graph (all layers, fixed shapes, device-resident
-counts, host branch as a host node) replays bit-identically to the eager calls:
+counts; the host branch answers a mailbox the kernels write, so the graph holds
+kernels only) replays bit-identically to the eager calls:
 every replay's outputs and the final cache state (residency, slot keys, LRU keys,
 clock) match an eager run on an identical context. Replays alternate with eager
 work and synchronisations on the same process."""
@@ -80,3 +81,50 @@ def test_graph_replay_matches_eager(cfg, kw):
     for u, v in zip(sa[:3], sb[:3]):
         assert np.array_equal(u, v)
     assert sa[3] == sb[3] == steps * L
+
+
+def test_chained_block_graph_matches_eager():
+    """moe_decode_block (router GEMV, decode layer, residual) chained over the layers of a token
+    and captured as one graph: every replay equals the eager chain, with the host branch on."""
+    import torch
+    import expert_cached_decode_amd as EC
+    cfg = QWEN_DECODE.with_(L=3, slots=20, bp=500, bh=1000)
+    L, steps = cfg.L, 8
+    pool = make_pool(cfg)
+    W = [torch.from_numpy(gen.router_weights(cfg, l).view(np.int16)).cuda() for l in range(L)]
+    x0 = torch.from_numpy(np.stack([gen.decode_x(cfg, s, 0) for s in range(steps)]).view(np.int16)).cuda()
+
+    def chain(ctx, src, bufs, stream=None):
+        cur = src
+        for l in range(L):
+            EC.moe_decode_block(ctx, l, cur, W[l], 1, bufs[l], stream)
+            cur = bufs[l]
+
+    ctx = make_ctx(cfg, pool)
+    bufs = [torch.empty((1, cfg.H), dtype=torch.int16, device="cuda") for _ in range(L)]
+    eager = []
+    for s in range(steps):
+        chain(ctx, x0[s], bufs)
+        torch.cuda.synchronize()
+        eager.append(bufs[-1].clone())
+    st_e = ctx.debug_state()
+    ctx.close()
+
+    ctx = make_ctx(cfg, pool)
+    src = torch.empty((1, cfg.H), dtype=torch.int16, device="cuda")
+    bufs = [torch.empty((1, cfg.H), dtype=torch.int16, device="cuda") for _ in range(L)]
+    g, cap = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        chain(ctx, src, bufs, cap)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        src.copy_(x0[s])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs[-1], eager[s]), s
+    st_g = ctx.debug_state()
+    ctx.close()
+    for u, v in zip(st_e[:3], st_g[:3]):
+        assert np.array_equal(u, v)
+    assert st_e[3] == st_g[3]
