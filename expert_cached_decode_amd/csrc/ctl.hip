@@ -20,73 +20,105 @@ namespace ec {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-    uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
-    return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-    return ((uint64_t)hi << 32) | lo;
+// Order-preserving 32-bit key of a finite logit (larger logit, larger key; -0 equals +0;
+// every finite value maps above 0).
+__device__ __forceinline__ uint32_t value_key(float v) {
+    uint32_t u = __float_as_uint(v + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-wide maximum of a 64-bit key through DPP row shifts and row broadcasts
-// (no LDS traffic); the result is returned to every lane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#define EC_DPP_MAX_STEP(CTRL, RMASK)                                                               \
+// The logit a value_key came from (-0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Wave-wide float sum through DPP row shifts and row broadcasts (lane 63 total, read back).
+__device__ __forceinline__ float wave_sum_f(float v) {
+#define EC_DPP_ADDF(CTRL, RMASK) \
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, RMASK, 0xf, false))
+    EC_DPP_ADDF(0x111, 0xf);
+    EC_DPP_ADDF(0x112, 0xf);
+    EC_DPP_ADDF(0x114, 0xf);
+    EC_DPP_ADDF(0x118, 0xf);
+    EC_DPP_ADDF(0x142, 0xa);
+    EC_DPP_ADDF(0x143, 0xc);
+#undef EC_DPP_ADDF
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Wave-wide maximum of a 32-bit value through DPP row shifts and row broadcasts.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define EC_DPP_MAX32(CTRL, RMASK)                                                                  \
     {                                                                                              \
-        const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);                                 \
-        const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, RMASK, 0xf, false);         \
-        const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, RMASK, 0xf, false);         \
-        const uint64_t o = ((uint64_t)ohi << 32) | olo;                                            \
+        const uint32_t o = __builtin_amdgcn_update_dpp(0u, v, CTRL, RMASK, 0xf, false);            \
         v = o > v ? o : v;                                                                         \
     }
-    EC_DPP_MAX_STEP(0x111, 0xf) // row_shr:1
-    EC_DPP_MAX_STEP(0x112, 0xf) // row_shr:2
-    EC_DPP_MAX_STEP(0x114, 0xf) // row_shr:4
-    EC_DPP_MAX_STEP(0x118, 0xf) // row_shr:8  -> lane 15 of each row holds the row maximum
-    EC_DPP_MAX_STEP(0x142, 0xa) // row_bcast:15 into rows 1 and 3
-    EC_DPP_MAX_STEP(0x143, 0xc) // row_bcast:31 into rows 2 and 3 -> lane 63 holds the maximum
-#undef EC_DPP_MAX_STEP
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+    EC_DPP_MAX32(0x111, 0xf)
+    EC_DPP_MAX32(0x112, 0xf)
+    EC_DPP_MAX32(0x114, 0xf)
+    EC_DPP_MAX32(0x118, 0xf)
+    EC_DPP_MAX32(0x142, 0xa)
+    EC_DPP_MAX32(0x143, 0xc)
+#undef EC_DPP_MAX32
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Order-preserving key of (logit, expert): larger logit first, then lower id.
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-    uint32_t u = __float_as_uint(v + 0.0f); // -0 -> +0: equal logits tie on the id
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+// A row of up to 512 logits in registers, eight per lane (element lane + 64 i).
+__device__ __forceinline__ void load_row512(const float* row, int E, float* v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? row[e] : 0.f;
+    }
 }
 
 // Top-k of one row of E logits by one wavefront: ids by (logit desc, id asc),
 // weights = softmax over the selected logits. ids/w may be global; lds_ids /
 // lds_w (optional) receive copies. Rows of up to 512 logits are held in
-// registers (8 per lane) so the k selection rounds touch memory once.
+// registers so the k selection rounds touch memory once; rv is such a row
+// preloaded by load_row512, or null to read it here.
 __device__ void wave_topk(const float* row, int E, int k, int32_t* ids, float* w, int32_t* lds_ids,
-                          float* lds_w) {
+                          float* lds_w, const float* rv = nullptr) {
     const int lane = lane_id();
     float sel_v = 0.f;
     int sel_i = 0;
     if (E <= 512) {
-        uint64_t key[8];
+        float v[8];
+        if (rv) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = rv[i];
+        } else {
+            load_row512(row, E, v);
+        }
+        // 32-bit order keys of the logits (0 marks a taken or absent element); each round takes
+        // the wave maximum and then the lowest expert id holding it (ballots in id order)
+        uint32_t key[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = lane + 64 * i;
-            key[i] = e < E ? route_key(row[e], e) : 0ull;
+            key[i] = e < E ? value_key(v[i]) : 0u;
         }
+        const int nreg = (E + 63) >> 6; // uniform
         for (int j = 0; j < k; ++j) {
-            uint64_t b = 0;
+            uint32_t b = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) b = key[i] > b ? key[i] : b;
-            b = wave_max_u64(b);
-            const int e = (int)(0xffffffffu - (uint32_t)b);
+            const uint32_t M = wave_max_u32(b);
+            int e = -1;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i < nreg && e < 0) {
+                    const uint64_t bl = __ballot(key[i] == M);
+                    if (bl) e = 64 * i + __ffsll((unsigned long long)bl) - 1;
+                }
+            }
             if ((e & 63) == lane) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    if (i == (e >> 6)) key[i] = 0ull;
+                    if (i == (e >> 6)) key[i] = 0u;
             }
-            if (lane == j) { sel_i = e; sel_v = row[e]; }
+            if (lane == j) { sel_i = e; sel_v = key_value(M); }
         }
     } else {
         uint64_t chosen = 0; // bit i: element lane + 64 i already selected
@@ -107,10 +139,9 @@ __device__ void wave_topk(const float* row, int E, int k, int32_t* ids, float* w
             if (lane == j) { sel_v = bv; sel_i = bi; }
         }
     }
-    const float top = __shfl(sel_v, 0);
+    const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
     float ex = lane < k ? expf(sel_v - top) : 0.f;
-    float s = ex;
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    const float s = wave_sum_f(ex);
     if (lane < k) {
         ids[lane] = sel_i;
         w[lane] = ex / s;
@@ -242,8 +273,13 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     const int nwords = (E + 31) >> 5;
     const uint64_t clk = *a.st.clock;
 
-    // 0. the slot table for the victim scan (LRU key + occupant of each slot), read
-    //    first: nothing before the victim rounds changes it
+    // 0. loads issued up front, in the order they are needed: the routing rows of the first
+    //    tokens (one per wavefront) and then the slot table for the victim scan (LRU key +
+    //    occupant of each slot; nothing before the victim rounds changes it), whose latency the
+    //    routing and dedup then hide
+    const bool pre = a.logits && E <= 512 && wave < T;
+    float rv[8];
+    if (pre) load_row512(a.logits + (int64_t)wave * E, E, rv);
     uint64_t pk[kSlotRegs];
     int po[kSlotRegs];
 #pragma unroll
@@ -252,12 +288,13 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
         pk[p] = s < C ? a.st.slot_lru[s] : ~0ull;
         po[p] = s < C ? a.st.slot_key[s] : -1;
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // 1. routing (fused) or routed ids from the caller
     if (a.logits) {
         for (int t = wave; t < T; t += kCtlWaves)
             wave_topk(a.logits + (int64_t)t * E, E, k, a.sb.ids + t * k, a.sb.w + t * k, s_ids + t * k,
-                      s_w + t * k);
+                      s_w + t * k, (pre && t == wave) ? rv : nullptr);
     } else {
         for (int i = tid; i < n; i += kCtlThreads) s_ids[i] = a.ids_in[i];
     }
@@ -265,7 +302,16 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     if (tid == 0) s_misc[0] = 0;
     __syncthreads();
 
-    // 2. dedup: bitmap of routed experts, ranks by prefix popcount
+    // 2. dedup: bitmap of routed experts, ranks by prefix popcount; the residency of every
+    //    routed expert is read now (kept per pair, in registers) so its latency overlaps the dedup
+    constexpr int kPairRegs = kMaxPairs / NT;
+    int res_p[kPairRegs];
+#pragma unroll
+    for (int c = 0; c < kPairRegs; ++c) {
+        const int i = tid + kCtlThreads * c;
+        const int id = i < n ? s_ids[i] : -1;
+        res_p[c] = (id >= 0 && id < E) ? a.st.resid[(int64_t)l * E + id] : -1;
+    }
     for (int i = tid; i < n; i += kCtlThreads) {
         int id = s_ids[i];
         if (id < 0 || id >= E) s_misc[0] = 1;
@@ -301,9 +347,15 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
             bits &= bits - 1;
         }
     }
-    for (int i = tid; i < n; i += kCtlThreads) {
-        int id = s_ids[i];
-        s_pos[i] = s_wpre[id >> 5] + __popc(s_bits[id >> 5] & ((1u << (id & 31)) - 1u));
+#pragma unroll
+    for (int c = 0; c < kPairRegs; ++c) {
+        const int i = tid + kCtlThreads * c;
+        if (i < n) {
+            const int id = s_ids[i];
+            const int ps = s_wpre[id >> 5] + __popc(s_bits[id >> 5] & ((1u << (id & 31)) - 1u));
+            s_pos[i] = ps;
+            s_slot[ps] = res_p[c]; // residency by unique index (equal for repeated ids)
+        }
     }
     __syncthreads();
 
@@ -311,7 +363,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     const int r = tid;
     const bool valid = r < U;
     const int u = valid ? s_uniq[r] : 0;
-    const int sl = valid ? a.st.resid[(int64_t)l * E + u] : -1;
+    const int sl = valid ? s_slot[r] : -1;
 
     // 4. classify, fill count q = min(m, floor(m*BP/BH), K, C - h)
     const bool miss = valid && sl < 0;
