@@ -7,6 +7,8 @@
 // Work is split over worker threads by (expert, block of rows): first the
 // gate/up rows (activations of every token routed to the expert), then the
 // down rows, so each weight byte is read from host memory once per step.
+// bf16 and MXFP4 rows use the host's AVX-512 bf16 dot unit when it has one
+// (the SwiGLU activations are then rounded to bf16, as on the GPU), else AVX2.
 #include "host_experts.h"
 
 #include <immintrin.h>
@@ -85,6 +87,70 @@ float dot_row(int wdt, const uint8_t* row, const uint8_t* srow, const float* v, 
     return s;
 }
 
+// ---- AVX-512 BF16 path (the host's bf16 dot-product unit), chosen at run time ----
+#define EC_BF16_TARGET __attribute__((target("avx512f,avx512bw,avx512vl,avx512bf16")))
+
+bool host_has_bf16_dot() {
+    static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                           __builtin_cpu_supports("avx512bf16");
+    return ok;
+}
+
+// dot of n bf16 weights with n bf16 activations (n a multiple of 64); products exact in fp32
+EC_BF16_TARGET float dot_bf16_bf16(const uint16_t* w, const uint16_t* x, int n) {
+    __m512 a0 = _mm512_setzero_ps(), a1 = _mm512_setzero_ps();
+    for (int i = 0; i < n; i += 64) {
+        a0 = _mm512_dpbf16_ps(a0, (__m512bh)_mm512_loadu_si512(w + i), (__m512bh)_mm512_loadu_si512(x + i));
+        a1 = _mm512_dpbf16_ps(a1, (__m512bh)_mm512_loadu_si512(w + i + 32),
+                              (__m512bh)_mm512_loadu_si512(x + i + 32));
+    }
+    return _mm512_reduce_add_ps(_mm512_add_ps(a0, a1));
+}
+
+// bf16 bit patterns of the 16 E2M1 codes (bit 3 the sign), OCP MX v1.0
+alignas(64) const uint16_t kE2M1Bf16[32] = {0x0000, 0x3F00, 0x3F80, 0x3FC0, 0x4000, 0x4040, 0x4080, 0x40C0,
+                                            0x8000, 0xBF00, 0xBF80, 0xBFC0, 0xC000, 0xC040, 0xC080, 0xC0C0};
+
+// MXFP4 row (codes + E8M0 scales) with n bf16 activations: each 32-code block becomes 32 bf16
+// weights by table lookup, its scale 2^(s-127) added to their exponent fields (exact while the
+// results stay normal: 2 <= s <= 252, checked by the caller), then the bf16 dot unit
+EC_BF16_TARGET float dot_mx_bf16(const uint8_t* codes, const uint8_t* sc, const uint16_t* x, int n) {
+    const __m512i lut = _mm512_load_si512(kE2M1Bf16);
+    const __m128i lo_mask = _mm_set1_epi8(0x0f);
+    __m512 acc = _mm512_setzero_ps();
+    for (int b = 0; b < n / 32; ++b) {
+        const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + 16 * b));
+        const __m128i lo = _mm_and_si128(raw, lo_mask), hi = _mm_and_si128(_mm_srli_epi16(raw, 4), lo_mask);
+        const __m256i el = _mm256_set_m128i(_mm_unpackhi_epi8(lo, hi), _mm_unpacklo_epi8(lo, hi));
+        __m512i w = _mm512_permutexvar_epi16(_mm512_cvtepu8_epi16(el), lut);
+        const __mmask32 nz = _mm512_test_epi16_mask(w, _mm512_set1_epi16(0x7fff));
+        w = _mm512_mask_add_epi16(w, nz, w, _mm512_set1_epi16((int16_t)(((int)sc[b] - 127) * 128)));
+        acc = _mm512_dpbf16_ps(acc, (__m512bh)w, (__m512bh)_mm512_loadu_si512(x + 32 * b));
+    }
+    return _mm512_reduce_add_ps(acc);
+}
+
+bool scales_in_range(const uint8_t* sc, int nblocks) {
+    for (int b = 0; b < nblocks; ++b)
+        if (sc[b] < 2 || sc[b] > 252) return false;
+    return true;
+}
+
+inline uint16_t bf16_rne(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// dot of a weight row with activations held both as f32 (v) and as bf16 (vb, or null)
+inline float dot_row_any(int wdt, const uint8_t* row, const uint8_t* srow, const float* v, const uint16_t* vb,
+                         int n) {
+    if (vb && wdt == 1) return dot_bf16_bf16(reinterpret_cast<const uint16_t*>(row), vb, n);
+    if (vb && wdt == 2 && scales_in_range(srow, n / 32)) return dot_mx_bf16(row, srow, vb, n);
+    return dot_row(wdt, row, srow, v, n);
+}
+
 } // namespace
 
 struct HostPool {
@@ -98,6 +164,8 @@ struct HostPool {
     std::vector<int> task_expert, task_r0;   // phase-1 and phase-2 task tables
     std::vector<std::vector<int>> pairs_of;  // host index -> pairs
     std::vector<float> xf;                   // [T][H] activations widened to f32
+    std::vector<uint16_t> act_b;             // [T*k][I] SwiGLU activations rounded to bf16 (bf16 dot path)
+    bool bf16dot = false;                    // bf16/MXFP4 weights on a host with the bf16 dot unit
     int n1 = 0, n2 = 0;
     std::atomic<int> next1{0}, next2{0}, done1{0}, done2{0}, arrived{0};
     int nworkers = 0;
@@ -119,9 +187,13 @@ struct HostPool {
                 const uint8_t* u = base + (uint64_t)I * rbH + i * rbH;
                 for (int p : pairs_of[e]) {
                     const float* xv = xf.data() + (uint64_t)(p / j.k) * H;
-                    float gv = dot_row(j.wdtype, g, gsc + (uint64_t)i * (H / 32), xv, H);
-                    float uv = dot_row(j.wdtype, u, usc + (uint64_t)i * (H / 32), xv, H);
-                    j.act[(uint64_t)p * I + i] = gv / (1.f + std::exp(-gv)) * uv;
+                    const uint16_t* xb = bf16dot ? reinterpret_cast<const uint16_t*>(j.x) + (uint64_t)(p / j.k) * H
+                                                 : nullptr;
+                    float gv = dot_row_any(j.wdtype, g, gsc + (uint64_t)i * (H / 32), xv, xb, H);
+                    float uv = dot_row_any(j.wdtype, u, usc + (uint64_t)i * (H / 32), xv, xb, H);
+                    const float hv = gv / (1.f + std::exp(-gv)) * uv;
+                    j.act[(uint64_t)p * I + i] = hv;
+                    if (bf16dot) act_b[(uint64_t)p * I + i] = bf16_rne(hv);
                 }
             }
             done1.fetch_add(1, std::memory_order_release);
@@ -136,7 +208,8 @@ struct HostPool {
             for (int h = r0; h < r0 + kRows && h < H; ++h)
                 for (int p : pairs_of[e])
                     j.y[((uint64_t)(p / j.k) * H + h) * j.k + p % j.k] =
-                        dot_row(j.wdtype, d + h * rbI, dsc + (uint64_t)h * (I / 32), j.act + (uint64_t)p * I, I);
+                        dot_row_any(j.wdtype, d + h * rbI, dsc + (uint64_t)h * (I / 32), j.act + (uint64_t)p * I,
+                                    bf16dot ? act_b.data() + (uint64_t)p * I : nullptr, I);
             done2.fetch_add(1, std::memory_order_release);
         }
     }
@@ -182,6 +255,10 @@ void host_pool_run(HostPool* p, const HostJob& j) {
             int h = -j.rewritten[i] - 1;
             if (h < j.n_experts) p->pairs_of[h].push_back(i);
         }
+    // bf16 and MXFP4 weights meet bf16 activations in the bf16 dot unit when the host has one:
+    // x is bf16 already, the SwiGLU activations are rounded to bf16 as on the GPU
+    p->bf16dot = j.wdtype != 0 && host_has_bf16_dot();
+    if (p->bf16dot) p->act_b.resize((size_t)j.T * j.k * j.I);
     p->xf.resize((size_t)j.T * j.H);
     for (size_t i = 0; i < p->xf.size(); ++i)
         p->xf[i] = j.wdtype == 0 ? reinterpret_cast<const float*>(j.x)[i]
