@@ -266,6 +266,7 @@ def main():
     if cold:
         result["cold_start"] = cold
     if args.workload == "stress":
+        result["cache_ctl"] = bench_cache_ctl(ctx, cfg)
         result["rebuild"] = bench_rebuild(ctx, cfg)
         if args.sweep_locality:
             result["locality_sweep"] = bench_locality_sweep(ctx, cfg)
@@ -399,6 +400,44 @@ def bench_locality_sweep(ctx, cfg, ps=(0.0, 0.3, 0.6, 0.9), warm=16, steps=48):
             del graph
     ctx.rebuild(budget)
     return out
+
+
+def bench_cache_ctl(ctx, cfg, calls=10000, batch=100):
+    """The fused cache-control step alone (expert_cache_step on given ids): T tokens x k experts,
+    ids drawn per call from the workload's routing, C slots, K victim candidates; per-call time from
+    events around batches of calls, median over the batches."""
+    import torch
+    import gen
+    import expert_cached_decode_amd as EC
+    T, L = cfg.T, cfg.L
+    lg = gen.decode_logits(cfg, steps=64)
+    ids = torch.from_numpy(np.stack([route_top_k(lg[s, l], cfg.k) for s in range(64) for l in range(L)])).cuda()
+    n = ids.shape[0]
+    stream = torch.cuda.current_stream()
+    for i in range(200):
+        EC.expert_cache_step(ctx, i % L, ids[i % n], T, stream)
+    torch.cuda.synchronize()
+    times = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for b in range(calls // batch):
+        e0.record()
+        for i in range(batch):
+            j = b * batch + i
+            EC.expert_cache_step(ctx, j % L, ids[j % n], T, stream)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / batch)
+    out = {"calls": calls, "us_per_call_median": round(float(np.median(times)), 3),
+           "us_per_call_min": round(float(np.min(times)), 3), "T": T, "k": cfg.k, "slots": cfg.slots, "K": cfg.K}
+    log("cache control alone (T=%d, k=%d, C=%d, K=%d): %.2f us per call (median of %d batches of %d)"
+        % (T, cfg.k, cfg.slots, cfg.K, out["us_per_call_median"], calls // batch, batch))
+    return out
+
+
+def route_top_k(logits, k):
+    """Routed ids [T, k] by (logit desc, id asc) (input preparation for the control-step timing)."""
+    order = np.lexsort((np.broadcast_to(np.arange(logits.shape[-1]), logits.shape), -logits), axis=-1)
+    return order[:, :k].astype(np.int32)
 
 
 def bench_rebuild(ctx, cfg):
