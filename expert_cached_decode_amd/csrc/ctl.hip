@@ -8,8 +8,9 @@
 // cache slots), writing fixed-shape buffers plus device-resident counts.
 //
 // The control work is tiny and latency-bound, so it runs in ONE workgroup (4
-// wavefronts when the step has at most 256 routed pairs, else 16): register
-// top-k with DPP wave reductions, bitmap dedup and prefix popcounts in LDS,
+// wavefronts when the step has at most 256 routed pairs, else 16): top-k with
+// DPP wave reductions (one token: a 64-logit segment per wavefront, then one
+// ranking pass over their candidates), bitmap dedup and prefix popcounts in LDS,
 // ballot/popcount block scans for the miss and cache-side lists, and the
 // victims from the slot table read once into registers (issued before the
 // routing, whose latency it then hides): q rounds of block-wide argmin over
@@ -63,29 +64,43 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// A row of up to 512 logits in registers, eight per lane (element lane + 64 i).
+// Inclusive wave-wide prefix sum through the same DPP row shifts and row broadcasts.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+#define EC_DPP_ADDI(CTRL, RMASK) v += __builtin_amdgcn_update_dpp(0, v, CTRL, RMASK, 0xf, false)
+    EC_DPP_ADDI(0x111, 0xf);
+    EC_DPP_ADDI(0x112, 0xf);
+    EC_DPP_ADDI(0x114, 0xf);
+    EC_DPP_ADDI(0x118, 0xf);
+    EC_DPP_ADDI(0x142, 0xa);
+    EC_DPP_ADDI(0x143, 0xc);
+#undef EC_DPP_ADDI
+    return v;
+}
+
+// A row of up to 512 logits in registers, eight per lane (element lane + 64 i). The loads are
+// unconditional (index clamped into the row) so all eight are in flight together.
 __device__ __forceinline__ void load_row512(const float* row, int E, float* v) {
     const int lane = lane_id();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? row[e] : 0.f;
+        v[i] = row[e < E ? e : E - 1];
     }
 }
 
 // Top-k of one row of E logits by one wavefront: ids by (logit desc, id asc),
 // weights = softmax over the selected logits. ids/w may be global; lds_ids /
 // lds_w (optional) receive copies. Rows of up to 512 logits are held in
-// registers so the k selection rounds touch memory once; rv is such a row
-// preloaded by load_row512, or null to read it here.
-__device__ void wave_topk(const float* row, int E, int k, int32_t* ids, float* w, int32_t* lds_ids,
-                          float* lds_w, const float* rv = nullptr) {
+// registers so the k selection rounds touch memory once; with use_rv the row
+// is rv, preloaded by load_row512, else it is read here.
+__device__ __forceinline__ void wave_topk(const float* row, int E, int k, int32_t* ids, float* w,
+                                          int32_t* lds_ids, float* lds_w, const float (&rv)[8], bool use_rv) {
     const int lane = lane_id();
     float sel_v = 0.f;
     int sel_i = 0;
     if (E <= 512) {
         float v[8];
-        if (rv) {
+        if (use_rv) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = rv[i];
         } else {
@@ -99,25 +114,21 @@ __device__ void wave_topk(const float* row, int E, int k, int32_t* ids, float* w
             const int e = lane + 64 * i;
             key[i] = e < E ? value_key(v[i]) : 0u;
         }
-        const int nreg = (E + 63) >> 6; // uniform
         for (int j = 0; j < k; ++j) {
             uint32_t b = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) b = key[i] > b ? key[i] : b;
             const uint32_t M = wave_max_u32(b);
-            int e = -1;
+            // wave-uniform: the first register (lowest id block) whose ballot holds the maximum
+            int e = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i < nreg && e < 0) {
-                    const uint64_t bl = __ballot(key[i] == M);
-                    if (bl) e = 64 * i + __ffsll((unsigned long long)bl) - 1;
-                }
+            for (int i = 7; i >= 0; --i) {
+                const uint64_t bl = __ballot(key[i] == M);
+                if (bl) e = 64 * i + __ffsll((unsigned long long)bl) - 1;
             }
-            if ((e & 63) == lane) {
+            const bool mine = (e & 63) == lane;
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (i == (e >> 6)) key[i] = 0u;
-            }
+            for (int i = 0; i < 8; ++i) key[i] = (mine && i == (e >> 6)) ? 0u : key[i];
             if (lane == j) { sel_i = e; sel_v = key_value(M); }
         }
     } else {
@@ -153,7 +164,61 @@ __global__ __launch_bounds__(256) void route_kernel(const float* logits, int T, 
                                                     float* w) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    wave_topk(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k, nullptr, nullptr);
+    const float none[8] = {};
+    wave_topk(logits + (int64_t)t * E, E, k, ids + (int64_t)t * k, w + (int64_t)t * k, nullptr, nullptr, none,
+              false);
+}
+
+// Top-k of one token's E <= 64 * (NT / 64) logits by the whole block: wavefront w takes the
+// top-k of logits 64w .. 64w + 63 (one per lane: k rounds of a DPP wave maximum and one ballot,
+// lowest lane = lowest id on ties), then wavefront 0 ranks the wavefronts' candidates by (logit
+// desc, id asc) in one pass. The weights are the softmax over the selected logits, computed
+// lane by lane exactly as in wave_topk. v is this thread's logit (element 64 wave + lane).
+template <int NT>
+__device__ __forceinline__ void block_topk1(float v, int E, int k, int32_t* ids, float* w, int32_t* lds_ids,
+                                            float* lds_w, uint32_t* s_ck, int32_t* s_ci) {
+    constexpr int kWaves = NT / 64;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    uint32_t key = 64 * wave + lane < E ? value_key(v) : 0u;
+    uint32_t ck = 0u;
+    int ci = -1;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t M = wave_max_u32(key);
+        const uint64_t bl = M ? __ballot(key == M) : 0ull;
+        if (bl) {
+            const int wl = __ffsll((unsigned long long)bl) - 1;
+            if (lane == wl) key = 0u;
+            if (lane == j) { ck = M; ci = 64 * wave + wl; }
+        }
+    }
+    if (lane < k) { s_ck[wave * k + lane] = ck; s_ci[wave * k + lane] = ci; }
+    __syncthreads();
+    if (wave == 0) {
+        const int nc = kWaves * k;
+        const uint32_t mk = lane < nc ? s_ck[lane] : 0u;
+        const uint32_t mi = lane < nc ? (uint32_t)s_ci[lane] : ~0u;
+        int rank = 0; // candidates are read from this wavefront's registers, one lane at a time
+#pragma unroll 4
+        for (int c = 0; c < nc; ++c) {
+            const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mk, c);
+            const uint32_t oi = (uint32_t)__builtin_amdgcn_readlane((int)mi, c);
+            rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
+        }
+        if (mk && rank < k) { lds_ids[rank] = (int)mi; lds_w[rank] = key_value(mk); }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const float sel_v = lane < k ? lds_w[lane] : 0.f;
+        const int sel_i = lane < k ? lds_ids[lane] : 0;
+        const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
+        const float ex = lane < k ? expf(sel_v - top) : 0.f;
+        const float sum = wave_sum_f(ex);
+        if (lane < k) {
+            ids[lane] = sel_i;
+            w[lane] = ex / sum;
+            lds_w[lane] = ex / sum;
+        }
+    }
 }
 
 // Wave-wide minimum of a 64-bit key through DPP row shifts and row broadcasts.
@@ -224,11 +289,7 @@ template <int NT>
 __device__ int block_scan(int v, int* s_wtot, int* total) {
     constexpr int kCtlWaves = NT / 64;
     const int lane = lane_id(), wave = threadIdx.x >> 6;
-    int incl = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
+    const int incl = wave_incl_scan(v);
     if (lane == 63) s_wtot[wave] = incl;
     __syncthreads();
     int wpre = 0, tot = 0;
@@ -266,6 +327,9 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     __shared__ int32_t s_vocc[kMaxK];
     __shared__ int32_t s_wtot[2 * kCtlWaves];
     __shared__ int32_t s_misc[4];
+    __shared__ int32_t s_res[512];
+    __shared__ uint32_t s_ck[64];
+    __shared__ int32_t s_ci[64];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int E = a.E, k = a.k, T = a.T, l = a.layer, C = a.C;
@@ -277,40 +341,70 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     //    tokens (one per wavefront) and then the slot table for the victim scan (LRU key +
     //    occupant of each slot; nothing before the victim rounds changes it), whose latency the
     //    routing and dedup then hide
-    const bool pre = a.logits && E <= 512 && wave < T;
-    float rv[8];
+    //    (one token with E <= 64 per wavefront: each wavefront holds a 64-logit segment), then
+    //    the layer's residency row (E <= 512; staged through LDS after the routing)
+    const bool seg = a.logits && T == 1 && E <= 64 * kCtlWaves && kCtlWaves * k <= 64;
+    const bool pre = a.logits && !seg && E <= 512 && wave < T;
+    float rv[8] = {};
     if (pre) load_row512(a.logits + (int64_t)wave * E, E, rv);
+    // One unconditional load per thread for the segment's logit or, without logits, for the
+    // thread's routed id (n <= NT: the launch picks NT >= T * k); otherwise it reads a word that
+    // is always valid. Unconditional loads keep the wait counts static, so no use of an early
+    // load waits for the loads issued after it.
+    const int seg_e = 64 * wave + lane;
+    const uint32_t* in_p = seg ? reinterpret_cast<const uint32_t*>(a.logits) + (seg_e < E ? seg_e : E - 1)
+                           : (!a.logits && n > 0) ? reinterpret_cast<const uint32_t*>(a.ids_in) + (tid < n ? tid : 0)
+                                                  : reinterpret_cast<const uint32_t*>(a.st.clock);
+    const uint32_t in_v = *in_p;
+    const float segv = __uint_as_float(in_v);
+    constexpr int kResRegs = (512 + NT - 1) / NT;
+    const bool rrow = E <= 512;
+    int rres[kResRegs];
+#pragma unroll
+    for (int p = 0; p < kResRegs; ++p) {
+        const int e = tid + NT * p;
+        rres[p] = a.st.resid[(int64_t)l * E + (e < E ? e : E - 1)];
+    }
     uint64_t pk[kSlotRegs];
     int po[kSlotRegs];
+    // (every load is unconditional, its index clamped into the table, so that the first use of
+    // the routing row waits for that row alone and not for the whole table)
 #pragma unroll
     for (int p = 0; p < kSlotRegs; ++p) {
         const int s = tid + kCtlThreads * p;
-        pk[p] = s < C ? a.st.slot_lru[s] : ~0ull;
-        po[p] = s < C ? a.st.slot_key[s] : -1;
+        pk[p] = a.st.slot_lru[s < C ? s : 0];
+        po[p] = a.st.slot_key[s < C ? s : 0];
     }
     __builtin_amdgcn_sched_barrier(0);
 
     // 1. routing (fused) or routed ids from the caller
-    if (a.logits) {
+    if (seg) {
+        block_topk1<NT>(segv, E, k, a.sb.ids, a.sb.w, s_ids, s_w, s_ck, s_ci);
+    } else if (a.logits) {
         for (int t = wave; t < T; t += kCtlWaves)
             wave_topk(a.logits + (int64_t)t * E, E, k, a.sb.ids + t * k, a.sb.w + t * k, s_ids + t * k,
-                      s_w + t * k, (pre && t == wave) ? rv : nullptr);
-    } else {
-        for (int i = tid; i < n; i += kCtlThreads) s_ids[i] = a.ids_in[i];
+                      s_w + t * k, rv, pre && t == wave);
+    } else if (tid < n) {
+        s_ids[tid] = (int32_t)in_v;
     }
     for (int wd = tid; wd < nwords; wd += kCtlThreads) s_bits[wd] = 0;
     if (tid == 0) s_misc[0] = 0;
+    if (rrow) {
+#pragma unroll
+        for (int p = 0; p < kResRegs; ++p)
+            if (tid + NT * p < E) s_res[tid + NT * p] = rres[p];
+    }
     __syncthreads();
 
     // 2. dedup: bitmap of routed experts, ranks by prefix popcount; the residency of every
-    //    routed expert is read now (kept per pair, in registers) so its latency overlaps the dedup
+    //    routed expert is looked up now (from the staged row, else from memory, kept per pair)
     constexpr int kPairRegs = kMaxPairs / NT;
     int res_p[kPairRegs];
 #pragma unroll
     for (int c = 0; c < kPairRegs; ++c) {
         const int i = tid + kCtlThreads * c;
         const int id = i < n ? s_ids[i] : -1;
-        res_p[c] = (id >= 0 && id < E) ? a.st.resid[(int64_t)l * E + id] : -1;
+        res_p[c] = (id >= 0 && id < E) ? (rrow ? s_res[id] : a.st.resid[(int64_t)l * E + id]) : -1;
     }
     for (int i = tid; i < n; i += kCtlThreads) {
         int id = s_ids[i];
@@ -327,11 +421,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
         int w0 = 2 * lane, w1 = 2 * lane + 1;
         int c0 = w0 < nwords ? __popc(s_bits[w0]) : 0;
         int c1 = w1 < nwords ? __popc(s_bits[w1]) : 0;
-        int v = c0 + c1, incl = v;
-        for (int off = 1; off < 64; off <<= 1) {
-            int o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
+        const int v = c0 + c1, incl = wave_incl_scan(v);
         if (w0 < nwords) s_wpre[w0] = incl - v;
         if (w1 < nwords) s_wpre[w1] = incl - v + c0;
         if (lane == 63) s_misc[1] = incl;
@@ -383,9 +473,10 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     //    previous one), the owner of each minimum records its slot and occupant.
     if (q > 0) {
 #pragma unroll
-        for (int p = 0; p < kSlotRegs; ++p) { // slots hit in this step are not candidates
+        for (int p = 0; p < kSlotRegs; ++p) { // slots past C and slots hit in this step are not candidates
             const uint32_t e = (uint32_t)(po[p] - l * E); // occupant in this layer?
-            if (e < (uint32_t)E && ((s_bits[e >> 5] >> (e & 31)) & 1u)) pk[p] = ~0ull;
+            const bool past = tid + kCtlThreads * p >= C;
+            if (past || (e < (uint32_t)E && ((s_bits[e >> 5] >> (e & 31)) & 1u))) pk[p] = ~0ull;
         }
         // each thread's smallest key (above lo), kept across rounds: only the owner of a
         // round's minimum has to look again
