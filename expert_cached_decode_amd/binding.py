@@ -57,7 +57,7 @@ EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec
            "ec_set_bandwidth", "moe_route", "expert_cache_step", "moe_decode_layer", "moe_prefill_layer",
            "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
            "ec_kernel_timing", "ec_kernel_time", "ec_calibrate_bandwidth", "moe_gate_logits",
-           "moe_decode_block", "ec_bank_write", "ec_bank_read"]
+           "moe_decode_block", "ec_bank_write", "ec_bank_read", "ec_last_step"]
 KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
@@ -81,6 +81,7 @@ def lib():
         L.ec_set_bandwidth.argtypes = [c_vp, c_u32, c_u32, c_vp]
         L.moe_route.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
         L.expert_cache_step.argtypes = [c_vp, c_i32, c_vp, c_i32, P(ec_step_view), c_vp]
+        L.ec_last_step.argtypes = [c_vp, P(ec_step_view)]
         L.moe_decode_layer.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]
         L.moe_prefill_layer.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]
         L.ec_set_prefill_overlap.argtypes = [c_vp, c_i32]
@@ -181,6 +182,13 @@ def moe_route(logits, T, E, k, ids, w, stream=None):
 def expert_cache_step(ctx, layer, ids, T, stream=None):
     v = ec_step_view()
     check(lib().expert_cache_step(ctx.handle, layer, _ptr(ids), T, ctypes.byref(v), _stream(stream)), ctx.handle)
+    return v
+
+
+def last_step(ctx):
+    """Device views of the step buffers the last step call on ctx wrote (ec_last_step)."""
+    v = ec_step_view()
+    check(lib().ec_last_step(ctx.handle, ctypes.byref(v)), ctx.handle)
     return v
 
 

@@ -430,6 +430,12 @@ ec_status expert_cache_step(ec_ctx* x, int32_t layer, const int32_t* ids, int32_
     return EC_OK;
 }
 
+ec_status ec_last_step(const ec_ctx* x, ec_step_view* out) {
+    if (!x || !out) return fail(nullptr, EC_EINVAL, "ctx and out must be non-NULL");
+    fill_view(const_cast<ec_ctx*>(x), out);
+    return EC_OK;
+}
+
 // Host branch ("Bandwidth-adaptive execution": misses left to the host are computed
 // there in place). The cache-control kernel writes a mailbox into pinned memory and
 // rings the doorbell with a new sequence number; this thread polls the doorbell,

@@ -621,6 +621,236 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     }
 }
 
+// The control step of one token (fused routing, E <= 256, k <= 16, C <= 5120: the batch-1
+// decode step). Same outputs and state updates as ctl_kernel, with fewer block barriers
+// and no dependent global loads: the token-level work (routing stage 2 and softmax, dedup,
+// classification, the fill count, assignment, rewrite, outputs and the mailbox) runs in
+// wavefront 0 with register permutes (lane r holds unique expert r, lane j routed pair j),
+// and all four wavefronts meet only for the routing candidates and for the victim scan over
+// the slot table. Everything read from memory (logits, the layer's residency row, the slot
+// table, the layer's stats row, the clock, BP/BH, the mailbox sequence) is loaded up front.
+// SR: slot-table entries per thread (C <= 256 SR).
+template <int SR>
+__global__ __launch_bounds__(256) void ctl1_kernel(CtlArgs a) {
+    constexpr int NT = 256, kWaves = NT / 64, kSlotRegs = SR;
+    __shared__ uint32_t s_ck[64];
+    __shared__ int32_t s_ci[64];
+    __shared__ int32_t s_res[256];
+    __shared__ uint32_t s_bits[8];
+    __shared__ uint64_t s_wmin[2][kWaves];
+    __shared__ int32_t s_vslot[kMaxK];
+    __shared__ int32_t s_vocc[kMaxK];
+    __shared__ int32_t s_q;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int E = a.E, k = a.k, l = a.layer, C = a.C;
+    const uint64_t lt = (1ull << lane) - 1ull;
+
+    // 0. loads, all unconditional (indices clamped), in the order they are needed
+    const int ec = tid < E ? tid : E - 1;
+    const float lv = a.logits[ec];                          // logit of expert tid
+    const int rres = a.st.resid[(int64_t)l * E + ec];       // residency of expert tid
+    uint64_t pk[kSlotRegs];
+    int po[kSlotRegs];
+#pragma unroll
+    for (int p = 0; p < kSlotRegs; ++p) {
+        const int s = tid + NT * p;
+        pk[p] = a.st.slot_lru[s < C ? s : 0];
+        po[p] = a.st.slot_key[s < C ? s : 0];
+    }
+    const unsigned long long st_v = a.st.stats[(int64_t)l * ST_N + (lane < ST_N ? lane : 0)];
+    const uint64_t clk = *a.st.clock;
+    const uint32_t bp = a.st.bw[0], bh = a.st.bw[1];
+    const uint32_t hs = *a.st.hseq;
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 1. routing, stage 1: the top-k of this wavefront's 64 logits (ties: lowest id)
+    uint32_t key = tid < E ? value_key(lv) : 0u;
+    uint32_t ck = 0u;
+    int ci = -1;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t M = wave_max_u32(key);
+        const uint64_t bl = M ? __ballot(key == M) : 0ull;
+        if (bl) {
+            const int wl = __ffsll((unsigned long long)bl) - 1;
+            if (lane == wl) key = 0u;
+            if (lane == j) { ck = M; ci = 64 * wave + wl; }
+        }
+    }
+    if (lane < k) { s_ck[wave * k + lane] = ck; s_ci[wave * k + lane] = ci; }
+    if (tid < E) s_res[tid] = rres;
+    if (tid < 8) s_bits[tid] = 0u;
+    __syncthreads();
+
+    // wavefront 0: per routed pair j (lane j < k) and per unique expert r (lane r < U = k)
+    int sel_i = 0, pos = 0, u = 0, pr = 0, sl = -1, midx = 0, m = 0, h = 0;
+    float wj = 0.f;
+    bool valid = false, miss = false;
+    if (wave == 0) {
+        // routing, stage 2: k rounds of a DPP wave maximum over the candidates (lane c holds
+        // candidate c; at least k are present since E >= k). Candidates sit in lane order of
+        // (wavefront, selection round), so among equal logits the lowest lane holds the lowest
+        // id. Lane j takes the j-th; the weights are the softmax over the k selected logits,
+        // computed lane by lane as in wave_topk.
+        const int nc = kWaves * k;
+        uint32_t ck2 = lane < nc ? s_ck[lane] : 0u;
+        const int ci2 = lane < nc ? s_ci[lane] : -1;
+        uint32_t sel_k = 0u;
+        for (int j = 0; j < k; ++j) {
+            const uint32_t M = wave_max_u32(ck2);
+            const int wl = __ffsll((unsigned long long)__ballot(ck2 == M)) - 1;
+            const int idw = __builtin_amdgcn_readlane(ci2, wl);
+            if (lane == wl) ck2 = 0u;
+            if (lane == j) { sel_k = M; sel_i = idw; }
+        }
+        const float sel_v = lane < k ? key_value(sel_k) : 0.f;
+        const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sel_v), 0));
+        const float ex = lane < k ? expf(sel_v - top) : 0.f;
+        const float sum = wave_sum_f(ex);
+        wj = ex / sum;
+        if (lane < k) { a.sb.ids[lane] = sel_i; a.sb.w[lane] = wj; }
+
+        // 2. dedup: the k ids of one token are distinct; a pair's unique index is the number
+        //    of routed ids below its own
+        for (int j2 = 0; j2 < k; ++j2)
+            pos += (uint32_t)__builtin_amdgcn_readlane(sel_i, j2) < (uint32_t)sel_i ? 1 : 0;
+        if (lane >= k) pos = lane;
+        u = __builtin_amdgcn_ds_permute(pos * 4, sel_i);
+        pr = __builtin_amdgcn_ds_permute(pos * 4, lane);
+        valid = lane < k;
+
+        // 3. residency of the unique experts; 4. classify, q = min(m, floor(m*BP/BH), K, C - h)
+        sl = valid ? s_res[u] : -1;
+        if (valid) atomicOr(&s_bits[u >> 5], 1u << (u & 31));
+        miss = valid && sl < 0;
+        const uint64_t bm = __ballot(miss);
+        m = __popcll(bm);
+        h = k - m;
+        midx = __popcll(bm & lt);
+        // min(m, floor(m*BP/BH)) for m <= 16 without a division: the number of i in 1..m
+        // with i*BH <= m*BP
+        const bool qi = bh != 0u && lane >= 1 && lane <= m && (uint64_t)lane * bh <= (uint64_t)m * bp;
+        int qq = __popcll(__ballot(qi));
+        qq = min(qq, a.K);
+        qq = min(qq, C - h);
+        if (lane == 0) s_q = qq > 0 ? qq : 0;
+    }
+    __syncthreads();
+    const int q = s_q;
+
+    // 5. victims: q rounds of block-wide argmin over the unique LRU keys of the untouched slots
+    if (q > 0) {
+#pragma unroll
+        for (int p = 0; p < kSlotRegs; ++p) { // slots past C and slots hit in this step are not candidates
+            const uint32_t e = (uint32_t)(po[p] - l * E);
+            const bool past = tid + NT * p >= C;
+            if (past || (e < (uint32_t)E && ((s_bits[e >> 5] >> (e & 31)) & 1u))) pk[p] = ~0ull;
+        }
+        auto local_min = [&](uint64_t lo, uint64_t& mine, int& ms, int& mo) {
+            mine = ~0ull; ms = -1; mo = -1;
+#pragma unroll
+            for (int p = 0; p < kSlotRegs; ++p)
+                if (pk[p] >= lo && pk[p] < mine) { mine = pk[p]; ms = tid + NT * p; mo = po[p]; }
+        };
+        uint64_t mine;
+        int ms, mo;
+        local_min(0, mine, ms, mo);
+        for (int rr = 0; rr < q; ++rr) {
+            const uint64_t wm = wave_min_u64(mine);
+            if (lane == 0) s_wmin[rr & 1][wave] = wm;
+            __syncthreads();
+            uint64_t gm = ~0ull;
+#pragma unroll
+            for (int w2 = 0; w2 < kWaves; ++w2) gm = s_wmin[rr & 1][w2] < gm ? s_wmin[rr & 1][w2] : gm;
+            if (mine == gm) { // keys are unique: one owner
+                s_vslot[rr] = ms;
+                s_vocc[rr] = mo;
+                local_min(gm + 1, mine, ms, mo);
+            }
+        }
+        __syncthreads();
+    }
+    if (wave != 0) return;
+
+    if (lane < a.K) {
+        a.sb.victims[lane] = lane < q ? s_vslot[lane] : -1;
+        if (lane >= q) { a.sb.fills[lane] = -1; a.sb.evicted[lane] = -1; }
+    }
+    // 6. assign fills to victims (oldest first), host list, LRU update (lane r: unique expert r)
+    int cls = CLS_HIT, slot_r = sl, ev = 0;
+    if (valid) {
+        if (miss) {
+            if (midx < q) {
+                const int v = s_vslot[midx];
+                const int old = s_vocc[midx];
+                a.sb.evicted[midx] = old;
+                if (old >= 0) { a.st.resid[old] = -1; ev = 1; }
+                a.st.slot_key[v] = l * E + u;
+                a.st.resid[(int64_t)l * E + u] = v;
+                a.sb.fills[midx] = u;
+                cls = CLS_FILL;
+                slot_r = v;
+            } else {
+                const int hidx = midx - q;
+                a.sb.host_list[hidx] = u;
+                cls = CLS_HOST;
+                slot_r = -(1 + hidx);
+            }
+        }
+        if (cls != CLS_HOST) a.st.slot_lru[slot_r] = kLruTouched | ((clk + 1) << 16) | (uint64_t)lane;
+        a.sb.uniq[lane] = u;
+        a.sb.cls[lane] = cls;
+        a.sb.slot[lane] = slot_r;
+    }
+    const uint64_t bg = __ballot(valid && cls != CLS_HOST);
+    const int n_gpu = __popcll(bg), g = __popcll(bg & lt);
+    const int n_ev = __popcll(__ballot(ev != 0));
+
+    // 7. rewrite pair j -> the slot of its unique expert, or -(1 + host index); one pair per
+    //    unique expert: tok_pairs[r] = its pair, descriptor {slot, r, 1, pair}
+    const int rw = __builtin_amdgcn_ds_bpermute(pos * 4, slot_r);
+    if (lane < k) { a.sb.rewritten[lane] = rw; a.sb.pos[lane] = pos; }
+    if (valid) a.sb.tok_pairs[lane] = pr;
+    if (valid && cls != CLS_HOST) a.sb.gpu_desc[g] = make_int4(slot_r, lane, 1, pr);
+
+    // 8. counts, stats, clock; mailbox for the host branch
+    if (lane == 0) {
+        int32_t* c = a.sb.counts;
+        c[CNT_U] = k; c[CNT_H] = h; c[CNT_M] = m; c[CNT_Q] = q; c[CNT_HOST] = m - q; c[CNT_GPU] = n_gpu;
+        c[6] = 0; c[7] = 0;
+        *a.st.clock = clk + 1;
+    }
+    if (lane <= ST_EVICT) {
+        const unsigned long long d = lane == ST_STEPS ? 1ull : lane == ST_HITS ? (unsigned long long)h
+                                   : lane == ST_MISSES ? (unsigned long long)m : lane == ST_FILLS ? (unsigned long long)q
+                                   : lane == ST_HOST ? (unsigned long long)(m - q) : (unsigned long long)n_ev;
+        a.st.stats[(int64_t)l * ST_N + lane] = st_v + d;
+    }
+    if (a.host_branch && m - q > 0) {
+        // mailbox in pinned host memory: [counts 8][host_list n][rewritten n][w n][x bytes], n = k;
+        // the wavefront's stores are made visible system-wide before lane 0 rings the doorbell
+        const int n = k;
+        int32_t* mb = a.sb.mailbox;
+        if (lane == 0) {
+            mb[CNT_U] = k; mb[CNT_H] = h; mb[CNT_M] = m; mb[CNT_Q] = q; mb[CNT_HOST] = m - q; mb[CNT_GPU] = n_gpu;
+            mb[6] = 1; mb[7] = l;
+        }
+        if (valid && cls == CLS_HOST) mb[CNT_N + (-slot_r - 1)] = u;
+        if (lane < n) {
+            mb[CNT_N + n + lane] = rw;
+            reinterpret_cast<float*>(mb)[CNT_N + 2 * n + lane] = wj;
+        }
+        const uint4* xs = reinterpret_cast<const uint4*>(a.x);
+        uint4* xd = reinterpret_cast<uint4*>(mb + CNT_N + 3 * n + ((4 - (3 * n) % 4) % 4));
+        for (int i = lane; i < a.x_bytes / 16; i += 64) xd[i] = xs[i];
+        __threadfence_system();
+        if (lane == 0) {
+            *a.st.hseq = hs + 1;
+            __hip_atomic_store(a.doorbell, hs + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+}
+
 __global__ void set_bw_kernel(uint32_t* bw, uint32_t bp, uint32_t bh) {
     if (threadIdx.x == 0) { bw[0] = bp; bw[1] = bh; }
 }
@@ -645,7 +875,12 @@ void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float*
 }
 
 void launch_ctl(const CtlArgs& a, hipStream_t s) {
-    if (a.T * a.k <= 256) hipLaunchKernelGGL(ctl_kernel<256>, dim3(1), dim3(256), 0, s, a);
+    if (a.logits && a.T == 1 && a.E <= 256 && a.k <= 16 && a.C <= 5120) {
+        if (a.C <= 2048) hipLaunchKernelGGL(ctl1_kernel<8>, dim3(1), dim3(256), 0, s, a);
+        else if (a.C <= 3072) hipLaunchKernelGGL(ctl1_kernel<12>, dim3(1), dim3(256), 0, s, a);
+        else if (a.C <= 4096) hipLaunchKernelGGL(ctl1_kernel<16>, dim3(1), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(ctl1_kernel<20>, dim3(1), dim3(256), 0, s, a);
+    } else if (a.T * a.k <= 256) hipLaunchKernelGGL(ctl_kernel<256>, dim3(1), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(ctl_kernel<1024>, dim3(1), dim3(1024), 0, s, a);
 }
 

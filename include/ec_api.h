@@ -217,6 +217,15 @@ ec_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_
 ec_status expert_cache_step(ec_ctx* ctx, int32_t layer, const int32_t* ids, int32_t T,
                             ec_step_view* out, void* stream);
 
+/* The step buffers written by the most recent expert_cache_step,
+ * moe_decode_layer or moe_decode_block call on the context (the decisions of
+ * the fused routing path included), as device pointers: the same pointers
+ * expert_cache_step returns. Valid until the next step call; read them after
+ * that step's stream work has completed. Enqueues nothing, does not sync.
+ *   out : host struct receiving the pointers (non-NULL).
+ * EC_EINVAL for a NULL ctx or out. */
+ec_status ec_last_step(const ec_ctx* ctx, ec_step_view* out);
+
 /* One decode MoE layer ("Bandwidth-adaptive execution", decode):
  * route -> cache control -> fill of the q victims from the host pool ->
  * SwiGLU of the cache-side experts from HBM, and of the host-list experts

@@ -1,4 +1,6 @@
-"""expert_cache_step on the GPU vs the literal LRU simulator (oracle/lru_sim.py).
+"""expert_cache_step on the GPU vs the literal LRU simulator (oracle/lru_sim.py),
+and the same decisions taken inside moe_decode_layer with fused routing (read
+back through ec_last_step).
 
 Every step of every trace is compared bit-exactly: unique experts, counts
 (h, m, q, host), classes, slots, fills, victims, evicted keys, host list and
@@ -24,7 +26,10 @@ def _small(cfg):
 
 
 def run_trace(cfg, steps, p=None, T=None, C=None, K=None, bp=None, bh=None, rebuild=None, ids_override=None,
-              check_every=1):
+              check_every=1, fused=False):
+    """fused: each step is moe_decode_layer on the step's logits (routing inside the control
+    kernel, then fill and GEMVs on zero inputs) and its decisions are read with ec_last_step;
+    otherwise expert_cache_step on the oracle-routed ids."""
     import torch
     import expert_cached_decode_amd as EC
     from expert_cached_decode_amd.binding import memcpy_async
@@ -52,6 +57,12 @@ def run_trace(cfg, steps, p=None, T=None, C=None, K=None, bp=None, bh=None, rebu
             ids = ids_override(s, l) if ids_override else route_ids(logits[s, l], cfg.k)
             all_ids.append(ids)
     ids_dev.copy_(torch.from_numpy(np.stack(all_ids)))
+    if fused:
+        assert ids_override is None
+        lg_dev = torch.from_numpy(np.ascontiguousarray(logits.reshape(steps * cfg.L, T, cfg.E), np.float32)).cuda()
+        xz = torch.zeros((T, sc.H), dtype=torch.int16, device="cuda")
+        yo = torch.empty((T, sc.H), dtype=torch.int16, device="cuda")
+        views = EC.last_step(ctx)
     results = []
     i = 0
     for s in range(steps):
@@ -60,7 +71,11 @@ def run_trace(cfg, steps, p=None, T=None, C=None, K=None, bp=None, bh=None, rebu
             newC = ctx.rebuild(rebuild[s])
             sim.rebuild(newC)
         for l in range(cfg.L):
-            v = EC.expert_cache_step(ctx, l, ids_dev[i], T)
+            if fused:
+                EC.moe_decode_layer(ctx, l, xz, lg_dev[i], T, yo)
+                v = views
+            else:
+                v = EC.expert_cache_step(ctx, l, ids_dev[i], T)
             row = log[i]
             o = 0
             for ptr, cnt in ((v.counts, 8), (v.uniq, Umax), (v.cls, Umax), (v.slot, Umax), (v.fills, Kc),
@@ -149,6 +164,26 @@ def test_duplicate_ids_in_a_step():
     cfg = TINY.with_(L=2, E=16, k=3, slots=4, K=3, T=4)
     rng = np.random.default_rng(9)
     run_trace(cfg, 30, ids_override=lambda s, l: rng.integers(0, 5, size=(4, 3)).astype(np.int32))
+
+
+def test_fused_routing_one_token_traces():
+    # batch-1 steps with routing fused into the control kernel: every decision bit-exact
+    res = run_trace(TINY, TINY.steps, fused=True)  # BP:BH 500:1000: host list in use
+    assert sum(r["nhost"] for r in res) > 0 and sum(r["q"] for r in res) > 0
+    run_trace(QWEN_DECODE, 64, fused=True)
+    res = run_trace(DSV4_DECODE, 128, bp=300, bh=1000, fused=True)
+    assert sum(r["nhost"] for r in res) > 0
+    run_trace(TINY.with_(L=2), 40, C=0, fused=True)
+    run_trace(TINY.with_(L=2), 40, C=1, K=2, bp=1000, bh=1000, fused=True)
+    c5 = STRESS.with_(T=1, slots=budget_slots(43, 256, 4000))
+    run_trace(c5, 48, T=1, rebuild={16: 1500, 32: 4000}, fused=True)
+
+
+def test_fused_routing_general_forms():
+    # fused routing outside the one-token form: E > 256, k > 16, T > 1
+    run_trace(TINY.with_(L=2, E=512, k=4, slots=64, K=4), 20, fused=True)
+    run_trace(TINY.with_(L=2, E=64, k=20, slots=64, K=20), 20, fused=True)
+    run_trace(STRESS, 12, T=16, p=0.5, fused=True)
 
 
 def test_invalid_id_sets_device_error():
