@@ -8,8 +8,9 @@ control -> fill -> gate/up GEMV -> down GEMV + exact merge, per layer, captured
 in one hipGraph per token. Inputs (router logits and layer inputs of every
 step) are resident in HBM before the timed region.
 
-Also measured in the same run: the gate/up GEMV's HBM roofline (kernels
-bracketed by HIP events in an eager pass), prefill seconds per 8192-token chunk
+Also measured in the same run: the gate/up GEMV's HBM roofline (kernel
+durations from HIP event pairs each launch stamps from its own dispatch, in an
+eager pass), prefill seconds per 8192-token chunk
 with full-layer double buffering against the measured host-link bound, and the
 CPU oracle on a bounded sample (cpu_baseline). Prints one JSON line.
 
@@ -102,6 +103,12 @@ def main():
     ap.add_argument("--host-threads", type=int, default=0, help="host-branch worker threads (0 = library default)")
     ap.add_argument("--sweep-locality", action="store_true",
                     help="stress workload: tok/s and miss rate against routing overlap at batch 1 and 16")
+    ap.add_argument("--sweep-ps", default="0,0.3,0.6,0.9", help="locality sweep: overlaps p (comma list)")
+    ap.add_argument("--sweep-T", default="1,16", help="locality sweep: tokens per step (comma list)")
+    ap.add_argument("--sweep-steps", type=int, default=48, help="locality sweep: timed steps per point")
+    ap.add_argument("--sweep-warm", type=int, default=16, help="locality sweep: warm-up steps per point")
+    ap.add_argument("--rebuild-recovery", action="store_true",
+                    help="stress workload: batch-1 miss rate by window across cache_rebuild 40%% -> 15%% -> 40%%")
     ap.add_argument("--cold-start-gb", type=float, default=0.0,
                     help="time a cold start: write about this many GB of the bank as a bank file and read it "
                          "back into pinned memory with parallel direct I/O (0 = skip)")
@@ -208,7 +215,8 @@ def main():
     log("decode: %d steps in %.3f s (wall %.3f s): %.2f tok/s; miss rate %.3f, fills/step %.2f, host/step %.2f"
         % (K, ms_total / 1e3, t_wall, tok_s, st["misses"] / max(lookups, 1), st["fills"] / K, st["host"] / K))
 
-    # kernel timing pass (eager, event-bracketed kernels), continuing the same workload
+    # kernel timing pass (eager; each decode kernel stamps a HIP event pair from its own dispatch on
+    # the launch stream), continuing the same workload
     ctx.kernel_timing(True)
     for s in range(W + K, total_steps):
         token_layers(xs[s], logits[s], stream)
@@ -245,7 +253,7 @@ def main():
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gu_kernel") if args.workload == "qwen" else None,
                      "bytes_per_launch": int(gu_bytes), "us_per_launch": round(gu_us, 3),
-                     "launches": int(n_launch), "timing": "HIP events around each launch, eager pass"},
+                     "launches": int(n_launch), "timing": "HIP event pair stamped by each launch's own dispatch on its stream (hipExtLaunchKernelGGL), eager pass"},
         "down_kernel": {"achieved": round(dn_gbs, 1), "unit": "GB/s", "frac": round(dn_gbs / HBM_PEAK_GBS, 4),
                         "bytes_per_launch": int(dn_bytes), "us_per_launch": round(dn_us, 3),
                         "traffic": measured_traffic("down_kernel") if args.workload == "qwen" else None},
@@ -269,7 +277,11 @@ def main():
         result["cache_ctl"] = bench_cache_ctl(ctx, cfg)
         result["rebuild"] = bench_rebuild(ctx, cfg)
         if args.sweep_locality:
-            result["locality_sweep"] = bench_locality_sweep(ctx, cfg)
+            result["locality_sweep"] = bench_locality_sweep(
+                ctx, cfg, ps=tuple(float(v) for v in args.sweep_ps.split(",")),
+                Ts=tuple(int(v) for v in args.sweep_T.split(",")), warm=args.sweep_warm, steps=args.sweep_steps)
+        if args.rebuild_recovery:
+            result["rebuild_recovery"] = bench_rebuild_recovery(ctx, cfg)
     if prefill_T:
         result["prefill"] = bench_prefill(ctx, cfg, QWEN_PREFILL, args.prefill_chunks)
     if not args.no_cpu:
@@ -348,7 +360,60 @@ def bench_cold_start(cfg, gb):
     return out
 
 
-def bench_locality_sweep(ctx, cfg, ps=(0.0, 0.3, 0.6, 0.9), warm=16, steps=48):
+def bench_rebuild_recovery(ctx, cfg, steps=768, window=32, at=(256, 512), budgets=(4000, 1500, 4000)):
+    """Elastic budget at batch 1: a cold cache of 40% of all experts, cache_rebuild to 15% at step
+    256 and back to 40% at step 512 (each cold, at a safe point between tokens); miss rate per
+    window of steps, tok/s per phase and each rebuild's latency. One graph per phase (a rebuild
+    changes the epoch, so the graph is captured again)."""
+    import torch
+    import gen
+    import expert_cached_decode_amd as EC
+    L, E, H = cfg.L, cfg.E, cfg.H
+    c = cfg.with_(T=1)
+    lg = torch.from_numpy(gen.decode_logits(c, steps=steps)).cuda()
+    xs = torch.from_numpy(np.stack([np.stack([gen.decode_x(c, s, l) for l in range(L)])
+                                    for s in range(4)]).view(np.int16)).cuda()
+    x_stage = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    lg_stage = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
+    outs = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    bounds = [0] + list(at) + [steps]
+    windows, phases = [], []
+    for ph in range(len(bounds) - 1):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        C = ctx.rebuild(budgets[ph])
+        torch.cuda.synchronize()
+        rb_ms = (time.perf_counter() - t0) * 1e3
+        graph, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        with torch.cuda.graph(graph, stream=side):
+            for l in range(L):
+                EC.moe_decode_layer(ctx, l, x_stage[l], lg_stage[l], 1, outs[l], side)
+        torch.cuda.synchronize()
+        ctx.stats(reset=True)
+        busy = 0.0
+        for w0 in range(bounds[ph], bounds[ph + 1], window):
+            w1 = min(w0 + window, bounds[ph + 1])
+            t0 = time.perf_counter()
+            for i in range(w0, w1):
+                x_stage.copy_(xs[i % 4]); lg_stage.copy_(lg[i])
+                graph.replay()
+            torch.cuda.synchronize()
+            busy += time.perf_counter() - t0
+            st = ctx.stats(reset=True)
+            windows.append({"steps": [w0, w1], "slots": C,
+                            "miss_rate": round(st["misses"] / max(st["hits"] + st["misses"], 1), 4)})
+        n = bounds[ph + 1] - bounds[ph]
+        phases.append({"budget_bp": budgets[ph], "slots": C, "rebuild_ms": round(rb_ms, 3),
+                       "tok_s": round(n / busy, 2), "steps": n})
+        log("rebuild recovery: %d slots from step %d (rebuild %.2f ms): %.2f tok/s; miss rate by window %s"
+            % (C, bounds[ph], rb_ms, n / busy,
+               " ".join("%.3f" % w["miss_rate"] for w in windows if bounds[ph] <= w["steps"][0] < bounds[ph + 1])))
+        del graph
+    ctx.rebuild(budgets[0])
+    return {"window": window, "phases": phases, "windows": windows}
+
+
+def bench_locality_sweep(ctx, cfg, ps=(0.0, 0.3, 0.6, 0.9), Ts=(1, 16), warm=16, steps=48):
     """tok/s and miss rate against step-to-step routing overlap p at batch 1 and 16 (cold cache at
     each point through cache_rebuild to the configured slot count, one graph per point)."""
     import torch
@@ -359,7 +424,8 @@ def bench_locality_sweep(ctx, cfg, ps=(0.0, 0.3, 0.6, 0.9), warm=16, steps=48):
     if budget * L * E // 10000 > cfg.slots:
         budget -= 1
     out = []
-    for T in (1, cfg.T):
+    for T in Ts:
+        assert 1 <= T <= cfg.T
         x_stage = torch.empty((L, T, H), dtype=torch.int16, device="cuda")
         lg_stage = torch.empty((L, T, E), dtype=torch.float32, device="cuda")
         outs = torch.empty((L, T, H), dtype=torch.int16, device="cuda")

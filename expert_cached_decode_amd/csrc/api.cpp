@@ -533,10 +533,8 @@ static ec_status decode_layer(ec_ctx* x, int32_t layer, const void* xin, const f
     a.host_branch = x->host_branch ? 1 : 0;
     a.sb.mailbox = x->mb_dev;
     a.doorbell = x->doorbell_dev;
-    hipEvent_t* tm = timer_next(x, 0);
-    if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
-    launch_ctl(a, s);
-    if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
+    // with kernel timing on, each kernel stamps its timer pair from its own dispatch
+    launch_ctl(a, s, timer_next(x, 0));
     HIPCHK(x, hipGetLastError());
     DecodeArgs d{};
     d.pool = x->host_pool_dev; d.slots = x->slot_pool; d.counts = x->sb.counts; d.fills = x->sb.fills;
@@ -548,21 +546,10 @@ static ec_status decode_layer(ec_ctx* x, int32_t layer, const void* xin, const f
     d.host_pairs = x->host_branch ? 1 : 0;
     d.host_done = x->doorbell_dev + kDone; d.hseq = x->st.hseq; d.hseen = x->st.hseen; d.err = x->st.err;
     d.residual = residual;
-    if (x->C > 0 && !x->host_only) {
-        tm = timer_next(x, 1);
-        if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
-        launch_fill(d, x->K, s);
-        if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
-    }
-    tm = timer_next(x, 2);
-    if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
-    launch_gu(d, s);
-    if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
+    if (x->C > 0 && !x->host_only) launch_fill(d, x->K, s, timer_next(x, 1));
+    launch_gu(d, s, timer_next(x, 2));
     HIPCHK(x, hipGetLastError());
-    tm = timer_next(x, 3);
-    if (tm) HIPCHK(x, hipEventRecord(tm[0], s));
-    launch_down(d, s);
-    if (tm) HIPCHK(x, hipEventRecord(tm[1], s));
+    launch_down(d, s, timer_next(x, 3));
     HIPCHK(x, hipGetLastError());
     return EC_OK;
 }

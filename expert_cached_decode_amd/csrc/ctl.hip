@@ -874,14 +874,15 @@ void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float*
     hipLaunchKernelGGL(route_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, w);
 }
 
-void launch_ctl(const CtlArgs& a, hipStream_t s) {
+void launch_ctl(const CtlArgs& a, hipStream_t s, const hipEvent_t* ev) {
+    const LaunchEvents le(ev);
     if (a.logits && a.T == 1 && a.E <= 256 && a.k <= 16 && a.C <= 5120) {
-        if (a.C <= 2048) hipLaunchKernelGGL(ctl1_kernel<8>, dim3(1), dim3(256), 0, s, a);
-        else if (a.C <= 3072) hipLaunchKernelGGL(ctl1_kernel<12>, dim3(1), dim3(256), 0, s, a);
-        else if (a.C <= 4096) hipLaunchKernelGGL(ctl1_kernel<16>, dim3(1), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(ctl1_kernel<20>, dim3(1), dim3(256), 0, s, a);
-    } else if (a.T * a.k <= 256) hipLaunchKernelGGL(ctl_kernel<256>, dim3(1), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(ctl_kernel<1024>, dim3(1), dim3(1024), 0, s, a);
+        if (a.C <= 2048) EC_LAUNCH(ctl1_kernel<8>, dim3(1), dim3(256), 0, s, a);
+        else if (a.C <= 3072) EC_LAUNCH(ctl1_kernel<12>, dim3(1), dim3(256), 0, s, a);
+        else if (a.C <= 4096) EC_LAUNCH(ctl1_kernel<16>, dim3(1), dim3(256), 0, s, a);
+        else EC_LAUNCH(ctl1_kernel<20>, dim3(1), dim3(256), 0, s, a);
+    } else if (a.T * a.k <= 256) EC_LAUNCH(ctl_kernel<256>, dim3(1), dim3(256), 0, s, a);
+    else EC_LAUNCH(ctl_kernel<1024>, dim3(1), dim3(1024), 0, s, a);
 }
 
 void launch_set_bw(uint32_t* bw, uint32_t bp, uint32_t bh, hipStream_t s) {

@@ -558,9 +558,10 @@ void launch_gate(const void* wr, const void* x, bool f32, int T, int E, int H, f
     else gate_nch<false>(reinterpret_cast<const uint8_t*>(wr), x, T, E, H, logits, s);
 }
 
-void launch_fill(const DecodeArgs& a, int K, hipStream_t s) {
+void launch_fill(const DecodeArgs& a, int K, hipStream_t s, const hipEvent_t* ev) {
+    const LaunchEvents le(ev);
     const int chunks = (int)((a.expert_bytes + kFillChunk - 1) / kFillChunk);
-    hipLaunchKernelGGL(fill_kernel, dim3(K * chunks), dim3(256), 0, s, a, chunks);
+    EC_LAUNCH(fill_kernel, dim3(K * chunks), dim3(256), 0, s, a, chunks);
 }
 
 
@@ -570,11 +571,11 @@ static void gu_go(const DecodeArgs& a, bool full, hipStream_t s) {
     const int chunks = a.I / (kGuWaves * RW);
     const dim3 grid(a.U_max * chunks), blk(256);
     if (full) {
-        if (a.T == 1) hipLaunchKernelGGL((gu_kernel<WDT, NCH, RW, true, true>), grid, blk, 0, s, a, chunks);
-        else hipLaunchKernelGGL((gu_kernel<WDT, NCH, RW, false, true>), grid, blk, 0, s, a, chunks);
+        if (a.T == 1) EC_LAUNCH((gu_kernel<WDT, NCH, RW, true, true>), grid, blk, 0, s, a, chunks);
+        else EC_LAUNCH((gu_kernel<WDT, NCH, RW, false, true>), grid, blk, 0, s, a, chunks);
     } else {
-        if (a.T == 1) hipLaunchKernelGGL((gu_kernel<WDT, NCH, RW, true, false>), grid, blk, 0, s, a, chunks);
-        else hipLaunchKernelGGL((gu_kernel<WDT, NCH, RW, false, false>), grid, blk, 0, s, a, chunks);
+        if (a.T == 1) EC_LAUNCH((gu_kernel<WDT, NCH, RW, true, false>), grid, blk, 0, s, a, chunks);
+        else EC_LAUNCH((gu_kernel<WDT, NCH, RW, false, false>), grid, blk, 0, s, a, chunks);
     }
 }
 
@@ -591,7 +592,8 @@ static void gu_nch(const DecodeArgs& a, hipStream_t s) {
 }
 
 // I is a multiple of 64, so I / (4 RW) blocks cover every row exactly.
-void launch_gu(const DecodeArgs& a, hipStream_t s) {
+void launch_gu(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev) {
+    const LaunchEvents le(ev);
     if (a.wdtype == EC_DT_F32) gu_nch<EC_DT_F32, 1>(a, s);
     else if (a.wdtype == EC_DT_BF16) gu_nch<EC_DT_BF16, 1>(a, s);
     else gu_nch<EC_DT_MXFP4, 2>(a, s);
@@ -601,7 +603,7 @@ template <int WDT, int NCH, int R, int G, bool STAGE>
 static void down_go2(const DecodeArgs& a, bool full, hipStream_t s) {
     const dim3 blk(256), grid(a.H / (4 * R), a.T);
     const size_t lds = STAGE ? (size_t)G * a.I * (WDT == EC_DT_F32 ? 4 : 2) : 0;
-#define EC_D1(HOST, FULL) hipLaunchKernelGGL((down_kernel<WDT, NCH, R, G, HOST, FULL, STAGE>), grid, blk, lds, s, a)
+#define EC_D1(HOST, FULL) EC_LAUNCH((down_kernel<WDT, NCH, R, G, HOST, FULL, STAGE>), grid, blk, lds, s, a)
     if constexpr (WDT != EC_DT_F32) { // f32 (small test shapes) only takes the guarded form
         if (full) {
             if (a.host_pairs) EC_D1(true, true); else EC_D1(false, true);
@@ -647,7 +649,8 @@ static void down_nch(const DecodeArgs& a, hipStream_t s) {
 
 // H is a multiple of 64, so H / (4 R) blocks cover every row exactly. MXFP4 rows
 // are short in bytes, so more of them share one staging of the activations.
-void launch_down(const DecodeArgs& a, hipStream_t s) {
+void launch_down(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev) {
+    const LaunchEvents le(ev);
     if (a.wdtype == EC_DT_F32) down_nch<EC_DT_F32, 1>(a, s);
     else if (a.wdtype == EC_DT_BF16) down_nch<EC_DT_BF16, 2>(a, s);
     else down_nch<EC_DT_MXFP4, 2>(a, s);

@@ -1,6 +1,7 @@
 // Internal definitions shared by the HIP kernels and the host runtime of
 // libexpert_cached_decode.so (never exported).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,6 +21,23 @@ struct Carve {
         return p;
     }
 };
+
+// Kernel timing (measurement only): a launcher given an event pair sets it for the one kernel it
+// launches, which then stamps the pair from its own dispatch (start and end of the kernel itself,
+// no marker commands around it); without a pair the launch is the plain one.
+inline thread_local const hipEvent_t* t_launch_ev = nullptr;
+struct LaunchEvents {
+    explicit LaunchEvents(const hipEvent_t* ev) { t_launch_ev = ev; }
+    ~LaunchEvents() { t_launch_ev = nullptr; }
+};
+#define EC_LAUNCH(KER, GRID, BLK, SH, S, ...)                                                          \
+    do {                                                                                                \
+        if (::ec::t_launch_ev)                                                                          \
+            hipExtLaunchKernelGGL(KER, GRID, BLK, SH, S, ::ec::t_launch_ev[0], ::ec::t_launch_ev[1], 0u,  \
+                                  __VA_ARGS__);                                                         \
+        else                                                                                            \
+            hipLaunchKernelGGL(KER, GRID, BLK, SH, S, __VA_ARGS__);                                     \
+    } while (0)
 
 constexpr int kMaxPairs = 1024;   // T_max * k
 constexpr int kMaxExperts = 4096; // E
@@ -83,7 +101,7 @@ struct CtlArgs {
 
 // Launchers (defined in the .hip files).
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
-void launch_ctl(const CtlArgs& a, hipStream_t s);
+void launch_ctl(const CtlArgs& a, hipStream_t s, const hipEvent_t* ev = nullptr);
 void launch_set_bw(uint32_t* bw, uint32_t bp, uint32_t bh, hipStream_t s);
 void launch_reset_cache(DevState st, int L, int E, int C, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
@@ -111,10 +129,10 @@ struct DecodeArgs {
     int32_t* err;              // device error flags
     int32_t residual;          // 1: out = x + merged output (chained MoE block)
 };
-void launch_fill(const DecodeArgs& a, int K, hipStream_t s);
+void launch_fill(const DecodeArgs& a, int K, hipStream_t s, const hipEvent_t* ev = nullptr);
 void launch_link_probe(const uint8_t* src_dev, uint64_t bytes, uint32_t* sink, hipStream_t s);
 void launch_gate(const void* wr, const void* x, bool f32, int T, int E, int H, float* logits, hipStream_t s);
-void launch_gu(const DecodeArgs& a, hipStream_t s);
-void launch_down(const DecodeArgs& a, hipStream_t s);
+void launch_gu(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev = nullptr);
+void launch_down(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev = nullptr);
 
 } // namespace ec

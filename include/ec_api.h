@@ -325,11 +325,12 @@ ec_status ec_get_stats(ec_ctx* ctx, ec_stats* out, int32_t reset);
 ec_status ec_debug_state(ec_ctx* ctx, int32_t* resid, int32_t* slot_key, uint64_t* slot_lru,
                          uint64_t* clock);
 
-/* Kernel timing (measurement support). While on, moe_decode_layer brackets
- * each of its kernels with HIP events recorded on the caller's stream (so a
- * step is then not capturable). Switching on allocates the events; off frees
- * them. Kinds: 0 cache control (route + control), 1 fill, 2 gate/up GEMV,
- * 3 down GEMV + exact merge. */
+/* Kernel timing (measurement support). While on, each kernel moe_decode_layer
+ * launches stamps a HIP event pair from its own dispatch on the caller's
+ * stream (start and end of the kernel itself; the step is then not
+ * capturable). Switching on allocates the events; off frees them. Kinds:
+ * 0 cache control (route + control), 1 fill, 2 gate/up GEMV, 3 down GEMV +
+ * exact merge. */
 ec_status ec_kernel_timing(ec_ctx* ctx, int32_t on);
 
 /* Sum of event-measured durations (ms) and number of launches of one kernel

@@ -177,6 +177,10 @@ def test_fused_routing_one_token_traces():
     run_trace(TINY.with_(L=2), 40, C=1, K=2, bp=1000, bh=1000, fused=True)
     c5 = STRESS.with_(T=1, slots=budget_slots(43, 256, 4000))
     run_trace(c5, 48, T=1, rebuild={16: 1500, 32: 4000}, fused=True)
+    # the form's limits: k = 16 (64 candidates in the second routing stage), k = 1 with a ragged
+    # E = 200 (the last wavefront holds 8 logits), C just above one register row per thread
+    run_trace(TINY.with_(L=3, E=256, k=16, slots=300, K=16, p=0.4), 24, fused=True)
+    run_trace(TINY.with_(L=3, E=200, k=1, slots=257, K=1, p=0.3), 40, fused=True)
 
 
 def test_fused_routing_general_forms():
