@@ -103,6 +103,7 @@ def main():
     ap.add_argument("--host-threads", type=int, default=0, help="host-branch worker threads (0 = library default)")
     ap.add_argument("--sweep-locality", action="store_true",
                     help="stress workload: tok/s and miss rate against routing overlap at batch 1 and 16")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the HBM copy and bf16 GEMM peak measurements")
     ap.add_argument("--sweep-ps", default="0,0.3,0.6,0.9", help="locality sweep: overlaps p (comma list)")
     ap.add_argument("--sweep-T", default="1,16", help="locality sweep: tokens per step (comma list)")
     ap.add_argument("--sweep-steps", type=int, default=48, help="locality sweep: timed steps per point")
@@ -267,7 +268,12 @@ def main():
         "bandwidth_mbps": {"bp_measured": bp_meas, "bh_measured": bh_meas, "bp_used": bp_used, "bh_used": bh_used},
         "cache": {"miss_rate": round(st["misses"] / max(lookups, 1), 4), "fills_per_step": round(st["fills"] / K, 3),
                   "host_per_step": round(st["host"] / K, 3), "fill_link_GBs": round(fill_gbs, 2)},
+        "token_bound": token_bound(cfg, st, K, bp_meas, bh_meas, tok_s),
     }
+    log("per-token bound (HBM at 8 TB/s + larger of link at the measured BP and host at the measured BH): "
+        "%.3f ms per step, %.2f tok/s; achieved %.1f%%" % (result["token_bound"]["ms_per_step"],
+                                                           result["token_bound"]["tok_s"],
+                                                           100 * result["token_bound"]["frac"]))
     if args.bpbh != "calibrate" and args.measured_split_steps > 0:
         result["measured_split"] = bench_measured_split(ctx, cfg, token_layers, xs, logits, x_stage, lg_stage,
                                                         total_steps, args.measured_split_steps)
@@ -282,12 +288,71 @@ def main():
                 Ts=tuple(int(v) for v in args.sweep_T.split(",")), warm=args.sweep_warm, steps=args.sweep_steps)
         if args.rebuild_recovery:
             result["rebuild_recovery"] = bench_rebuild_recovery(ctx, cfg)
+    if not args.no_peaks:
+        result["peaks"] = bench_peaks()
     if prefill_T:
         result["prefill"] = bench_prefill(ctx, cfg, QWEN_PREFILL, args.prefill_chunks)
     if not args.no_cpu:
         result["cpu_baseline"] = bench_cpu(cfg, logits.cpu().numpy(), P, period)
     ctx.close()
     print(json.dumps(result), flush=True)
+
+
+def bench_peaks(copy_bytes=1 << 30, reps=8, n=8192):
+    """Measured device peaks next to the spec figures (reference points for the rooflines, timed
+    with library kernels): an HBM device-to-device copy over 4 rotating 1 GiB buffer pairs (8 GiB
+    of distinct memory, far above the 256 MB MALL), counted as read + write bytes; and a bf16
+    n x n x n GEMM through torch.matmul (hipBLASLt)."""
+    import torch
+    srcs = [torch.empty(copy_bytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    dsts = [torch.empty(copy_bytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    for i in range(4):
+        dsts[i].copy_(srcs[i])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for r in range(reps):
+        dsts[r % 4].copy_(srcs[r % 4])
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * copy_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del srcs, dsts
+    a = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        c = torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    out = {"hbm_copy_GBs": round(copy_gbs, 1), "hbm_spec_GBs": HBM_PEAK_GBS,
+           "bf16_gemm_TFLOPs": round(tflops, 1), "bf16_spec_TFLOPs": 2500.0,
+           "method": "copy: read + write bytes over 4 x 1 GiB buffer pairs; gemm: torch.matmul %d^3 bf16" % n}
+    log("peaks: HBM copy %.0f GB/s (spec %.0f); bf16 GEMM %.0f TFLOP/s (spec 2500)"
+        % (copy_gbs, HBM_PEAK_GBS, tflops))
+    return out
+
+
+def token_bound(cfg, st, steps, bp_mbps, bh_mbps, tok_s):
+    """Per-token bound of the decode: per layer step, the cache-side experts streamed from HBM at
+    8 TB/s plus the larger of the fills over the host link (measured BP) and the host-list experts
+    on the host branch (measured BH). The larger-of is taken over the run's totals, which is exact
+    when one of the two terms is zero throughout (every miss filled, or none) and otherwise a lower
+    bound of the per-layer sum."""
+    se = cfg.expert_bytes
+    hbm = (st["hits"] + st["fills"]) * se / (HBM_PEAK_GBS * 1e9) / steps
+    link = st["fills"] * se / (bp_mbps * 1e6) / steps if bp_mbps > 0 else 0.0
+    host = st["host"] * se / (bh_mbps * 1e6) / steps if bh_mbps > 0 else 0.0
+    ms = 1e3 * (hbm + max(link, host))
+    return {"ms_per_step": round(ms, 4), "tok_s": round(1e3 * cfg.T / ms, 2) if ms > 0 else None,
+            "frac": round(tok_s / (1e3 * cfg.T / ms), 4) if ms > 0 else None,
+            "terms_ms": {"hbm": round(1e3 * hbm, 4), "link": round(1e3 * link, 4), "host": round(1e3 * host, 4)},
+            "link_GBs": round(bp_mbps / 1e3, 2), "host_GBs": round(bh_mbps / 1e3, 2), "hbm_GBs": HBM_PEAK_GBS}
 
 
 def bench_measured_split(ctx, cfg, token_layers, xs, logits, x_stage, lg_stage, n_inputs, steps):
@@ -319,8 +384,9 @@ def bench_measured_split(ctx, cfg, token_layers, xs, logits, x_stage, lg_stage, 
     out = {"bp_mbps": bp, "bh_mbps": bh, "steps": steps, "tok_s": round(steps * cfg.T / dt, 3),
            "miss_rate": round(st["misses"] / max(st["hits"] + st["misses"], 1), 4),
            "fills_per_step": round(st["fills"] / steps, 3), "host_per_step": round(st["host"] / steps, 3)}
-    log("measured split BP:BH %d:%d: %.2f tok/s, fills/step %.2f, host/step %.2f"
-        % (bp, bh, out["tok_s"], out["fills_per_step"], out["host_per_step"]))
+    out["token_bound"] = token_bound(cfg, st, steps, bp, bh, out["tok_s"])
+    log("measured split BP:BH %d:%d: %.2f tok/s, fills/step %.2f, host/step %.2f; per-token bound %.2f tok/s"
+        % (bp, bh, out["tok_s"], out["fills_per_step"], out["host_per_step"], out["token_bound"]["tok_s"]))
     return out
 
 

@@ -84,3 +84,10 @@ def test_route_argument_checks_enqueue_nothing():
 def test_calibration_rejects_a_null_context():
     lib = E.lib()
     assert lib.ec_calibrate_bandwidth(None, 8, 1, None, None) == -1
+
+
+def test_last_step_rejects_null_arguments():
+    lib = E.lib()
+    v = B.ec_step_view()
+    assert lib.ec_last_step(None, ctypes.byref(v)) == -1
+    assert lib.ec_last_step(None, None) == -1
