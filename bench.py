@@ -62,7 +62,8 @@ def workload(args):
     elif args.workload == "dsv4":
         cfg = DSV4_DECODE.with_(bp=1000, bh=1000)
         text = ("DeepSeek-V4-Flash-shaped MoE decode: 43 layers, 256 experts, top-6, hidden 4096, expert "
-                "intermediate 2048, MXFP4 experts (147.2 GB pinned bank), shared LRU cache of 2752 slots (25%)")
+                "intermediate 2048, MXFP4 experts (147.2 GB bank, held as 16 distinct pinned layers of 3.42 GB), "
+                "shared LRU cache of 2752 slots (25%)")
     else:
         cfg = STRESS.with_(T=args.tokens or 16)
         text = ("stress: DeepSeek-V4-Flash shapes (MXFP4), 4096-slot cache, K = 64")

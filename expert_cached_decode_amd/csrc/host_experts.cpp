@@ -14,6 +14,7 @@
 #include <immintrin.h>
 
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <cstring>
@@ -157,8 +158,8 @@ struct HostPool {
     std::vector<std::thread> threads;
     std::mutex mu;
     std::condition_variable cv;
-    uint64_t generation = 0;
-    bool stop = false;
+    std::atomic<uint64_t> generation{0}; // bumped (under mu) for every job
+    std::atomic<bool> stop{false};
     const HostJob* job = nullptr;
     // phase bookkeeping
     std::vector<int> task_expert, task_r0;   // phase-1 and phase-2 task tables
@@ -214,15 +215,27 @@ struct HostPool {
         }
     }
 
+    // After a job a worker spins for kSpin on the generation counter before it sleeps on the
+    // condition variable: during decode the next layer's job arrives well within that, so the
+    // workers start it without a wake-up; an idle context still sleeps.
+    static constexpr std::chrono::microseconds kSpin{2000};
     void loop() {
         uint64_t seen = 0;
         for (;;) {
-            {
-                std::unique_lock<std::mutex> lk(mu);
-                cv.wait(lk, [&] { return stop || generation != seen; });
-                if (stop) return;
-                seen = generation;
+            const auto t0 = std::chrono::steady_clock::now();
+            bool woke = false;
+            for (uint32_t i = 0;; ++i) {
+                if (stop.load(std::memory_order_acquire)) return;
+                if (generation.load(std::memory_order_acquire) != seen) { woke = true; break; }
+                _mm_pause();
+                if ((i & 255) == 255 && std::chrono::steady_clock::now() - t0 > kSpin) break;
             }
+            if (!woke) {
+                std::unique_lock<std::mutex> lk(mu);
+                cv.wait(lk, [&] { return stop.load() || generation.load() != seen; });
+                if (stop.load()) return;
+            }
+            seen = generation.load(std::memory_order_acquire);
             work();
             arrived.fetch_add(1, std::memory_order_release);
         }
@@ -239,7 +252,7 @@ HostPool* host_pool_create(int threads) {
 void host_pool_destroy(HostPool* p) {
     {
         std::lock_guard<std::mutex> lk(p->mu);
-        p->stop = true;
+        p->stop.store(true, std::memory_order_release);
     }
     p->cv.notify_all();
     for (auto& t : p->threads) t.join();
@@ -274,7 +287,7 @@ void host_pool_run(HostPool* p, const HostJob& j) {
     p->next1 = 0; p->next2 = 0; p->done1 = 0; p->done2 = 0; p->arrived = 0;
     {
         std::lock_guard<std::mutex> lk(p->mu);
-        p->generation++;
+        p->generation.fetch_add(1, std::memory_order_release);
     }
     p->cv.notify_all();
     p->work();
