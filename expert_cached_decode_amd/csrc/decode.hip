@@ -296,22 +296,25 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
 // and ec_get_stats reports it), so no wave can spin forever.
 constexpr uint32_t kHostWaitPolls = 1u << 22;
 
-__device__ __noinline__ void wait_host_branch(const DecodeArgs& a) {
+// (out of line, the polling loop stays out of the GEMV's registers; its arguments are plain
+// pointers so that the kernel's argument block is not copied to private memory)
+__device__ __noinline__ void wait_host_branch(const uint32_t* hseq, const uint32_t* host_done, uint32_t* hseen,
+                                              int32_t* err) {
     if (threadIdx.x == 0) {
-        const uint32_t want = *a.hseq;
+        const uint32_t want = *hseq;
         const bool relay = blockIdx.x == 0 && blockIdx.y == 0;
-        const uint32_t* flag = relay ? a.host_done : a.hseen;
+        const uint32_t* flag = relay ? host_done : hseen;
         uint32_t it = 0;
         while (relay ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != want
                      : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
             if (++it > kHostWaitPolls) {
-                atomicOr(a.err, 2);
+                atomicOr(err, 2);
                 break;
             }
             __builtin_amdgcn_s_sleep(8);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-        if (relay) __hip_atomic_store(a.hseen, want, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (relay) __hip_atomic_store(hseen, want, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
 }
@@ -348,23 +351,56 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
     const uint64_t down_off = 2ull * I * row_bytes<WDT>(H) + (uint64_t)row0 * rbi;
     const uint64_t dsc_off = 3ull * I * row_bytes<WDT>(H) + 2ull * I * (H / 32) + (uint64_t)row0 * (I / 32);
     const uint4* actq = reinterpret_cast<const uint4*>(a.act);
+    // issued first: whether the step has host-side pairs (read again only in the epilogue)
+    const int nhost = HOST ? a.counts[CNT_HOST] : 0;
     {
         const int t = blockIdx.y; // one token per grid row: tokens run in parallel
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
+        int rw0 = 0;     // lane j < k: pair j's rewritten id and weight (first group's loads)
+        float w0 = 0.f;
+        constexpr int SQ = STAGE ? G : 1; // staged quads per thread held in registers (I * AB <= 4096)
+        uint32_t sqx[SQ], sqy[SQ], sqz[SQ], sqw[SQ];
         for (int j0 = 0; j0 < k; j0 += G) {
             const int ng = min(G, k - j0); // uniform
             // one vector load per index array (lane j: pair j0 + j), then broadcasts
             const int pl = t * k + min(j0 + lane, k - 1);
             const int rw_l = a.rewritten[pl];
             const float w_l = a.w[pl];
+            if (j0 == 0) { rw0 = rw_l; w0 = w_l; }
             int rw[G];
             float wt[G];
 #pragma unroll
             for (int jj = 0; jj < G; ++jj) {
                 rw[jj] = __builtin_amdgcn_readlane(rw_l, jj);
                 wt[jj] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), jj));
+            }
+            // the group's activations are issued before its weight rows: loads complete in order,
+            // so the staging (or the first pair's arithmetic) then waits for the activations and
+            // the weights already in flight, not for the whole weight stream
+            uint4 ar[STAGE ? 1 : G][NCH][QB];
+            const int nst = ng * IQ;
+            if constexpr (STAGE) {
+#pragma unroll
+                for (int u = 0; u < SQ; ++u) { // unconditional (index clamped): the quads stay in registers
+                    const int i = min(tid + 256 * u, nst - 1);
+                    const int jj = i / IQ, e = i - jj * IQ;
+                    const uint4 v = actq[(int64_t)(t * k + j0 + jj) * IQ + e];
+                    sqx[u] = v.x; sqy[u] = v.y; sqz[u] = v.z; sqw[u] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < G; ++jj) {
+                    if (jj >= ng) break;
+#pragma unroll
+                    for (int q = 0; q < NCH; ++q) {
+                        const int c = lane + 64 * q;
+                        if (FULL || c < n16)
+#pragma unroll
+                            for (int d = 0; d < QB; ++d) ar[jj][q][d] = actq[(int64_t)(t * k + j0 + jj) * IQ + c * QB + d];
+                    }
+                }
             }
             uint4 wd[G][R][NCH];
             uint32_t sd[G][R][NCH];
@@ -386,27 +422,23 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
                         }
                     }
             }
-            uint4 ar[STAGE ? 1 : G][NCH][QB];
             if constexpr (STAGE) {
                 __syncthreads(); // the previous group's reads are done
-                for (int i = tid; i < ng * IQ; i += 256) {
+#pragma unroll
+                for (int u = 0; u < SQ; ++u) {
+                    const int i = tid + 256 * u;
+                    if (i < nst) {
+                        const int e = i - (i / IQ) * IQ, jj = i / IQ;
+                        const int c = e / QB, d = e - c * QB;
+                        s_q[jj * IQ + c * QB + (d ^ (c % QB))] = make_uint4(sqx[u], sqy[u], sqz[u], sqw[u]);
+                    }
+                }
+                for (int i = tid + 256 * SQ; i < nst; i += 256) { // wider activation rows than registers hold
                     const int jj = i / IQ, e = i - jj * IQ;
                     const int c = e / QB, d = e - c * QB;
                     s_q[jj * IQ + c * QB + (d ^ (c % QB))] = actq[(int64_t)(t * k + j0 + jj) * IQ + e];
                 }
                 __syncthreads();
-            } else {
-#pragma unroll
-                for (int jj = 0; jj < G; ++jj) {
-                    if (jj >= ng) break;
-#pragma unroll
-                    for (int q = 0; q < NCH; ++q) {
-                        const int c = lane + 64 * q;
-                        if (FULL || c < n16)
-#pragma unroll
-                            for (int d = 0; d < QB; ++d) ar[jj][q][d] = actq[(int64_t)(t * k + j0 + jj) * IQ + c * QB + d];
-                    }
-                }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -443,11 +475,10 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r) hs[r] = 0.f;
         if (HOST) {
-            if (a.counts[CNT_HOST] > 0) wait_host_branch(a);
+            if (nhost > 0) wait_host_branch(a.hseq, a.host_done, a.hseen, a.err);
             // lane j < k carries pair j's host-side term (zero for cache-side pairs)
-            const int pj = t * k + min(lane, k - 1);
-            const bool hj = lane < k && a.rewritten[pj] < 0;
-            const float wj = a.w[pj];
+            const bool hj = lane < k && rw0 < 0;
+            const float wj = w0;
 #pragma unroll
             for (int r = 0; r < R; ++r) hs[r] = hj ? wj * a.y_host[((int64_t)t * H + row0 + r) * k + min(lane, k - 1)] : 0.f;
         }
@@ -622,16 +653,18 @@ static void down_go(const DecodeArgs& a, bool full, hipStream_t s) {
     down_go2<WDT, NCH, R, G, WDT == EC_DT_MXFP4>(a, full, s);
 }
 
-// Pairs per group: up to 8 (fewer for small top-k), G activation rows of LDS at
-// most 64 KiB, and at most 32 weight chunks in registers per lane (G * R * NCH).
+// Pairs per group: up to 8 (2, 4, 6 or 8: the token's top-k in one group where it
+// fits), G activation rows of LDS at most 64 KiB, and at most 32 weight chunks in
+// registers per lane (G * R * NCH).
 template <int WDT, int NCH, int R>
 static void down_g(const DecodeArgs& a, bool full, hipStream_t s) {
     const int ab = WDT == EC_DT_F32 ? 4 : 2;
-    int g = a.k <= 2 ? 2 : a.k <= 4 ? 4 : 8;
-    while (g > 2 && (g * a.I * ab > 65536 || g * R * NCH > 32)) g >>= 1;
+    const int want = a.k <= 2 ? 2 : a.k <= 4 ? 4 : a.k <= 6 ? 6 : 8; // 6: top-6 routing in one group
+    auto fits = [&](int g) { return g * a.I * ab <= 65536 && g * R * NCH <= 32; };
     static_assert(2 * R * NCH <= 32, "weight chunks per lane");
-    if (g == 8 && 8 * R * NCH <= 32) down_go<WDT, NCH, R, (8 * R * NCH <= 32 ? 8 : 2)>(a, full, s);
-    else if (g >= 4 && 4 * R * NCH <= 32) down_go<WDT, NCH, R, (4 * R * NCH <= 32 ? 4 : 2)>(a, full, s);
+    if (want == 8 && fits(8)) down_go<WDT, NCH, R, (8 * R * NCH <= 32 ? 8 : 2)>(a, full, s);
+    else if (want >= 6 && fits(6)) down_go<WDT, NCH, R, (6 * R * NCH <= 32 ? 6 : 2)>(a, full, s);
+    else if (want >= 4 && fits(4)) down_go<WDT, NCH, R, (4 * R * NCH <= 32 ? 4 : 2)>(a, full, s);
     else down_go<WDT, NCH, R, 2>(a, full, s);
 }
 
