@@ -212,6 +212,32 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
     const int row0 = (ch * kGuWaves + wave) * RW;
     const bool xbf16 = WDT != EC_DT_F32;
 
+    // x: f32 for f32 weights, else bf16 kept in packed pairs for the dot2 unit. With one token it
+    // is loaded before the weight rows (loads complete in order, so the arithmetic then waits for
+    // the weights in flight, not behind them); with more, each pair loads its token in turn (the
+    // early load measured slower there).
+    constexpr bool PK = WDT != EC_DT_F32;
+    float xv[NCH][PK ? 1 : EPC];
+    uint32_t xw[NCH][PK ? EPC / 2 : 1];
+    auto load_x = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int c = lane + 64 * j;
+            if (FULL || c < n16) {
+                if constexpr (PK) {
+                    const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)t * H + (int64_t)c * EPC);
+#pragma unroll
+                    for (int q = 0; q < EPC / 8; ++q) {
+                        const uint4 u = xp[q];
+                        xw[j][4 * q] = u.x; xw[j][4 * q + 1] = u.y; xw[j][4 * q + 2] = u.z; xw[j][4 * q + 3] = u.w;
+                    }
+                } else {
+                    load_vec<EPC>(a.x, (int64_t)t * H + (int64_t)c * EPC, xbf16, xv[j]);
+                }
+            }
+        }
+    };
+    if constexpr (T1) load_x(0);
     uint4 wg[RW][NCH], wu[RW][NCH];
     uint32_t sg[RW][NCH], su[RW][NCH];
 #pragma unroll
@@ -238,26 +264,7 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
     for (int pi = 0; pi < np; ++pi) {
         const int pair = (T1 || pi == 0) ? d.w : a.tok_pairs[d.y + pi];
         const int t = T1 ? 0 : pair / a.k;
-        // x: f32 for f32 weights, else bf16 kept in packed pairs for the dot2 unit
-        constexpr bool PK = WDT != EC_DT_F32;
-        float xv[NCH][PK ? 1 : EPC];
-        uint32_t xw[NCH][PK ? EPC / 2 : 1];
-#pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const int c = lane + 64 * j;
-            if (FULL || c < n16) {
-                if constexpr (PK) {
-                    const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)t * H + (int64_t)c * EPC);
-#pragma unroll
-                    for (int q = 0; q < EPC / 8; ++q) {
-                        const uint4 u = xp[q];
-                        xw[j][4 * q] = u.x; xw[j][4 * q + 1] = u.y; xw[j][4 * q + 2] = u.z; xw[j][4 * q + 3] = u.w;
-                    }
-                } else {
-                    load_vec<EPC>(a.x, (int64_t)t * H + (int64_t)c * EPC, xbf16, xv[j]);
-                }
-            }
-        }
+        if (!T1) load_x(t);
 #pragma unroll
         for (int rr = 0; rr < RW; ++rr) {
             float accg = 0.f, accu = 0.f;
