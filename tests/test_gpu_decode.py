@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import gen
-from gen.configs import DSV4_DECODE, QWEN_DECODE, STRESS, TINY
+from gen.configs import BF16, DSV4_DECODE, F32, MXFP4, QWEN_DECODE, STRESS, TINY
 from oracle.lru_sim import LRUSim
 from tests.harness import (empty_out, make_ctx, make_pool, oracle_layer, out_to_host, route_ids, row_rel_err,
                            x_to_device)
@@ -82,6 +82,25 @@ def test_qwen_shapes_two_layers():
     st = ctx.stats()
     ref = sim_counts(cfg, logits, 2, 1, 64, cfg.K, cfg.bp, cfg.bh)
     assert {k: st[k] for k in ref} == ref
+    ctx.close()
+
+
+@pytest.mark.parametrize("wd,k,T,H,I", [
+    (BF16, 1, 1, 512, 256), (BF16, 3, 1, 512, 256), (BF16, 5, 2, 512, 256), (BF16, 6, 1, 512, 256),
+    (BF16, 7, 3, 512, 256), (MXFP4, 3, 1, 512, 256), (MXFP4, 6, 4, 512, 256), (MXFP4, 7, 2, 512, 256),
+    (MXFP4, 5, 2, 1024, 2048), (F32, 6, 2, 256, 128)])
+def test_down_group_sizes(wd, k, T, H, I):
+    """The down GEMV's pair groups (2, 4, 6, 8) with full and partial last groups, one and several
+    tokens, guarded and full MXFP4 rows, with a host split: outputs against the oracle."""
+    cfg = TINY.with_(L=2, E=32, k=k, H=H, I=I, wdtype=wd, slots=24, K=4, T=T, bp=500, bh=1000, p=0.5)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool)
+    outs, logits = run_decode(cfg, ctx, 10, 2, T, lambda s, l: s % 3 == 1)
+    check_against_oracle(cfg, outs, 1e-5 if wd == F32 else 1e-2)
+    st = ctx.stats()
+    ref = sim_counts(cfg, logits, 2, T, 24, 4, 500, 1000)
+    assert {k_: st[k_] for k_ in ref} == ref
+    assert st["host"] > 0 and (st["fills"] > 0 or k * T < 2)  # one pair per step: floor(m / 2) = 0
     ctx.close()
 
 
