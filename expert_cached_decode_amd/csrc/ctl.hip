@@ -169,6 +169,70 @@ __global__ __launch_bounds__(256) void route_kernel(const float* logits, int T, 
               false);
 }
 
+// Butterfly maximum / minimum over the 16 lanes of a DPP row: quad swaps, then the half-row and
+// row mirrors; every lane of the row ends with the result.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+#define EC_ROW_MAX(CTRL) { const uint32_t o = __builtin_amdgcn_update_dpp(v, v, CTRL, 0xf, 0xf, false); v = o > v ? o : v; }
+    EC_ROW_MAX(0xB1) EC_ROW_MAX(0x4E) EC_ROW_MAX(0x141) EC_ROW_MAX(0x140)
+#undef EC_ROW_MAX
+    return v;
+}
+__device__ __forceinline__ int row_min_i32(int v) {
+#define EC_ROW_MIN(CTRL) { const int o = __builtin_amdgcn_update_dpp(v, v, CTRL, 0xf, 0xf, false); v = o < v ? o : v; }
+    EC_ROW_MIN(0xB1) EC_ROW_MIN(0x4E) EC_ROW_MIN(0x141) EC_ROW_MIN(0x140)
+#undef EC_ROW_MIN
+    return v;
+}
+
+// Top-k of four tokens at once per wavefront (E <= 256, k <= 16): DPP row r holds token t0 + r, its
+// lane l the logits 16 i + l (i < 16; lv, loaded by the caller). Each round takes the row maximum and
+// then the lowest id holding it (the smallest 16 i + l); lane j of the row records the j-th. The
+// weights are the softmax over the selected logits summed in wave_topk's order (row shifts, the
+// total at the row's last lane), so they are bit-identical to it.
+__device__ __forceinline__ void rows_topk(const float (&lv)[16], int T, int E, int k, int t0, int32_t* ids,
+                                          float* w, int32_t* lds_ids, float* lds_w) {
+    const int lane = lane_id(), l = lane & 15;
+    const int t = t0 + (lane >> 4);
+    const bool tv = t < T;
+    uint32_t key[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) key[i] = (tv && 16 * i + l < E) ? value_key(lv[i]) : 0u;
+    uint32_t sel_k = 0u;
+    int sel_i = 0;
+    for (int j = 0; j < k; ++j) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) b = key[i] > b ? key[i] : b;
+        const uint32_t M = row_max_u32(b);
+        int best = 1 << 20;
+#pragma unroll
+        for (int i = 15; i >= 0; --i) best = (M != 0u && key[i] == M) ? 16 * i + l : best;
+        const int e = row_min_i32(best);
+        const bool mine = e < (1 << 20) && (e & 15) == l;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) key[i] = (mine && i == (e >> 4)) ? 0u : key[i];
+        if (l == j) { sel_k = M; sel_i = e; }
+    }
+    const float sel_v = l < k ? key_value(sel_k) : 0.f;
+    const float top = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 48) * 4, __float_as_int(sel_v)));
+    float ex = l < k ? expf(sel_v - top) : 0.f;
+#define EC_DPP_ADDF(CTRL) ex += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ex), CTRL, 0xf, 0xf, false))
+    EC_DPP_ADDF(0x111);
+    EC_DPP_ADDF(0x112);
+    EC_DPP_ADDF(0x114);
+    EC_DPP_ADDF(0x118);
+#undef EC_DPP_ADDF
+    const float sum = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane & 48) | 15) * 4, __float_as_int(ex)));
+    const float ex0 = l < k ? expf(sel_v - top) : 0.f;
+    if (tv && l < k) {
+        const float wj = ex0 / sum;
+        ids[t * k + l] = sel_i;
+        w[t * k + l] = wj;
+        lds_ids[t * k + l] = sel_i;
+        lds_w[t * k + l] = wj;
+    }
+}
+
 // Top-k of one token's E <= 64 * (NT / 64) logits by the whole block: wavefront w takes the
 // top-k of logits 64w .. 64w + 63 (one per lane: k rounds of a DPP wave maximum and one ballot,
 // lowest lane = lowest id on ties), then wavefront 0 ranks the wavefronts' candidates by (logit
@@ -328,6 +392,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     __shared__ int32_t s_wtot[2 * kCtlWaves];
     __shared__ int32_t s_misc[4];
     __shared__ int32_t s_res[512];
+    __shared__ uint32_t s_emask[512]; // fused routing, T <= 32: bit t set when token t routes to expert e
     __shared__ uint32_t s_ck[64];
     __shared__ int32_t s_ci[64];
 
@@ -344,9 +409,29 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     //    (one token with E <= 64 per wavefront: each wavefront holds a 64-logit segment), then
     //    the layer's residency row (E <= 512; staged through LDS after the routing)
     const bool seg = a.logits && T == 1 && E <= 64 * kCtlWaves && kCtlWaves * k <= 64;
-    const bool pre = a.logits && !seg && E <= 512 && wave < T;
-    float rv[8] = {};
-    if (pre) load_row512(a.logits + (int64_t)wave * E, E, rv);
+    // several tokens with E <= 256, k <= 16: four per wavefront, one per DPP row (rows_topk);
+    // else one per wavefront from a row of up to 512 logits held in registers (wave_topk)
+    const bool rows = a.logits && !seg && T > 1 && E <= 256 && k <= 16;
+    const bool pre = a.logits && !seg && !rows && E <= 512 && wave < T;
+    // with fused routing a token's k ids are distinct, so a pair's rank among the earlier pairs of
+    // its expert is the number of earlier tokens routed to that expert (token masks in LDS)
+    const bool tmask = a.logits && T <= 32 && E <= 512;
+    // The first routing rows, as 16 unconditional loads per lane (index clamped; a valid dummy
+    // word when neither form applies): rows: logits 16 i + (lane & 15) of token 4 wave + lane / 16;
+    // pre: logits lane + 64 i (i < 8) of token wave.
+    float rl[16];
+    {
+        const int tr = rows ? min(4 * wave + (lane >> 4), T - 1) : wave;
+        const float* base = (rows || pre) ? a.logits + (int64_t)tr * E : reinterpret_cast<const float*>(a.st.clock);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = rows ? 16 * i + (lane & 15) : pre ? lane + 64 * (i & 7) : 0;
+            rl[i] = base[(rows || pre) ? (e < E ? e : E - 1) : 0];
+        }
+    }
+    float rv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rv[i] = rl[i];
     // One unconditional load per thread for the segment's logit or, without logits, for the
     // thread's routed id (n <= NT: the launch picks NT >= T * k); otherwise it reads a word that
     // is always valid. Unconditional loads keep the wait counts static, so no use of an early
@@ -380,6 +465,18 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     // 1. routing (fused) or routed ids from the caller
     if (seg) {
         block_topk1<NT>(segv, E, k, a.sb.ids, a.sb.w, s_ids, s_w, s_ck, s_ci);
+    } else if (rows) {
+        for (int t0 = 4 * wave; t0 < T; t0 += 4 * kCtlWaves) {
+            if (t0 != 4 * wave) { // later groups of four tokens (more than 4 per wavefront)
+                const int tr = min(t0 + (lane >> 4), T - 1);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int e = 16 * i + (lane & 15);
+                    rl[i] = a.logits[(int64_t)tr * E + (e < E ? e : E - 1)];
+                }
+            }
+            rows_topk(rl, T, E, k, t0, a.sb.ids, a.sb.w, s_ids, s_w);
+        }
     } else if (a.logits) {
         for (int t = wave; t < T; t += kCtlWaves)
             wave_topk(a.logits + (int64_t)t * E, E, k, a.sb.ids + t * k, a.sb.w + t * k, s_ids + t * k,
@@ -388,6 +485,8 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
         s_ids[tid] = (int32_t)in_v;
     }
     for (int wd = tid; wd < nwords; wd += kCtlThreads) s_bits[wd] = 0;
+    if (tmask)
+        for (int e = tid; e < E; e += kCtlThreads) s_emask[e] = 0u;
     if (tid == 0) s_misc[0] = 0;
     if (rrow) {
 #pragma unroll
@@ -409,7 +508,10 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     for (int i = tid; i < n; i += kCtlThreads) {
         int id = s_ids[i];
         if (id < 0 || id >= E) s_misc[0] = 1;
-        else atomicOr(&s_bits[id >> 5], 1u << (id & 31));
+        else {
+            atomicOr(&s_bits[id >> 5], 1u << (id & 31));
+            if (tmask) atomicOr(&s_emask[id], 1u << (i / k));
+        }
     }
     __syncthreads();
     if (s_misc[0]) { // invalid expert id: flag it, do nothing else
@@ -575,7 +677,11 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
         for (int i = tid; i < n; i += kCtlThreads) {
             const int pr = s_pos[i];
             int within = 0;
-            for (int i2 = 0; i2 < i; ++i2) within += (s_pos[i2] == pr);
+            if (tmask) {
+                within = __popc(s_emask[s_ids[i]] & ((1u << (i / k)) - 1u));
+            } else {
+                for (int i2 = 0; i2 < i; ++i2) within += (s_pos[i2] == pr);
+            }
             a.sb.tok_pairs[s_off[pr] + within] = i;
             if (within == 0) s_first[pr] = i;
         }

@@ -188,6 +188,11 @@ def test_fused_routing_general_forms():
     run_trace(TINY.with_(L=2, E=512, k=4, slots=64, K=4), 20, fused=True)
     run_trace(TINY.with_(L=2, E=64, k=20, slots=64, K=20), 20, fused=True)
     run_trace(STRESS, 12, T=16, p=0.5, fused=True)
+    # several tokens per wavefront (four per pass, one per DPP row): ragged T over three passes,
+    # k = 16 with E not a multiple of 16, and 1024 threads with T > 32 (no token masks)
+    run_trace(TINY.with_(L=2, E=256, k=4, slots=64, K=8, p=0.4), 12, T=37, fused=True)
+    run_trace(TINY.with_(L=2, E=200, k=16, slots=64, K=16, p=0.4), 12, T=5, fused=True)
+    run_trace(TINY.with_(L=2, E=256, k=8, slots=128, K=32, p=0.4), 8, T=40, fused=True)
 
 
 def test_invalid_id_sets_device_error():
