@@ -196,18 +196,22 @@ __global__ __launch_bounds__(256) void fill_kernel(DecodeArgs a, int chunks) {
 // registers, so one expert's weights are read once whatever its token count.
 // Grid: U_max x (I / (4 RW)); blocks past the step's cache-side count exit.
 // FULL: every lane owns NCH whole chunks (row bytes = 1024 NCH), no guards.
+// The leading scalar arguments are everything the descriptor and weight addresses need: they
+// are preloaded into SGPRs at dispatch (kernarg preloading), so the first loads do not wait
+// for a fetch of the argument block, whose remaining fields are needed only later.
 template <int WDT, int NCH, int RW, bool T1, bool FULL>
-__global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
+__global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const int4* gpu_desc, const uint8_t* slots,
+                                                 uint64_t expert_bytes, const void* xin, int H, int I, int chunks,
+                                                 DecodeArgs a) {
     constexpr int EPC = Fmt<WDT>::EPC;
     const int g = blockIdx.x / chunks, ch = blockIdx.x % chunks;
     // both loads are issued before the exit test (one round trip)
-    const int n_gpu = a.counts[CNT_GPU];
-    const int4 d = a.gpu_desc[g];
+    const int n_gpu = counts[CNT_GPU];
+    const int4 d = gpu_desc[g];
     if (g >= n_gpu || d.x < 0) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H, I = a.I;
     const int rb = row_bytes<WDT>(H), n16 = rb >> 4;
-    const uint8_t* base = a.slots + (uint64_t)d.x * a.expert_bytes;
+    const uint8_t* base = slots + (uint64_t)d.x * expert_bytes;
     const uint8_t* gsc = base + 3ull * I * rb; // MXFP4 scale rows (H/32 bytes each)
     const int row0 = (ch * kGuWaves + wave) * RW;
     const bool xbf16 = WDT != EC_DT_F32;
@@ -225,14 +229,14 @@ __global__ __launch_bounds__(256) void gu_kernel(DecodeArgs a, int chunks) {
             const int c = lane + 64 * j;
             if (FULL || c < n16) {
                 if constexpr (PK) {
-                    const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + (int64_t)t * H + (int64_t)c * EPC);
+                    const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(xin) + (int64_t)t * H + (int64_t)c * EPC);
 #pragma unroll
                     for (int q = 0; q < EPC / 8; ++q) {
                         const uint4 u = xp[q];
                         xw[j][4 * q] = u.x; xw[j][4 * q + 1] = u.y; xw[j][4 * q + 2] = u.z; xw[j][4 * q + 3] = u.w;
                     }
                 } else {
-                    load_vec<EPC>(a.x, (int64_t)t * H + (int64_t)c * EPC, xbf16, xv[j]);
+                    load_vec<EPC>(xin, (int64_t)t * H + (int64_t)c * EPC, xbf16, xv[j]);
                 }
             }
         }
@@ -608,13 +612,16 @@ template <int WDT, int NCH, int RW>
 static void gu_go(const DecodeArgs& a, bool full, hipStream_t s) {
     const int chunks = a.I / (kGuWaves * RW);
     const dim3 grid(a.U_max * chunks), blk(256);
+#define EC_GU(T1, FULL) EC_LAUNCH((gu_kernel<WDT, NCH, RW, T1, FULL>), grid, blk, 0, s, a.counts, a.gpu_desc, \
+                                   (const uint8_t*)a.slots, a.expert_bytes, a.x, a.H, a.I, chunks, a)
     if (full) {
-        if (a.T == 1) EC_LAUNCH((gu_kernel<WDT, NCH, RW, true, true>), grid, blk, 0, s, a, chunks);
-        else EC_LAUNCH((gu_kernel<WDT, NCH, RW, false, true>), grid, blk, 0, s, a, chunks);
+        if (a.T == 1) EC_GU(true, true);
+        else EC_GU(false, true);
     } else {
-        if (a.T == 1) EC_LAUNCH((gu_kernel<WDT, NCH, RW, true, false>), grid, blk, 0, s, a, chunks);
-        else EC_LAUNCH((gu_kernel<WDT, NCH, RW, false, false>), grid, blk, 0, s, a, chunks);
+        if (a.T == 1) EC_GU(true, false);
+        else EC_GU(false, false);
     }
+#undef EC_GU
 }
 
 template <int WDT, int RW>
