@@ -735,9 +735,12 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
 // and all four wavefronts meet only for the routing candidates and for the victim scan over
 // the slot table. Everything read from memory (logits, the layer's residency row, the slot
 // table, the layer's stats row, the clock, BP/BH, the mailbox sequence) is loaded up front.
-// SR: slot-table entries per thread (C <= 256 SR).
+// SR: slot-table entries per thread (C <= 256 SR). The leading scalar arguments (what the
+// up-front loads need) are preloaded into SGPRs at dispatch, so those loads do not wait for a
+// fetch of the argument block.
 template <int SR>
-__global__ __launch_bounds__(256) void ctl1_kernel(CtlArgs a) {
+__global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const int32_t* resid, const uint64_t* slot_lru,
+                                                   const int32_t* slot_key, int E, int k, int l, int C, CtlArgs a) {
     constexpr int NT = 256, kWaves = NT / 64, kSlotRegs = SR;
     __shared__ uint32_t s_ck[64];
     __shared__ int32_t s_ci[64];
@@ -749,20 +752,19 @@ __global__ __launch_bounds__(256) void ctl1_kernel(CtlArgs a) {
     __shared__ int32_t s_q;
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int E = a.E, k = a.k, l = a.layer, C = a.C;
     const uint64_t lt = (1ull << lane) - 1ull;
 
     // 0. loads, all unconditional (indices clamped), in the order they are needed
     const int ec = tid < E ? tid : E - 1;
-    const float lv = a.logits[ec];                          // logit of expert tid
-    const int rres = a.st.resid[(int64_t)l * E + ec];       // residency of expert tid
+    const float lv = logits[ec];                          // logit of expert tid
+    const int rres = resid[(int64_t)l * E + ec];          // residency of expert tid
     uint64_t pk[kSlotRegs];
     int po[kSlotRegs];
 #pragma unroll
     for (int p = 0; p < kSlotRegs; ++p) {
         const int s = tid + NT * p;
-        pk[p] = a.st.slot_lru[s < C ? s : 0];
-        po[p] = a.st.slot_key[s < C ? s : 0];
+        pk[p] = slot_lru[s < C ? s : 0];
+        po[p] = slot_key[s < C ? s : 0];
     }
     const unsigned long long st_v = a.st.stats[(int64_t)l * ST_N + (lane < ST_N ? lane : 0)];
     const uint64_t clk = *a.st.clock;
@@ -983,10 +985,13 @@ void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float*
 void launch_ctl(const CtlArgs& a, hipStream_t s, const hipEvent_t* ev) {
     const LaunchEvents le(ev);
     if (a.logits && a.T == 1 && a.E <= 256 && a.k <= 16 && a.C <= 5120) {
-        if (a.C <= 2048) EC_LAUNCH(ctl1_kernel<8>, dim3(1), dim3(256), 0, s, a);
-        else if (a.C <= 3072) EC_LAUNCH(ctl1_kernel<12>, dim3(1), dim3(256), 0, s, a);
-        else if (a.C <= 4096) EC_LAUNCH(ctl1_kernel<16>, dim3(1), dim3(256), 0, s, a);
-        else EC_LAUNCH(ctl1_kernel<20>, dim3(1), dim3(256), 0, s, a);
+#define EC_C1(SR) EC_LAUNCH(ctl1_kernel<SR>, dim3(1), dim3(256), 0, s, a.logits, (const int32_t*)a.st.resid, \
+                         (const uint64_t*)a.st.slot_lru, (const int32_t*)a.st.slot_key, a.E, a.k, a.layer, a.C, a)
+        if (a.C <= 2048) EC_C1(8);
+        else if (a.C <= 3072) EC_C1(12);
+        else if (a.C <= 4096) EC_C1(16);
+        else EC_C1(20);
+#undef EC_C1
     } else if (a.T * a.k <= 256) EC_LAUNCH(ctl_kernel<256>, dim3(1), dim3(256), 0, s, a);
     else EC_LAUNCH(ctl_kernel<1024>, dim3(1), dim3(1024), 0, s, a);
 }

@@ -166,16 +166,20 @@ __device__ __forceinline__ float chunk_dot_packed(uint4 wv, uint32_t scale, cons
 // ---------------------------------------------------------------------------
 // Fill: copy the q filled experts from the pinned host pool (read over the
 // host link by the GPU itself: the slot addresses are decided on the device)
-// into their victim slots. Grid: K x chunks; blocks past q exit.
+// into their victim slots. Grid: K x chunks; blocks past q exit. pool_l is the
+// layer's first expert in the pool. Every argument is a scalar, preloaded into
+// SGPRs at dispatch, so the count and list loads are issued at once.
 constexpr uint64_t kFillChunk = 256 * 1024;
 
-__global__ __launch_bounds__(256) void fill_kernel(DecodeArgs a, int chunks) {
+__global__ __launch_bounds__(256) void fill_kernel(const int32_t* counts, const int32_t* fills, const int32_t* victims,
+                                                   const uint8_t* pool_l, uint8_t* slots, uint64_t expert_bytes,
+                                                   int chunks) {
     const int i = blockIdx.x / chunks, c = blockIdx.x % chunks;
-    if (i >= a.counts[CNT_Q]) return;
-    const int f = a.fills[i], v = a.victims[i];
-    const uint64_t n16 = a.expert_bytes / 16;
-    const uint4* src = reinterpret_cast<const uint4*>(a.pool + ((uint64_t)a.layer * a.E + f) * a.expert_bytes);
-    uint4* dst = reinterpret_cast<uint4*>(a.slots + (uint64_t)v * a.expert_bytes);
+    if (i >= counts[CNT_Q]) return;
+    const int f = fills[i], v = victims[i];
+    const uint64_t n16 = expert_bytes / 16;
+    const uint4* src = reinterpret_cast<const uint4*>(pool_l + (uint64_t)f * expert_bytes);
+    uint4* dst = reinterpret_cast<uint4*>(slots + (uint64_t)v * expert_bytes);
     const uint64_t b0 = (uint64_t)c * (kFillChunk / 16);
     uint64_t b1 = b0 + kFillChunk / 16;
     if (b1 > n16) b1 = n16;
@@ -349,19 +353,23 @@ __device__ __noinline__ void wait_host_branch(const uint32_t* hseq, const uint32
 // d at slot c*QB + (d ^ (c % QB)), so the wave's 16-byte reads of one quad
 // index hit consecutive bank groups. With `residual` set, the layer input is
 // added to each merged output row before rounding (a chained MoE block).
+// The leading scalar arguments (what the first loads and the weight addresses need) are
+// preloaded into SGPRs at dispatch; the argument block is read for the epilogue only.
 template <int WDT, int NCH, int R, int G, bool HOST, bool FULL, bool STAGE>
-__global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, const float* wts, const void* actp,
+                                                   const uint8_t* slots, uint64_t expert_bytes, int H, int I, int k,
+                                                   DecodeArgs a) {
     constexpr int EPC = Fmt<WDT>::EPC;
     constexpr int AB = WDT == EC_DT_F32 ? 4 : 2; // bytes per activation element
     constexpr int QB = EPC * AB / 16;            // 16-byte quads per chunk
     extern __shared__ uint4 s_q[];               // [G][I * AB / 16]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row0 = (blockIdx.x * 4 + wave) * R;
-    const int H = a.H, I = a.I, k = a.k, IQ = I * AB / 16;
+    const int IQ = I * AB / 16;
     const int rbi = row_bytes<WDT>(I), n16 = rbi >> 4;
     const uint64_t down_off = 2ull * I * row_bytes<WDT>(H) + (uint64_t)row0 * rbi;
     const uint64_t dsc_off = 3ull * I * row_bytes<WDT>(H) + 2ull * I * (H / 32) + (uint64_t)row0 * (I / 32);
-    const uint4* actq = reinterpret_cast<const uint4*>(a.act);
+    const uint4* actq = reinterpret_cast<const uint4*>(actp);
     // issued first: whether the step has host-side pairs (read again only in the epilogue)
     const int nhost = HOST ? a.counts[CNT_HOST] : 0;
     {
@@ -377,8 +385,8 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
             const int ng = min(G, k - j0); // uniform
             // one vector load per index array (lane j: pair j0 + j), then broadcasts
             const int pl = t * k + min(j0 + lane, k - 1);
-            const int rw_l = a.rewritten[pl];
-            const float w_l = a.w[pl];
+            const int rw_l = rewritten[pl];
+            const float w_l = wts[pl];
             if (j0 == 0) { rw0 = rw_l; w0 = w_l; }
             int rw[G];
             float wt[G];
@@ -419,9 +427,9 @@ __global__ __launch_bounds__(256) void down_kernel(DecodeArgs a) {
             for (int jj = 0; jj < G; ++jj) {
                 if (jj >= ng) break;
                 const bool hp = HOST && rw[jj] < 0;
-                const uint8_t* base = a.slots + (uint64_t)(hp ? 0 : rw[jj]) * a.expert_bytes;
-                const uint8_t* rowp = hp ? reinterpret_cast<const uint8_t*>(a.act) : base + down_off;
-                const uint8_t* scp = hp ? reinterpret_cast<const uint8_t*>(a.act) : base + dsc_off;
+                const uint8_t* base = slots + (uint64_t)(hp ? 0 : rw[jj]) * expert_bytes;
+                const uint8_t* rowp = hp ? reinterpret_cast<const uint8_t*>(actp) : base + down_off;
+                const uint8_t* scp = hp ? reinterpret_cast<const uint8_t*>(actp) : base + dsc_off;
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -603,7 +611,9 @@ void launch_gate(const void* wr, const void* x, bool f32, int T, int E, int H, f
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s, const hipEvent_t* ev) {
     const LaunchEvents le(ev);
     const int chunks = (int)((a.expert_bytes + kFillChunk - 1) / kFillChunk);
-    EC_LAUNCH(fill_kernel, dim3(K * chunks), dim3(256), 0, s, a, chunks);
+    const uint8_t* pool_l = a.pool + (uint64_t)a.layer * a.E * a.expert_bytes;
+    EC_LAUNCH(fill_kernel, dim3(K * chunks), dim3(256), 0, s, a.counts, a.fills, a.victims, pool_l, a.slots,
+              a.expert_bytes, chunks);
 }
 
 
@@ -648,7 +658,8 @@ template <int WDT, int NCH, int R, int G, bool STAGE>
 static void down_go2(const DecodeArgs& a, bool full, hipStream_t s) {
     const dim3 blk(256), grid(a.H / (4 * R), a.T);
     const size_t lds = STAGE ? (size_t)G * a.I * (WDT == EC_DT_F32 ? 4 : 2) : 0;
-#define EC_D1(HOST, FULL) EC_LAUNCH((down_kernel<WDT, NCH, R, G, HOST, FULL, STAGE>), grid, blk, lds, s, a)
+#define EC_D1(HOST, FULL) EC_LAUNCH((down_kernel<WDT, NCH, R, G, HOST, FULL, STAGE>), grid, blk, lds, s, a.rewritten, \
+                                  a.w, (const void*)a.act, (const uint8_t*)a.slots, a.expert_bytes, a.H, a.I, a.k, a)
     if constexpr (WDT != EC_DT_F32) { // f32 (small test shapes) only takes the guarded form
         if (full) {
             if (a.host_pairs) EC_D1(true, true); else EC_D1(false, true);
