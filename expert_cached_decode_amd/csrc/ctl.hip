@@ -370,9 +370,13 @@ __device__ int block_scan(int v, int* s_wtot, int* total) {
 // NT threads (256 when T*k <= 256: one wavefront per SIMD keeps the VALU cost of
 // this latency-bound kernel low; 1024 otherwise). Each thread holds SR entries
 // of the slot table in registers (slots tid + NT p): 5120 slots; larger tables
-// are re-read from memory in the victim rounds.
+// are re-read from memory in the victim rounds. The leading scalar arguments (the
+// pointers and sizes of the up-front loads; resid_l is the layer's residency row)
+// are preloaded into SGPRs at dispatch.
 template <int NT>
-__global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
+__global__ __launch_bounds__(NT) void ctl_kernel(const float* logits, const int32_t* ids_in, const int32_t* resid_l,
+                                                 const uint64_t* slot_lru, const int32_t* slot_key, int E, int k, int T,
+                                                 int C, CtlArgs a) {
     constexpr int kCtlThreads = NT;
     constexpr int kCtlWaves = NT / 64;
     constexpr int kSlotRegs = 5120 / NT;
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     __shared__ int32_t s_ci[64];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int E = a.E, k = a.k, T = a.T, l = a.layer, C = a.C;
+    const int l = a.layer;
     const int n = T * k;
     const int nwords = (E + 31) >> 5;
     const uint64_t clk = *a.st.clock;
@@ -408,21 +412,21 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     //    routing and dedup then hide
     //    (one token with E <= 64 per wavefront: each wavefront holds a 64-logit segment), then
     //    the layer's residency row (E <= 512; staged through LDS after the routing)
-    const bool seg = a.logits && T == 1 && E <= 64 * kCtlWaves && kCtlWaves * k <= 64;
+    const bool seg = logits && T == 1 && E <= 64 * kCtlWaves && kCtlWaves * k <= 64;
     // several tokens with E <= 256, k <= 16: four per wavefront, one per DPP row (rows_topk);
     // else one per wavefront from a row of up to 512 logits held in registers (wave_topk)
-    const bool rows = a.logits && !seg && T > 1 && E <= 256 && k <= 16;
-    const bool pre = a.logits && !seg && !rows && E <= 512 && wave < T;
+    const bool rows = logits && !seg && T > 1 && E <= 256 && k <= 16;
+    const bool pre = logits && !seg && !rows && E <= 512 && wave < T;
     // with fused routing a token's k ids are distinct, so a pair's rank among the earlier pairs of
     // its expert is the number of earlier tokens routed to that expert (token masks in LDS)
-    const bool tmask = a.logits && T <= 32 && E <= 512;
+    const bool tmask = logits && T <= 32 && E <= 512;
     // The first routing rows, as 16 unconditional loads per lane (index clamped; a valid dummy
     // word when neither form applies): rows: logits 16 i + (lane & 15) of token 4 wave + lane / 16;
     // pre: logits lane + 64 i (i < 8) of token wave.
     float rl[16];
     {
         const int tr = rows ? min(4 * wave + (lane >> 4), T - 1) : wave;
-        const float* base = (rows || pre) ? a.logits + (int64_t)tr * E : reinterpret_cast<const float*>(a.st.clock);
+        const float* base = (rows || pre) ? logits + (int64_t)tr * E : reinterpret_cast<const float*>(resid_l);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int e = rows ? 16 * i + (lane & 15) : pre ? lane + 64 * (i & 7) : 0;
@@ -437,9 +441,9 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     // is always valid. Unconditional loads keep the wait counts static, so no use of an early
     // load waits for the loads issued after it.
     const int seg_e = 64 * wave + lane;
-    const uint32_t* in_p = seg ? reinterpret_cast<const uint32_t*>(a.logits) + (seg_e < E ? seg_e : E - 1)
-                           : (!a.logits && n > 0) ? reinterpret_cast<const uint32_t*>(a.ids_in) + (tid < n ? tid : 0)
-                                                  : reinterpret_cast<const uint32_t*>(a.st.clock);
+    const uint32_t* in_p = seg ? reinterpret_cast<const uint32_t*>(logits) + (seg_e < E ? seg_e : E - 1)
+                           : (!logits && n > 0) ? reinterpret_cast<const uint32_t*>(ids_in) + (tid < n ? tid : 0)
+                                                  : reinterpret_cast<const uint32_t*>(resid_l);
     const uint32_t in_v = *in_p;
     const float segv = __uint_as_float(in_v);
     constexpr int kResRegs = (512 + NT - 1) / NT;
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
 #pragma unroll
     for (int p = 0; p < kResRegs; ++p) {
         const int e = tid + NT * p;
-        rres[p] = a.st.resid[(int64_t)l * E + (e < E ? e : E - 1)];
+        rres[p] = resid_l[e < E ? e : E - 1];
     }
     uint64_t pk[kSlotRegs];
     int po[kSlotRegs];
@@ -457,8 +461,8 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
 #pragma unroll
     for (int p = 0; p < kSlotRegs; ++p) {
         const int s = tid + kCtlThreads * p;
-        pk[p] = a.st.slot_lru[s < C ? s : 0];
-        po[p] = a.st.slot_key[s < C ? s : 0];
+        pk[p] = slot_lru[s < C ? s : 0];
+        po[p] = slot_key[s < C ? s : 0];
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -472,14 +476,14 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int e = 16 * i + (lane & 15);
-                    rl[i] = a.logits[(int64_t)tr * E + (e < E ? e : E - 1)];
+                    rl[i] = logits[(int64_t)tr * E + (e < E ? e : E - 1)];
                 }
             }
             rows_topk(rl, T, E, k, t0, a.sb.ids, a.sb.w, s_ids, s_w);
         }
-    } else if (a.logits) {
+    } else if (logits) {
         for (int t = wave; t < T; t += kCtlWaves)
-            wave_topk(a.logits + (int64_t)t * E, E, k, a.sb.ids + t * k, a.sb.w + t * k, s_ids + t * k,
+            wave_topk(logits + (int64_t)t * E, E, k, a.sb.ids + t * k, a.sb.w + t * k, s_ids + t * k,
                       s_w + t * k, rv, pre && t == wave);
     } else if (tid < n) {
         s_ids[tid] = (int32_t)in_v;
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
     for (int c = 0; c < kPairRegs; ++c) {
         const int i = tid + kCtlThreads * c;
         const int id = i < n ? s_ids[i] : -1;
-        res_p[c] = (id >= 0 && id < E) ? (rrow ? s_res[id] : a.st.resid[(int64_t)l * E + id]) : -1;
+        res_p[c] = (id >= 0 && id < E) ? (rrow ? s_res[id] : resid_l[id]) : -1;
     }
     for (int i = tid; i < n; i += kCtlThreads) {
         int id = s_ids[i];
@@ -588,8 +592,8 @@ __global__ __launch_bounds__(NT) void ctl_kernel(CtlArgs a) {
             for (int p = 0; p < kSlotRegs; ++p)
                 if (pk[p] >= lo && pk[p] < mine) { mine = pk[p]; ms = tid + kCtlThreads * p; mo = po[p]; }
             for (int s = tid + kCtlThreads * kSlotRegs; s < C; s += kCtlThreads) { // tables beyond the registers
-                uint64_t key = a.st.slot_lru[s];
-                const int occ = a.st.slot_key[s];
+                uint64_t key = slot_lru[s];
+                const int occ = slot_key[s];
                 const uint32_t e = (uint32_t)(occ - l * E);
                 if (e < (uint32_t)E && ((s_bits[e >> 5] >> (e & 31)) & 1u)) key = ~0ull;
                 if (key >= lo && key < mine) { mine = key; ms = s; mo = occ; }
@@ -992,8 +996,14 @@ void launch_ctl(const CtlArgs& a, hipStream_t s, const hipEvent_t* ev) {
         else if (a.C <= 4096) EC_C1(16);
         else EC_C1(20);
 #undef EC_C1
-    } else if (a.T * a.k <= 256) EC_LAUNCH(ctl_kernel<256>, dim3(1), dim3(256), 0, s, a);
-    else EC_LAUNCH(ctl_kernel<1024>, dim3(1), dim3(1024), 0, s, a);
+    } else {
+        const int32_t* resid_l = a.st.resid + (int64_t)a.layer * a.E;
+#define EC_CG(NT) EC_LAUNCH(ctl_kernel<NT>, dim3(1), dim3(NT), 0, s, a.logits, a.ids_in, resid_l, \
+                            (const uint64_t*)a.st.slot_lru, (const int32_t*)a.st.slot_key, a.E, a.k, a.T, a.C, a)
+        if (a.T * a.k <= 256) EC_CG(256);
+        else EC_CG(1024);
+#undef EC_CG
+    }
 }
 
 void launch_set_bw(uint32_t* bw, uint32_t bp, uint32_t bh, hipStream_t s) {
