@@ -208,6 +208,23 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
                                                  uint64_t expert_bytes, const void* xin, int H, int I, int chunks,
                                                  DecodeArgs a) {
     constexpr int EPC = Fmt<WDT>::EPC;
+    constexpr bool PK = WDT != EC_DT_F32;
+    // One token, packed input, whole chunks: the block loads x once (XQ 16-byte quads per thread,
+    // issued first of all) and its wavefronts read it from LDS, rather than each wavefront loading
+    // all of x through the CU's vector memory path ahead of its weight rows.
+    constexpr int XQ = PK ? NCH * (EPC / 8) / kGuWaves : 0;
+    constexpr bool XL = T1 && PK && FULL && XQ >= 1 && (NCH * (EPC / 8)) % kGuWaves == 0;
+    __shared__ uint4 s_xq[XL ? 256 * XQ : 1];
+    // (plain 32-bit arrays: an array of uint4 can be placed in LDS by the compiler, which then
+    // waits for these loads before the weight rows are issued)
+    uint32_t xqx[XL ? XQ : 1], xqy[XL ? XQ : 1], xqz[XL ? XQ : 1], xqw[XL ? XQ : 1];
+    if constexpr (XL) {
+#pragma unroll
+        for (int u = 0; u < XQ; ++u) {
+            const uint4 v = reinterpret_cast<const uint4*>(xin)[threadIdx.x + 256 * u];
+            xqx[u] = v.x; xqy[u] = v.y; xqz[u] = v.z; xqw[u] = v.w;
+        }
+    }
     const int g = blockIdx.x / chunks, ch = blockIdx.x % chunks;
     // both loads are issued before the exit test (one round trip)
     const int n_gpu = counts[CNT_GPU];
@@ -224,7 +241,6 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
     // is loaded before the weight rows (loads complete in order, so the arithmetic then waits for
     // the weights in flight, not behind them); with more, each pair loads its token in turn (the
     // early load measured slower there).
-    constexpr bool PK = WDT != EC_DT_F32;
     float xv[NCH][PK ? 1 : EPC];
     uint32_t xw[NCH][PK ? EPC / 2 : 1];
     auto load_x = [&](int t) {
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
             }
         }
     };
-    if constexpr (T1) load_x(0);
+    if constexpr (T1 && !XL) load_x(0);
     uint4 wg[RW][NCH], wu[RW][NCH];
     uint32_t sg[RW][NCH], su[RW][NCH];
 #pragma unroll
@@ -268,6 +284,22 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
     // keep every weight load ahead of the arithmetic (the scheduler would otherwise
     // interleave them with the dot products and cut the loads in flight)
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XL) { // x quad q holds elements 8q..8q+7; chunk c uses quads c * EPC / 8 onward
+#pragma unroll
+        for (int u = 0; u < XQ; ++u) s_xq[threadIdx.x + 256 * u] = make_uint4(xqx[u], xqy[u], xqz[u], xqw[u]);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int c = lane + 64 * j;
+#pragma unroll
+            for (int q = 0; q < EPC / 8; ++q) {
+                const uint4 u = s_xq[c * (EPC / 8) + q];
+                xw[j][4 * q] = u.x; xw[j][4 * q + 1] = u.y; xw[j][4 * q + 2] = u.z; xw[j][4 * q + 3] = u.w;
+            }
+        }
+        // (no use of the weights or scales moves above the staging: the barrier waits for x only)
+        __builtin_amdgcn_sched_barrier(0);
+    }
     const int np = T1 ? 1 : d.z;
     for (int pi = 0; pi < np; ++pi) {
         const int pair = (T1 || pi == 0) ? d.w : a.tok_pairs[d.y + pi];
