@@ -264,6 +264,23 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
     if constexpr (T1 && !XL) load_x(0);
     uint4 wg[RW][NCH], wu[RW][NCH];
     uint32_t sg[RW][NCH], su[RW][NCH];
+    // MXFP4 block scales on the one-token path: the RW gate rows' scale bytes are contiguous
+    // (RW * NCH * 64 bytes), as are the up rows'. They are read as 32-bit words, one per lane and
+    // load (issued ahead of the codes), and each lane takes its byte from the owning lane by
+    // ds_bpermute when it uses it: two vector loads and two registers where one byte load per row
+    // and chunk took RW * NCH of each.
+    constexpr bool SCW = WDT == EC_DT_MXFP4 && XL && (RW * NCH * 16) % 64 == 0;
+    constexpr int NSD = SCW ? RW * NCH * 16 / 64 : 1;
+    uint32_t scg[NSD], scu[NSD];
+    if constexpr (SCW) {
+        const uint32_t* gs = reinterpret_cast<const uint32_t*>(gsc + (uint64_t)row0 * (H / 32));
+        const uint32_t* us = reinterpret_cast<const uint32_t*>(gsc + (uint64_t)(I + row0) * (H / 32));
+#pragma unroll
+        for (int u = 0; u < NSD; ++u) {
+            scg[u] = gs[lane + 64 * u];
+            scu[u] = us[lane + 64 * u];
+        }
+    }
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
         const uint8_t* gp = base + (uint64_t)(row0 + rr) * rb;
@@ -274,7 +291,7 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
             if (FULL || c < n16) {
                 wg[rr][j] = load_stream(gp + 16ull * c);
                 wu[rr][j] = load_stream(up + 16ull * c);
-                if (WDT == EC_DT_MXFP4) {
+                if (WDT == EC_DT_MXFP4 && !SCW) {
                     sg[rr][j] = gsc[(uint64_t)(row0 + rr) * (H / 32) + c];
                     su[rr][j] = gsc[(uint64_t)(I + row0 + rr) * (H / 32) + c];
                 }
@@ -284,21 +301,53 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
     // keep every weight load ahead of the arithmetic (the scheduler would otherwise
     // interleave them with the dot products and cut the loads in flight)
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (XL) { // x quad q holds elements 8q..8q+7; chunk c uses quads c * EPC / 8 onward
+    if constexpr (XL) {
+        // x quad q holds elements 8q..8q+7; chunk c uses quads c * EPC / 8 onward. The chunks are
+        // taken in turn (x read from LDS per chunk, every row's accumulators live), which keeps the
+        // register count low enough for all of the launch's wavefronts to be resident at once;
+        // each accumulator still sums its chunks in ascending order.
 #pragma unroll
         for (int u = 0; u < XQ; ++u) s_xq[threadIdx.x + 256 * u] = make_uint4(xqx[u], xqy[u], xqz[u], xqw[u]);
         __syncthreads();
+        float ag[RW], au[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) ag[rr] = au[rr] = 0.f;
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const int c = lane + 64 * j;
+            uint32_t xj[EPC / 2];
 #pragma unroll
             for (int q = 0; q < EPC / 8; ++q) {
                 const uint4 u = s_xq[c * (EPC / 8) + q];
-                xw[j][4 * q] = u.x; xw[j][4 * q + 1] = u.y; xw[j][4 * q + 2] = u.z; xw[j][4 * q + 3] = u.w;
+                xj[4 * q] = u.x; xj[4 * q + 1] = u.y; xj[4 * q + 2] = u.z; xj[4 * q + 3] = u.w;
+            }
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr) {
+                uint32_t gsb = 0u, usb = 0u;
+                if constexpr (SCW) {
+                    // byte c of row rr is word rr * 16 NCH + 16 j + lane / 4 of the RW rows: load
+                    // (rr * 16 NCH + 16 j) / 64, lane (rr * 16 NCH + 16 j) % 64 + lane / 4
+                    const int w0 = rr * 16 * NCH + 16 * j, u = w0 / 64;
+                    const int src = ((w0 % 64) + (lane >> 2)) * 4, sh = 8 * (lane & 3);
+                    gsb = ((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)scg[u]) >> sh) & 0xffu;
+                    usb = ((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)scu[u]) >> sh) & 0xffu;
+                } else if constexpr (WDT == EC_DT_MXFP4) {
+                    gsb = sg[rr][j];
+                    usb = su[rr][j];
+                }
+                ag[rr] = chunk_dot_packed<WDT>(wg[rr][j], gsb, xj, ag[rr]);
+                au[rr] = chunk_dot_packed<WDT>(wu[rr][j], usb, xj, au[rr]);
             }
         }
-        // (no use of the weights or scales moves above the staging: the barrier waits for x only)
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+            const float accg = wave_sum(ag[rr]), accu = wave_sum(au[rr]);
+            if (lane == 0) {
+                const float h = accg / (1.f + expf(-accg)) * accu;
+                reinterpret_cast<uint16_t*>(a.act)[(int64_t)d.w * I + row0 + rr] = f32_to_bf16(h);
+            }
+        }
+        return;
     }
     const int np = T1 ? 1 : d.z;
     for (int pi = 0; pi < np; ++pi) {
