@@ -198,14 +198,15 @@ __global__ __launch_bounds__(256) void fill_kernel(const int32_t* counts, const 
 // consumes on the matrix-core prefill path as well). A wavefront owns RW row
 // pairs of one expert; each lane holds NCH 16-byte chunks of every row in
 // registers, so one expert's weights are read once whatever its token count.
-// Grid: U_max x (I / (4 RW)); blocks past the step's cache-side count exit.
+// Grid: (I / (4 RW)) x U_max (no division for the block's expert); blocks past the step's
+// cache-side count exit.
 // FULL: every lane owns NCH whole chunks (row bytes = 1024 NCH), no guards.
 // The leading scalar arguments are everything the descriptor and weight addresses need: they
 // are preloaded into SGPRs at dispatch (kernarg preloading), so the first loads do not wait
 // for a fetch of the argument block, whose remaining fields are needed only later.
 template <int WDT, int NCH, int RW, bool T1, bool FULL>
 __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const int4* gpu_desc, const uint8_t* slots,
-                                                 uint64_t expert_bytes, const void* xin, int H, int I, int chunks,
+                                                 uint64_t expert_bytes, const void* xin, int H, int I,
                                                  DecodeArgs a) {
     constexpr int EPC = Fmt<WDT>::EPC;
     constexpr bool PK = WDT != EC_DT_F32;
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
             xqx[u] = v.x; xqy[u] = v.y; xqz[u] = v.z; xqw[u] = v.w;
         }
     }
-    const int g = blockIdx.x / chunks, ch = blockIdx.x % chunks;
+    const int g = blockIdx.y, ch = blockIdx.x;
     // both loads are issued before the exit test (one round trip)
     const int n_gpu = counts[CNT_GPU];
     const int4 d = gpu_desc[g];
@@ -702,9 +703,9 @@ void launch_fill(const DecodeArgs& a, int K, hipStream_t s, const hipEvent_t* ev
 template <int WDT, int NCH, int RW>
 static void gu_go(const DecodeArgs& a, bool full, hipStream_t s) {
     const int chunks = a.I / (kGuWaves * RW);
-    const dim3 grid(a.U_max * chunks), blk(256);
+    const dim3 grid(chunks, a.U_max), blk(256);
 #define EC_GU(T1, FULL) EC_LAUNCH((gu_kernel<WDT, NCH, RW, T1, FULL>), grid, blk, 0, s, a.counts, a.gpu_desc, \
-                                   (const uint8_t*)a.slots, a.expert_bytes, a.x, a.H, a.I, chunks, a)
+                                   (const uint8_t*)a.slots, a.expert_bytes, a.x, a.H, a.I, a)
     if (full) {
         if (a.T == 1) EC_GU(true, true);
         else EC_GU(false, true);
