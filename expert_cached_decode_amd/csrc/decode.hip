@@ -491,24 +491,26 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
                     sqx[u] = v.x; sqy[u] = v.y; sqz[u] = v.z; sqw[u] = v.w;
                 }
             } else {
+                // every slot of the group loads (a partial group's spare slots re-read its last row),
+                // so no load is behind a branch and the compiler's wait counts stay exact
 #pragma unroll
                 for (int jj = 0; jj < G; ++jj) {
-                    if (jj >= ng) break;
+                    const int jc = min(jj, ng - 1);
 #pragma unroll
                     for (int q = 0; q < NCH; ++q) {
                         const int c = lane + 64 * q;
                         if (FULL || c < n16)
 #pragma unroll
-                            for (int d = 0; d < QB; ++d) ar[jj][q][d] = actq[(int64_t)(t * k + j0 + jj) * IQ + c * QB + d];
+                            for (int d = 0; d < QB; ++d) ar[jj][q][d] = actq[(int64_t)(t * k + j0 + jc) * IQ + c * QB + d];
                     }
                 }
             }
             uint4 wd[G][R][NCH];
             uint32_t sd[G][R][NCH];
+            // a spare slot of a partial group (jj >= ng) reads the dummy row like a host-side pair
 #pragma unroll
             for (int jj = 0; jj < G; ++jj) {
-                if (jj >= ng) break;
-                const bool hp = HOST && rw[jj] < 0;
+                const bool hp = jj >= ng || (HOST && rw[jj] < 0);
                 const uint8_t* base = slots + (uint64_t)(hp ? 0 : rw[jj]) * expert_bytes;
                 const uint8_t* rowp = hp ? reinterpret_cast<const uint8_t*>(actp) : base + down_off;
                 const uint8_t* scp = hp ? reinterpret_cast<const uint8_t*>(actp) : base + dsc_off;
@@ -544,8 +546,7 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int jj = 0; jj < G; ++jj) {
-                if (jj >= ng) break;
-                const bool hp = HOST && rw[jj] < 0;
+                const bool hp = jj >= ng || (HOST && rw[jj] < 0); // excluded by select below
 #pragma unroll
                 for (int q = 0; q < NCH; ++q) {
                     const int c = lane + 64 * q;
