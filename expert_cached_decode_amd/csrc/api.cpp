@@ -204,11 +204,17 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     x->st.resid = d.take<int32_t>(LE);
     x->st.slot_key = d.take<int32_t>(LE);
     x->st.slot_lru = d.take<uint64_t>(LE);
-    x->st.clock = d.take<uint64_t>(1);
-    x->st.bw = d.take<uint32_t>(2);
+    // the LRU clock, BP/BH, the mailbox sequences and the per-layer stats share one block, so
+    // that the one-token control kernel reaches them from one pointer: clock at +0, bw[2] at +8,
+    // hseq at +16, hseen at +20, stats [L][ST_N] from +32
+    uint64_t* words = d.take<uint64_t>(4 + (uint64_t)x->L * ST_N);
+    x->st.clock = words;
+    x->st.bw = words ? reinterpret_cast<uint32_t*>(words + 1) : nullptr;
+    x->st.hseq = words ? reinterpret_cast<uint32_t*>(words + 2) : nullptr;
+    x->st.hseen = words ? reinterpret_cast<uint32_t*>(words + 2) + 1 : nullptr;
+    x->st.stats = words ? reinterpret_cast<unsigned long long*>(words + 4) : nullptr;
     x->st.err = d.take<int32_t>(1);
     x->probe_sink = d.take<uint32_t>(4);
-    x->st.stats = d.take<unsigned long long>((uint64_t)x->L * ST_N);
     const int n = x->nmax, U = x->Umax;
     x->sb.ids = d.take<int32_t>(n);
     x->sb.w = d.take<float>(n);
@@ -224,8 +230,6 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     x->sb.rewritten = d.take<int32_t>(n);
     x->sb.gpu_desc = d.take<int4>(U);
     x->sb.tok_pairs = d.take<int32_t>(n);
-    x->st.hseq = d.take<uint32_t>(1);
-    x->st.hseen = d.take<uint32_t>(1);
     x->gate_logits = d.take<float>((uint64_t)x->Tmax * x->E);
     const uint64_t xbytes = (uint64_t)x->Tmax * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
     const uint64_t mb_bytes = mailbox_ints(n) * 4 + xbytes;

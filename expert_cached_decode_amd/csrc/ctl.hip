@@ -741,10 +741,13 @@ __global__ __launch_bounds__(NT) void ctl_kernel(const float* logits, const int3
 // table, the layer's stats row, the clock, BP/BH, the mailbox sequence) is loaded up front.
 // SR: slot-table entries per thread (C <= 256 SR). The leading scalar arguments (what the
 // up-front loads need) are preloaded into SGPRs at dispatch, so those loads do not wait for a
-// fetch of the argument block.
+// fetch of the argument block; `words` is the state block holding the clock, BP/BH, the mailbox
+// sequence and the per-layer stats (clock at +0, bw at +8, hseq at +16, stats from +32), read
+// and updated through it.
 template <int SR>
 __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const int32_t* resid, const uint64_t* slot_lru,
-                                                   const int32_t* slot_key, int E, int k, int l, int C, CtlArgs a) {
+                                                   const int32_t* slot_key, int E, int k, int l, int C,
+                                                   uint64_t* words, CtlArgs a) {
     constexpr int NT = 256, kWaves = NT / 64, kSlotRegs = SR;
     __shared__ uint32_t s_ck[64];
     __shared__ int32_t s_ci[64];
@@ -770,10 +773,16 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
         pk[p] = slot_lru[s < C ? s : 0];
         po[p] = slot_key[s < C ? s : 0];
     }
-    const unsigned long long st_v = a.st.stats[(int64_t)l * ST_N + (lane < ST_N ? lane : 0)];
-    const uint64_t clk = *a.st.clock;
-    const uint32_t bp = a.st.bw[0], bh = a.st.bw[1];
-    const uint32_t hs = *a.st.hseq;
+    const uint64_t clk = words[0];
+    const uint32_t bp = reinterpret_cast<const uint32_t*>(words + 1)[0];
+    const uint32_t bh = reinterpret_cast<const uint32_t*>(words + 1)[1];
+    const uint32_t hs = reinterpret_cast<const uint32_t*>(words + 2)[0];
+    unsigned long long* stats = reinterpret_cast<unsigned long long*>(words + 4);
+    const unsigned long long st_v = stats[(int64_t)l * ST_N + (lane < ST_N ? lane : 0)];
+    // output pointers of the argument block, fetched now (the empty asm keeps the compiler from
+    // sinking their loads past the first routing stage, where the block barrier would wait for them)
+    asm volatile("" ::"s"(a.sb.ids), "s"(a.sb.w), "s"(a.sb.uniq), "s"(a.sb.counts), "s"(a.sb.pos), "s"(a.sb.cls),
+                 "s"(a.sb.slot), "s"(a.sb.fills), "s"(a.x), "s"(a.x_bytes));
     __builtin_amdgcn_sched_barrier(0);
 
     // 1. routing, stage 1: the top-k of this wavefront's 64 logits (ties: lowest id)
@@ -930,13 +939,13 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
         int32_t* c = a.sb.counts;
         c[CNT_U] = k; c[CNT_H] = h; c[CNT_M] = m; c[CNT_Q] = q; c[CNT_HOST] = m - q; c[CNT_GPU] = n_gpu;
         c[6] = 0; c[7] = 0;
-        *a.st.clock = clk + 1;
+        words[0] = clk + 1;
     }
     if (lane <= ST_EVICT) {
         const unsigned long long d = lane == ST_STEPS ? 1ull : lane == ST_HITS ? (unsigned long long)h
                                    : lane == ST_MISSES ? (unsigned long long)m : lane == ST_FILLS ? (unsigned long long)q
                                    : lane == ST_HOST ? (unsigned long long)(m - q) : (unsigned long long)n_ev;
-        a.st.stats[(int64_t)l * ST_N + lane] = st_v + d;
+        stats[(int64_t)l * ST_N + lane] = st_v + d;
     }
     if (a.host_branch && m - q > 0) {
         // mailbox in pinned host memory: [counts 8][host_list n][rewritten n][w n][x bytes], n = k;
@@ -957,7 +966,7 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
         for (int i = lane; i < a.x_bytes / 16; i += 64) xd[i] = xs[i];
         __threadfence_system();
         if (lane == 0) {
-            *a.st.hseq = hs + 1;
+            reinterpret_cast<uint32_t*>(words + 2)[0] = hs + 1;
             __hip_atomic_store(a.doorbell, hs + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
@@ -990,7 +999,8 @@ void launch_ctl(const CtlArgs& a, hipStream_t s, const hipEvent_t* ev) {
     const LaunchEvents le(ev);
     if (a.logits && a.T == 1 && a.E <= 256 && a.k <= 16 && a.C <= 5120) {
 #define EC_C1(SR) EC_LAUNCH(ctl1_kernel<SR>, dim3(1), dim3(256), 0, s, a.logits, (const int32_t*)a.st.resid, \
-                         (const uint64_t*)a.st.slot_lru, (const int32_t*)a.st.slot_key, a.E, a.k, a.layer, a.C, a)
+                         (const uint64_t*)a.st.slot_lru, (const int32_t*)a.st.slot_key, a.E, a.k, a.layer, a.C, \
+                         a.st.clock, a)
         if (a.C <= 2048) EC_C1(8);
         else if (a.C <= 3072) EC_C1(12);
         else if (a.C <= 4096) EC_C1(16);

@@ -58,7 +58,8 @@ struct DevState {
     int32_t* resid;    // [L*E] slot or -1
     int32_t* slot_key; // [L*E] (only the first C used) l*E+e or -1
     uint64_t* slot_lru;// [L*E] LRU key
-    uint64_t* clock;   // [1]
+    uint64_t* clock;   // [1]; clock, bw, hseq, hseen and stats share one block: bw = clock + 1 (as
+                       // two u32), hseq = clock + 2 (as u32), hseen right after hseq, stats = clock + 4
     uint32_t* bw;      // [2] BP, BH
     int32_t* err;      // [1] device error flags (bit 0 bad expert id, bit 1 host branch timeout)
     unsigned long long* stats; // [L][ST_N]
