@@ -206,31 +206,33 @@ __global__ __launch_bounds__(256) void fill_kernel(const int32_t* counts, const 
 // for a fetch of the argument block, whose remaining fields are needed only later.
 template <int WDT, int NCH, int RW, bool T1, bool FULL>
 __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const int4* gpu_desc, const uint8_t* slots,
-                                                 uint64_t expert_bytes, const void* xin, int H, int I,
+                                                 uint64_t expert_bytes, const void* xin, int H, int I, int k,
                                                  DecodeArgs a) {
     constexpr int EPC = Fmt<WDT>::EPC;
     constexpr bool PK = WDT != EC_DT_F32;
-    // One token, packed input, whole chunks: the block loads x once (XQ 16-byte quads per thread,
-    // issued first of all) and its wavefronts read it from LDS, rather than each wavefront loading
-    // all of x through the CU's vector memory path ahead of its weight rows.
+    // Packed input, whole chunks: for each pair the block loads the token's x once (XQ 16-byte
+    // quads per thread; the first pair's before the weight rows) and its wavefronts read it from
+    // LDS, rather than each wavefront loading all of x through the CU's vector memory path.
     constexpr int XQ = PK ? NCH * (EPC / 8) / kGuWaves : 0;
-    constexpr bool XL = T1 && PK && FULL && XQ >= 1 && (NCH * (EPC / 8)) % kGuWaves == 0;
+    constexpr bool XL = PK && FULL && XQ >= 1 && (NCH * (EPC / 8)) % kGuWaves == 0;
     __shared__ uint4 s_xq[XL ? 256 * XQ : 1];
     // (plain 32-bit arrays: an array of uint4 can be placed in LDS by the compiler, which then
     // waits for these loads before the weight rows are issued)
     uint32_t xqx[XL ? XQ : 1], xqy[XL ? XQ : 1], xqz[XL ? XQ : 1], xqw[XL ? XQ : 1];
-    if constexpr (XL) {
+    auto load_xq = [&](int t) {
 #pragma unroll
         for (int u = 0; u < XQ; ++u) {
-            const uint4 v = reinterpret_cast<const uint4*>(xin)[threadIdx.x + 256 * u];
+            const uint4 v = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(xin) + (int64_t)t * H)[threadIdx.x + 256 * u];
             xqx[u] = v.x; xqy[u] = v.y; xqz[u] = v.z; xqw[u] = v.w;
         }
-    }
+    };
+    if constexpr (XL && T1) load_xq(0);
     const int g = blockIdx.y, ch = blockIdx.x;
     // both loads are issued before the exit test (one round trip)
     const int n_gpu = counts[CNT_GPU];
     const int4 d = gpu_desc[g];
     if (g >= n_gpu || d.x < 0) return;
+    if constexpr (XL && !T1) load_xq(d.w / k); // the expert's first pair
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rb = row_bytes<WDT>(H), n16 = rb >> 4;
     const uint8_t* base = slots + (uint64_t)d.x * expert_bytes;
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
     if constexpr (T1 && !XL) load_x(0);
     uint4 wg[RW][NCH], wu[RW][NCH];
     uint32_t sg[RW][NCH], su[RW][NCH];
-    // MXFP4 block scales on the one-token path: the RW gate rows' scale bytes are contiguous
+    // MXFP4 block scales on the LDS-staged path: the RW gate rows' scale bytes are contiguous
     // (RW * NCH * 64 bytes), as are the up rows'. They are read as 32-bit words, one per lane and
     // load (issued ahead of the codes), and each lane takes its byte from the owning lane by
     // ds_bpermute when it uses it: two vector loads and two registers where one byte load per row
@@ -305,47 +307,55 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
     if constexpr (XL) {
         // x quad q holds elements 8q..8q+7; chunk c uses quads c * EPC / 8 onward. The chunks are
         // taken in turn (x read from LDS per chunk, every row's accumulators live), which keeps the
-        // register count low enough for all of the launch's wavefronts to be resident at once;
-        // each accumulator still sums its chunks in ascending order.
+        // register count low enough for many wavefronts to be resident at once; each accumulator
+        // still sums its chunks in ascending order.
+        const int np = T1 ? 1 : d.z;
+        for (int pi = 0; pi < np; ++pi) {
+            const int pair = (T1 || pi == 0) ? d.w : a.tok_pairs[d.y + pi];
+            if (pi > 0) {
+                load_xq(pair / k);
+                __syncthreads(); // every wavefront is done with the previous pair's x
+            }
 #pragma unroll
-        for (int u = 0; u < XQ; ++u) s_xq[threadIdx.x + 256 * u] = make_uint4(xqx[u], xqy[u], xqz[u], xqw[u]);
-        __syncthreads();
-        float ag[RW], au[RW];
+            for (int u = 0; u < XQ; ++u) s_xq[threadIdx.x + 256 * u] = make_uint4(xqx[u], xqy[u], xqz[u], xqw[u]);
+            __syncthreads();
+            float ag[RW], au[RW];
 #pragma unroll
-        for (int rr = 0; rr < RW; ++rr) ag[rr] = au[rr] = 0.f;
+            for (int rr = 0; rr < RW; ++rr) ag[rr] = au[rr] = 0.f;
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const int c = lane + 64 * j;
-            uint32_t xj[EPC / 2];
+            for (int j = 0; j < NCH; ++j) {
+                const int c = lane + 64 * j;
+                uint32_t xj[EPC / 2];
 #pragma unroll
-            for (int q = 0; q < EPC / 8; ++q) {
-                const uint4 u = s_xq[c * (EPC / 8) + q];
-                xj[4 * q] = u.x; xj[4 * q + 1] = u.y; xj[4 * q + 2] = u.z; xj[4 * q + 3] = u.w;
+                for (int q = 0; q < EPC / 8; ++q) {
+                    const uint4 u = s_xq[c * (EPC / 8) + q];
+                    xj[4 * q] = u.x; xj[4 * q + 1] = u.y; xj[4 * q + 2] = u.z; xj[4 * q + 3] = u.w;
+                }
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr) {
+                    uint32_t gsb = 0u, usb = 0u;
+                    if constexpr (SCW) {
+                        // byte c of row rr is word rr * 16 NCH + 16 j + lane / 4 of the RW rows: load
+                        // (rr * 16 NCH + 16 j) / 64, lane (rr * 16 NCH + 16 j) % 64 + lane / 4
+                        const int w0 = rr * 16 * NCH + 16 * j, u = w0 / 64;
+                        const int src = ((w0 % 64) + (lane >> 2)) * 4, sh = 8 * (lane & 3);
+                        gsb = ((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)scg[u]) >> sh) & 0xffu;
+                        usb = ((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)scu[u]) >> sh) & 0xffu;
+                    } else if constexpr (WDT == EC_DT_MXFP4) {
+                        gsb = sg[rr][j];
+                        usb = su[rr][j];
+                    }
+                    ag[rr] = chunk_dot_packed<WDT>(wg[rr][j], gsb, xj, ag[rr]);
+                    au[rr] = chunk_dot_packed<WDT>(wu[rr][j], usb, xj, au[rr]);
+                }
             }
 #pragma unroll
             for (int rr = 0; rr < RW; ++rr) {
-                uint32_t gsb = 0u, usb = 0u;
-                if constexpr (SCW) {
-                    // byte c of row rr is word rr * 16 NCH + 16 j + lane / 4 of the RW rows: load
-                    // (rr * 16 NCH + 16 j) / 64, lane (rr * 16 NCH + 16 j) % 64 + lane / 4
-                    const int w0 = rr * 16 * NCH + 16 * j, u = w0 / 64;
-                    const int src = ((w0 % 64) + (lane >> 2)) * 4, sh = 8 * (lane & 3);
-                    gsb = ((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)scg[u]) >> sh) & 0xffu;
-                    usb = ((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)scu[u]) >> sh) & 0xffu;
-                } else if constexpr (WDT == EC_DT_MXFP4) {
-                    gsb = sg[rr][j];
-                    usb = su[rr][j];
+                const float accg = wave_sum(ag[rr]), accu = wave_sum(au[rr]);
+                if (lane == 0) {
+                    const float h = accg / (1.f + expf(-accg)) * accu;
+                    reinterpret_cast<uint16_t*>(a.act)[(int64_t)pair * I + row0 + rr] = f32_to_bf16(h);
                 }
-                ag[rr] = chunk_dot_packed<WDT>(wg[rr][j], gsb, xj, ag[rr]);
-                au[rr] = chunk_dot_packed<WDT>(wu[rr][j], usb, xj, au[rr]);
-            }
-        }
-#pragma unroll
-        for (int rr = 0; rr < RW; ++rr) {
-            const float accg = wave_sum(ag[rr]), accu = wave_sum(au[rr]);
-            if (lane == 0) {
-                const float h = accg / (1.f + expf(-accg)) * accu;
-                reinterpret_cast<uint16_t*>(a.act)[(int64_t)d.w * I + row0 + rr] = f32_to_bf16(h);
             }
         }
         return;
@@ -706,7 +716,7 @@ static void gu_go(const DecodeArgs& a, bool full, hipStream_t s) {
     const int chunks = a.I / (kGuWaves * RW);
     const dim3 grid(chunks, a.U_max), blk(256);
 #define EC_GU(T1, FULL) EC_LAUNCH((gu_kernel<WDT, NCH, RW, T1, FULL>), grid, blk, 0, s, a.counts, a.gpu_desc, \
-                                   (const uint8_t*)a.slots, a.expert_bytes, a.x, a.H, a.I, a)
+                                   (const uint8_t*)a.slots, a.expert_bytes, a.x, a.H, a.I, a.k, a)
     if (full) {
         if (a.T == 1) EC_GU(true, true);
         else EC_GU(false, true);
