@@ -534,9 +534,10 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
                             if (WDT == EC_DT_MXFP4) sd[jj][r][q] = scp[(hp ? 0 : r * (I / 32)) + c];
                         }
                     }
+                __builtin_amdgcn_sched_barrier(0); // issued pair by pair, each pair's codes with its scales
             }
             if constexpr (STAGE) {
-                __syncthreads(); // the previous group's reads are done
+                if (j0 > 0) __syncthreads(); // the previous group's reads are done
 #pragma unroll
                 for (int u = 0; u < SQ; ++u) {
                     const int i = tid + 256 * u;
