@@ -10,7 +10,7 @@
 //
 // Compute per layer: route every token (top-k, softmax over the selected k),
 // a stable counting sort of the (token, j) pairs by expert, a grouped
-// SwiGLU GEMM on bf16 matrix cores (v_mfma_f32_16x16x32_bf16; 64x64 block
+// SwiGLU GEMM on bf16 matrix cores (v_mfma_f32_16x16x32_bf16; 128x64 block
 // tiles, gate and up sharing the A tile), a grouped down-projection GEMM, and
 // the exact merge out[t] = sum_j w[t,j] y[t,j] in j order.
 #include "prefill.h"
@@ -20,8 +20,13 @@ namespace ec {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f2v __attribute__((ext_vector_type(2)));
+// 16-byte chunk in flight between global memory and LDS (a native vector type, so that the
+// prefetch arrays stay in registers; arrays of uint4 were placed in private memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 64, BN = 64, BK = 64, LDSP = BK + 8; // LDS row pitch in bf16 elements
+constexpr int BM = 128, BN = 64, BK = 64, LDSP = BK + 8; // LDS row pitch in bf16 elements
+constexpr int AQ = BM * BK / 8 / 256, BQ = BN * BK / 8 / 256; // 16-byte chunks per thread of an A / B tile
+static_assert(AQ * 256 * 8 == BM * BK && BQ * 256 * 8 == BN * BK, "tile chunks per thread");
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
@@ -38,7 +43,7 @@ __global__ void count_kernel(const int32_t* ids, int n, int32_t* cnt) {
     if (i < n) atomicAdd(&cnt[ids[i]], 1);
 }
 
-// off[e] = rows before expert e; toff[e] = 64-row tiles before expert e
+// off[e] = rows before expert e; toff[e] = BM-row tiles before expert e
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* cnt, int E, int32_t* off, int32_t* toff) {
     __shared__ int s_w[16][2];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -103,15 +108,15 @@ __device__ __forceinline__ int tile_expert(const int32_t* toff, int E, int tt) {
     return lo;
 }
 
-// B tile rows [n0, n0+64) x cols [k0, k0+64) of a [N][K] weight matrix, as 2
+// B tile rows [n0, n0+BN) x cols [k0, k0+BK) of a [N][K] weight matrix, as BQ
 // 16-byte chunks per thread (bf16 source), or decoded from MXFP4.
 template <int WDT>
-__device__ __forceinline__ void load_b(const uint8_t* W, const uint8_t* Ws, int K, int n0, int k0, uint4 (&r)[2]) {
+__device__ __forceinline__ void load_b(const uint8_t* W, const uint8_t* Ws, int K, int n0, int k0, u32x4 (&r)[BQ]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < BQ; ++q) {
         const int c = threadIdx.x + 256 * q, row = c >> 3, col = (c & 7) * 8;
         if constexpr (WDT == EC_DT_BF16) {
-            r[q] = *reinterpret_cast<const uint4*>(W + ((uint64_t)(n0 + row) * K + k0 + col) * 2);
+            r[q] = *reinterpret_cast<const u32x4*>(W + ((uint64_t)(n0 + row) * K + k0 + col) * 2);
         } else {
             // 8 MXFP4 elements (4 bytes) -> 8 bf16, exact (E2M1 x 2^(s-127) fits bf16)
             const uint32_t codes = *reinterpret_cast<const uint32_t*>(W + ((uint64_t)(n0 + row) * K + k0 + col) / 2);
@@ -129,11 +134,12 @@ __device__ __forceinline__ void load_b(const uint8_t* W, const uint8_t* Ws, int 
     }
 }
 
-__device__ __forceinline__ void store_lds(uint16_t* lds, const uint4 (&r)[2]) {
+template <int NQ>
+__device__ __forceinline__ void store_lds(uint16_t* lds, const u32x4 (&r)[NQ]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < NQ; ++q) {
         const int c = threadIdx.x + 256 * q, row = c >> 3, col = (c & 7) * 8;
-        *reinterpret_cast<uint4*>(lds + row * LDSP + col) = r[q];
+        *reinterpret_cast<u32x4*>(lds + row * LDSP + col) = r[q];
     }
 }
 
@@ -176,30 +182,32 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     const uint8_t* Wm[2] = {ebase + a.off_a, ebase + a.off_b};
     const uint8_t* Ws[2] = {ebase + a.off_sa, ebase + a.off_sb};
 
-    // A rows this thread loads (2 chunks), clamped to a valid row
-    const uint16_t* arow[2];
+    // A rows this thread loads (AQ chunks), clamped to a valid row
+    const uint16_t* arow[AQ];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < AQ; ++q) {
         const int c = threadIdx.x + 256 * q, r = c >> 3;
         const int rr = r < rows ? r : 0;
         if (FIRST) arow[q] = a.x + (uint64_t)(a.perm[g0 + rr] / a.k) * a.H;
         else arow[q] = a.act_in + (uint64_t)(g0 + rr) * a.I;
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-    f32x4 acc[NB][2][2];
+    // wavefront (wm, wn) owns rows wm * BM/2 .. + BM/2 (MI 16-row fragments) and columns wn * 32 .. + 32
+    constexpr int MI = BM / 32;
+    f32x4 acc[NB][MI][2];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint4 ra[2], rb[NB][2];
+    u32x4 ra[AQ], rb[NB][BQ];
     auto gload = [&](int k0) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < AQ; ++q) {
             const int c = threadIdx.x + 256 * q, col = (c & 7) * 8;
-            ra[q] = *reinterpret_cast<const uint4*>(arow[q] + k0 + col);
+            ra[q] = *reinterpret_cast<const u32x4*>(arow[q] + k0 + col);
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b) load_b<WDT>(Wm[b], Ws[b], K, n0, k0, rb[b]);
@@ -215,28 +223,28 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 32) {
             const int kc = kk + (lane >> 4) * 8;
-            bf16x8 fa[2];
+            bf16x8 fa[MI];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = lds_frag(sA, wm * 32 + i * 16 + (lane & 15), kc);
+            for (int i = 0; i < MI; ++i) fa[i] = lds_frag(sA, wm * (BM / 2) + i * 16 + (lane & 15), kc);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     bf16x8 fb = lds_frag(sB[b], wn * 32 + j * 16 + (lane & 15), kc);
 #pragma unroll
-                    for (int i = 0; i < 2; ++i)
+                    for (int i = 0; i < MI; ++i)
                         acc[b][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb, acc[b][i][j], 0, 0, 0);
                 }
         }
     }
     // epilogue: lane holds D[(lane/16)*4 + q][lane%16] of each 16x16 tile
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int r = wm * 32 + i * 16 + (lane >> 4) * 4 + q;
+                const int r = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + q;
                 const int n = n0 + wn * 32 + j * 16 + (lane & 15);
                 if (r >= rows) continue;
                 if constexpr (FIRST) {
