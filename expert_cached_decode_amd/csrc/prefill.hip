@@ -192,15 +192,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
         else arow[q] = a.act_in + (uint64_t)(g0 + rr) * a.I;
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-    // wavefront (wm, wn) owns rows wm * BM/2 .. + BM/2 (MI 16-row fragments) and columns wn * 32 .. + 32
+    // wavefront (wm, wn) owns rows wm * BM/2 .. + BM/2 (MI 16-row fragments) and columns
+    // wn * BN/2 .. + BN/2 (NJ 16-column fragments)
     constexpr int MI = BM / 32;
-    f32x4 acc[NB][MI][2];
+    constexpr int NJ = BN / 32;
+    f32x4 acc[NB][MI][NJ];
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NJ; ++j) acc[b][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     u32x4 ra[AQ], rb[NB][BQ];
     auto gload = [&](int k0) {
@@ -229,8 +231,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    bf16x8 fb = lds_frag(sB[b], wn * 32 + j * 16 + (lane & 15), kc);
+                for (int j = 0; j < NJ; ++j) {
+                    bf16x8 fb = lds_frag(sB[b], wn * (BN / 2) + j * 16 + (lane & 15), kc);
 #pragma unroll
                     for (int i = 0; i < MI; ++i)
                         acc[b][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb, acc[b][i][j], 0, 0, 0);
@@ -241,11 +243,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int r = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + q;
-                const int n = n0 + wn * 32 + j * 16 + (lane & 15);
+                const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
                 if (r >= rows) continue;
                 if constexpr (FIRST) {
                     const float gv = acc[0][i][j][q], uv = acc[1][i][j][q];
