@@ -104,20 +104,23 @@ def test_down_group_sizes(wd, k, T, H, I):
     ctx.close()
 
 
-@pytest.mark.parametrize("wd,H,I", [(BF16, 1024, 256), (BF16, 2048, 128), (BF16, 4096, 256), (MXFP4, 2048, 256),
-                                     (MXFP4, 4096, 128), (MXFP4, 8192, 256)])
-def test_gate_up_one_token_forms(wd, H, I):
-    """The one-token gate/up GEMV's forms: x staged in LDS (bf16 rows of 4 and 8 chunks per lane,
-    MXFP4 rows of 1, 2 and 4), MXFP4 block scales as byte loads (1 chunk) or as words handed out by
-    ds_bpermute (2 and 4 chunks: one and two words per lane), and the register form (bf16, 2 chunks);
-    with a host split. Outputs against the oracle, counters against the LRU simulator."""
-    cfg = TINY.with_(L=2, E=32, k=4, H=H, I=I, wdtype=wd, slots=24, K=4, T=1, bp=500, bh=1000, p=0.5)
+@pytest.mark.parametrize("wd,H,I,T", [(BF16, 1024, 256, 1), (BF16, 2048, 128, 1), (BF16, 4096, 256, 1),
+                                       (MXFP4, 2048, 256, 1), (MXFP4, 4096, 128, 1), (MXFP4, 8192, 256, 1),
+                                       (BF16, 2048, 128, 3), (BF16, 4096, 256, 2), (MXFP4, 2048, 256, 2),
+                                       (MXFP4, 4096, 128, 3)])
+def test_gate_up_forms(wd, H, I, T):
+    """The gate/up GEMV's forms: x staged in LDS (bf16 rows of 4 and 8 chunks per lane, MXFP4 rows
+    of 1, 2 and 4; with several tokens, each pair's token in turn behind a block barrier), MXFP4 block
+    scales as byte loads (1 chunk) or as words handed out by ds_bpermute (2 and 4 chunks: one and two
+    words per lane), and the register form (bf16, 2 chunks); with a host split. Outputs against the
+    oracle, counters against the LRU simulator."""
+    cfg = TINY.with_(L=2, E=32, k=4, H=H, I=I, wdtype=wd, slots=24, K=4, T=T, bp=500, bh=1000, p=0.5)
     pool = make_pool(cfg)
     ctx = make_ctx(cfg, pool)
-    outs, logits = run_decode(cfg, ctx, 10, 2, 1, lambda s, l: s % 3 == 1)
+    outs, logits = run_decode(cfg, ctx, 10, 2, T, lambda s, l: s % 3 == 1)
     check_against_oracle(cfg, outs, 1e-2)
     st = ctx.stats()
-    ref = sim_counts(cfg, logits, 2, 1, 24, 4, 500, 1000)
+    ref = sim_counts(cfg, logits, 2, T, 24, 4, 500, 1000)
     assert {k_: st[k_] for k_ in ref} == ref
     assert st["host"] > 0 and st["fills"] > 0
     ctx.close()
