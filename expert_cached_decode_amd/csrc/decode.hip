@@ -240,10 +240,10 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
     const int row0 = (ch * kGuWaves + wave) * RW;
     const bool xbf16 = WDT != EC_DT_F32;
 
-    // x: f32 for f32 weights, else bf16 kept in packed pairs for the dot2 unit. With one token it
+    // Register form (f32 weights, or rows that are not whole chunks per lane): each wavefront holds
+    // x itself, f32 for f32 weights, else bf16 in packed pairs for the dot2 unit. With one token it
     // is loaded before the weight rows (loads complete in order, so the arithmetic then waits for
-    // the weights in flight, not behind them); with more, each pair loads its token in turn (the
-    // early load measured slower there).
+    // the weights in flight, not behind them); with more, each pair loads its token in turn.
     float xv[NCH][PK ? 1 : EPC];
     uint32_t xw[NCH][PK ? EPC / 2 : 1];
     auto load_x = [&](int t) {
