@@ -91,3 +91,18 @@ def test_last_step_rejects_null_arguments():
     v = B.ec_step_view()
     assert lib.ec_last_step(None, ctypes.byref(v)) == -1
     assert lib.ec_last_step(None, None) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: any other --gpus (or a multi-rank launch) exits with a message
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+    env = dict(os.environ, WORLD_SIZE="2")
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py")], capture_output=True, text=True,
+                       timeout=120, env=env)
+    assert r.returncode == 2 and "one GPU" in r.stderr
