@@ -26,6 +26,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* FP4 E2M1 code -> value, from the field definition (not a lookup table). */
@@ -43,42 +44,67 @@ static double bf16_value(uint16_t b) {
     return (double)f;
 }
 
-/* element (r, c) of a [rows][cols] matrix in format wfmt */
-static double weight_at(int wfmt, const void* w, const uint8_t* sc, int cols, int64_t r, int64_t c) {
-    int64_t i = r * cols + c;
-    if (wfmt == 0) return (double)((const float*)w)[i];
-    if (wfmt == 1) return bf16_value(((const uint16_t*)w)[i]);
-    double v = e2m1_value(((const uint8_t*)w)[i]);
-    int e = (int)sc[r * (cols / 32) + c / 32] - 127;
-    return ldexp(v, e);
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Row r of a [rows][cols] weight matrix in format wfmt, widened exactly to
+ * fp64: f32 and bf16 values directly; MXFP4 element c is its E2M1 value times
+ * 2^(scale - 127), the scale byte being that of the row's block of 32
+ * elements containing c. */
+static void widen_row(int wfmt, const void* w, const uint8_t* sc, int cols, int64_t r, double* out) {
+    if (wfmt == 0) {
+        const float* p = (const float*)w + r * cols;
+        for (int c = 0; c < cols; ++c) out[c] = (double)p[c];
+    } else if (wfmt == 1) {
+        const uint16_t* p = (const uint16_t*)w + r * cols;
+        for (int c = 0; c < cols; ++c) out[c] = bf16_value(p[c]);
+    } else {
+        /* the 16 code values from the field definition; scaling one of them by the block's
+         * power of two is exact (at most 2 significant bits, exponent within fp64's range) */
+        double val[16];
+        for (unsigned code = 0; code < 16; ++code) val[code] = e2m1_value(code);
+        const uint8_t* p = (const uint8_t*)w + r * cols;
+        for (int c0 = 0; c0 < cols; c0 += 32) {
+            const double scale = ldexp(1.0, (int)sc[r * (cols / 32) + c0 / 32] - 127);
+            for (int c = c0; c < c0 + 32; ++c) out[c] = val[p[c] & 15u] * scale;
+        }
+    }
 }
 
 void oracle_decode_weights(int wfmt, const void* w, const uint8_t* sc, int rows, int cols, double* out) {
-    for (int64_t r = 0; r < rows; ++r)
-        for (int64_t c = 0; c < cols; ++c) out[r * cols + c] = weight_at(wfmt, w, sc, cols, r, c);
+    for (int64_t r = 0; r < rows; ++r) widen_row(wfmt, w, sc, cols, r, out + r * cols);
 }
 
-static double silu(double z) { return z / (1.0 + exp(-z)); }
-
 /* y[H] = f_e(x) for one expert and one token. act[I] receives the SwiGLU
- * activation silu(gate x) * (up x) (optional, may be NULL). */
+ * activation silu(gate x) * (up x) (optional, may be NULL). Each dot product
+ * runs over the contraction index in ascending order. */
 void oracle_expert(int wfmt, int H, int I, const void* wg, const uint8_t* sg, const void* wu,
                    const uint8_t* su, const void* wd, const uint8_t* sd, const double* x, double* y,
                    double* act_out) {
     double* act = act_out;
-    #pragma omp parallel for schedule(static)
-    for (int i = 0; i < I; ++i) {
-        double g = 0.0, u = 0.0;
-        for (int h = 0; h < H; ++h) {
-            g += weight_at(wfmt, wg, sg, H, i, h) * x[h];
-            u += weight_at(wfmt, wu, su, H, i, h) * x[h];
+    #pragma omp parallel
+    {
+        double* rg = (double*)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+        double* ru = (double*)malloc(sizeof(double) * (size_t)H);
+        #pragma omp for schedule(static)
+        for (int i = 0; i < I; ++i) {
+            widen_row(wfmt, wg, sg, H, i, rg);
+            widen_row(wfmt, wu, su, H, i, ru);
+            double g = 0.0, u = 0.0;
+            for (int h = 0; h < H; ++h) {
+                g += rg[h] * x[h];
+                u += ru[h] * x[h];
+            }
+            act[i] = silu(g) * u;
         }
-        act[i] = silu(g) * u;
-    }
-    #pragma omp parallel for schedule(static)
-    for (int h = 0; h < H; ++h) {
-        double s = 0.0;
-        for (int i = 0; i < I; ++i) s += weight_at(wfmt, wd, sd, I, h, i) * act[i];
-        y[h] = s;
+        /* (the implicit barrier of the loop above: every act[i] is written before it is read) */
+        #pragma omp for schedule(static)
+        for (int h = 0; h < H; ++h) {
+            widen_row(wfmt, wd, sd, I, h, rg);
+            double s = 0.0;
+            for (int i = 0; i < I; ++i) s += rg[i] * act[i];
+            y[h] = s;
+        }
+        free(rg);
+        free(ru);
     }
 }

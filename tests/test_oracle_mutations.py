@@ -24,13 +24,12 @@ GOLD = os.path.join(ROOT, "tests", "golden")
 C_MUTANTS = {
     "swap_gate_up": ("act[i] = silu(g) * u;", "act[i] = silu(u) * g;"),
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
-    "down_index": ("s += weight_at(wfmt, wd, sd, I, h, i) * act[i];",
-                   "s += weight_at(wfmt, wd, sd, I, h, I - 1 - i) * act[i];"),
-    "mx_bias": ("sc[r * (cols / 32) + c / 32] - 127", "sc[r * (cols / 32) + c / 32] - 128"),
+    "down_index": ("s += rg[i] * act[i];", "s += rg[I - 1 - i] * act[i];"),
+    "mx_bias": ("sc[r * (cols / 32) + c0 / 32] - 127", "sc[r * (cols / 32) + c0 / 32] - 128"),
     "e2m1_subnormal": ("0.5 * man", "1.0 * man"),
-    "dropped_term": ("g += weight_at(wfmt, wg, sg, H, i, h) * x[h];",
-                     "g += (h ? weight_at(wfmt, wg, sg, H, i, h) * x[h] : 0.0);"),
-    "mx_block_row": ("sc[r * (cols / 32) + c / 32]", "sc[(r / 2) * (cols / 32) + c / 32]"),
+    "dropped_term": ("g += rg[h] * x[h];", "g += (h ? rg[h] * x[h] : 0.0);"),
+    "mx_block_row": ("sc[r * (cols / 32) + c0 / 32]", "sc[(r / 2) * (cols / 32) + c0 / 32]"),
+    "mx_code_sign": ("val[code] = e2m1_value(code);", "val[code] = e2m1_value(code & 7u);"),
 }
 
 
