@@ -57,7 +57,7 @@ EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec
            "ec_set_bandwidth", "moe_route", "expert_cache_step", "moe_decode_layer", "moe_prefill_layer",
            "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
            "ec_kernel_timing", "ec_kernel_time", "ec_calibrate_bandwidth", "moe_gate_logits",
-           "moe_decode_block", "ec_bank_write", "ec_bank_read", "ec_last_step"]
+           "moe_decode_block", "ec_bank_write", "ec_bank_read", "ec_last_step", "ec_rebuild_slots"]
 KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
@@ -86,6 +86,7 @@ def lib():
         L.moe_prefill_layer.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]
         L.ec_set_prefill_overlap.argtypes = [c_vp, c_i32]
         L.cache_rebuild.argtypes = [c_vp, c_i32, c_vp, c_u64]
+        L.ec_rebuild_slots.argtypes = [c_vp, c_i32, P(c_i32), P(c_u64)]
         L.ec_epoch.restype = c_u64
         L.ec_epoch.argtypes = [c_vp]
         L.ec_get_stats.argtypes = [c_vp, P(ec_stats), c_i32]
@@ -276,11 +277,16 @@ class Context:
     def set_prefill_overlap(self, on):
         check(lib().ec_set_prefill_overlap(self.handle, 1 if on else 0), self.handle)
 
+    def rebuild_slots(self, budget_bp):
+        """(C, slot-pool bytes) that cache_rebuild chooses for budget_bp (ec_rebuild_slots)."""
+        C, need = c_i32(), c_u64()
+        check(lib().ec_rebuild_slots(self.handle, budget_bp, ctypes.byref(C), ctypes.byref(need)), self.handle)
+        return C.value, need.value
+
     def rebuild(self, budget_bp, new_slot_pool=None):
+        """cache_rebuild; returns the slot count the library chose (read back from its stats)."""
         import torch
-        L, E = self.shape.layers, self.shape.experts
-        C = (budget_bp * L * E) // 10000
-        need = C * self.layout.expert_bytes
+        _, need = self.rebuild_slots(budget_bp)
         if new_slot_pool is None:
             if self.slot_pool.numel() >= need:
                 new_slot_pool = self.slot_pool
@@ -289,7 +295,7 @@ class Context:
         check(lib().cache_rebuild(self.handle, budget_bp, new_slot_pool.data_ptr(), new_slot_pool.numel()),
               self.handle)
         self.slot_pool = new_slot_pool
-        return C
+        return self.stats()["slots"]
 
     def kernel_timing(self, on):
         check(lib().ec_kernel_timing(self.handle, 1 if on else 0), self.handle)
@@ -304,18 +310,21 @@ class Context:
     def epoch(self):
         return lib().ec_epoch(self.handle)
 
-    def stats(self, reset=False):
+    def stats(self, reset=False, allow_bad_ids=False):
+        """Totals since creation (or the last reset). Raises ECError on a device error (a host-branch
+        timeout, or a host-side pair in a step without the host branch), except that with
+        allow_bad_ids the bad-expert-id bit alone is returned in device_error."""
         s = ec_stats()
         st = lib().ec_get_stats(self.handle, ctypes.byref(s), 1 if reset else 0)
         out = {f: getattr(s, f) for f, _ in ec_stats._fields_}
-        if st != 0 and st != -7:
+        if st != 0 and not (st == -7 and allow_bad_ids and out["device_error"] == 1):
             check(st, self.handle)
         return out
 
     def debug_state(self):
         import numpy as np
         LE = self.shape.layers * self.shape.experts
-        C = self.stats()["slots"]
+        C = self.stats(allow_bad_ids=True)["slots"]
         resid = np.empty(LE, np.int32)
         sk = np.empty(max(C, 1), np.int32)
         lru = np.empty(max(C, 1), np.uint64)

@@ -622,12 +622,13 @@ ec_status moe_prefill_layer(ec_ctx* x, int32_t layer, const void* xin, const flo
 
 ec_status cache_rebuild(ec_ctx* x, int32_t budget_bp, void* new_slot_pool, uint64_t bytes) {
     if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
-    if (budget_bp < 0 || budget_bp > 10000) return fail(x, EC_EINVAL, "budget_bp must be in [0, 10000]");
-    const int64_t C = ((int64_t)budget_bp * x->L * x->E) / 10000;
-    if ((uint64_t)C * x->lay.expert_bytes > bytes || (C > 0 && !new_slot_pool))
+    int32_t C = 0;
+    uint64_t need = 0;
+    if (ec_rebuild_slots(x, budget_bp, &C, &need)) return fail(x, EC_EINVAL, "budget_bp must be in [0, 10000]");
+    if (need > bytes || (C > 0 && !new_slot_pool))
         return fail(x, EC_ENOSPC, "new slot pool smaller than C * expert_bytes");
     HIPCHK(x, hipDeviceSynchronize()); // safe point: nothing of this context in flight
-    x->C = (int)C;
+    x->C = C;
     x->slot_pool = (uint8_t*)new_slot_pool;
     x->slot_pool_bytes = bytes;
     launch_reset_cache(x->st, x->L, x->E, x->C, x->side);
@@ -782,7 +783,19 @@ ec_status ec_get_stats(ec_ctx* x, ec_stats* o, int32_t reset) {
         HIPCHK(x, hipStreamSynchronize(x->side));
     }
     if (err & 2) return fail(x, EC_EDEVICE, "the host branch did not deliver its partial sums in time");
+    if (err & 4)
+        return fail(x, EC_EDEVICE, "a host-side expert reached a step compiled without the host branch "
+                                   "(a graph replayed after the epoch changed)");
     return err ? fail(x, EC_EDEVICE, "an expert id outside [0, E) was passed to expert_cache_step") : EC_OK;
+}
+
+ec_status ec_rebuild_slots(const ec_ctx* x, int32_t budget_bp, int32_t* slots, uint64_t* slot_pool_bytes) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    if (budget_bp < 0 || budget_bp > 10000) return fail(nullptr, EC_EINVAL, "budget_bp must be in [0, 10000]");
+    const int64_t C = ((int64_t)budget_bp * x->L * x->E) / 10000;
+    if (slots) *slots = (int32_t)C;
+    if (slot_pool_bytes) *slot_pool_bytes = (uint64_t)C * x->lay.expert_bytes;
+    return EC_OK;
 }
 
 ec_status ec_debug_state(ec_ctx* x, int32_t* resid, int32_t* slot_key, uint64_t* slot_lru, uint64_t* clock) {

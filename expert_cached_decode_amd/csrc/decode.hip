@@ -517,10 +517,12 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
             }
             uint4 wd[G][R][NCH];
             uint32_t sd[G][R][NCH];
-            // a spare slot of a partial group (jj >= ng) reads the dummy row like a host-side pair
+            // a spare slot of a partial group (jj >= ng) reads the dummy row like a host-side pair;
+            // so does a negative id in the form without the host branch (a graph captured before the
+            // branch was switched on and replayed after): it is skipped and flagged, never addressed
 #pragma unroll
             for (int jj = 0; jj < G; ++jj) {
-                const bool hp = jj >= ng || (HOST && rw[jj] < 0);
+                const bool hp = jj >= ng || rw[jj] < 0;
                 const uint8_t* base = slots + (uint64_t)(hp ? 0 : rw[jj]) * expert_bytes;
                 const uint8_t* rowp = hp ? reinterpret_cast<const uint8_t*>(actp) : base + down_off;
                 const uint8_t* scp = hp ? reinterpret_cast<const uint8_t*>(actp) : base + dsc_off;
@@ -557,7 +559,7 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int jj = 0; jj < G; ++jj) {
-                const bool hp = jj >= ng || (HOST && rw[jj] < 0); // excluded by select below
+                const bool hp = jj >= ng || rw[jj] < 0; // excluded by select below
 #pragma unroll
                 for (int q = 0; q < NCH; ++q) {
                     const int c = lane + 64 * q;
@@ -587,6 +589,10 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
         float hs[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) hs[r] = 0.f;
+        if (!HOST) { // a host-side pair without the host branch: its term is missing, flag it
+            const bool stale = __ballot(lane < k && rw0 < 0) != 0ull; // whole wavefront votes
+            if (stale && blockIdx.x == 0 && tid == 0) atomicOr(a.err, 4);
+        }
         if (HOST) {
             if (nhost > 0) wait_host_branch(a.hseq, a.host_done, a.hseen, a.err);
             // lane j < k carries pair j's host-side term (zero for cache-side pairs)

@@ -32,9 +32,16 @@
  *     ec_destroy (or, for slot pools replaced by cache_rebuild, until the
  *     rebuild returns). The library allocates no device or pinned memory; the
  *     context owns host-heap state, HIP events and its host worker threads.
- *   - Asynchronous device-side errors (an expert id outside [0, E) passed to
- *     expert_cache_step) set a device flag reported as EC_EDEVICE by
- *     ec_get_stats; HIP runtime errors are EC_EHIP.
+ *   - Asynchronous device-side errors set bits of a device flag that
+ *     ec_get_stats reports (ec_stats.device_error) and turns into EC_EDEVICE:
+ *       bit 0: an expert id outside [0, E) reached the cache control (the step
+ *              is skipped);
+ *       bit 1: the host branch did not publish a step's partial sums within
+ *              the down GEMV's bounded wait (that step's output is wrong);
+ *       bit 2: a host-side pair reached a step launched without the host
+ *              branch, i.e. a graph captured before ec_epoch() changed was
+ *              replayed (the pair is skipped, the output is wrong).
+ *     No device error faults or hangs the GPU. HIP runtime errors are EC_EHIP.
  *   - One context is driven from one host thread at a time.
  *
  * Graph capture: moe_route, expert_cache_step, moe_decode_layer and
@@ -63,7 +70,7 @@ typedef int32_t ec_status;
 #define EC_EHIP (-4)    /* HIP runtime error */
 #define EC_ESTATE (-5)  /* call not valid in the current state */
 #define EC_EUNSUP (-6)  /* dtype or device not supported (needs gfx950) */
-#define EC_EDEVICE (-7) /* a device-side check failed (bad expert id) */
+#define EC_EDEVICE (-7) /* a device-side check failed (device error bits below) */
 
 /* expert weight dtypes */
 #define EC_DT_F32 0
@@ -130,7 +137,8 @@ typedef struct ec_step_view {
 
 typedef struct ec_stats {
     uint64_t steps, hits, misses, fills, host, evictions; /* totals over layers */
-    int32_t device_error; /* nonzero: a bad expert id was seen (EC_EDEVICE) */
+    int32_t device_error; /* device error bits (see Conventions): 1 bad expert id, 2 host-branch
+                             timeout, 4 host-side pair in a step without the host branch */
     int32_t slots;        /* current C */
     uint64_t clock;       /* LRU clock: expert_cache_step calls so far */
     int32_t host_only;    /* 1: the host pool is not device-accessible (see ec_create) */
@@ -287,6 +295,13 @@ ec_status ec_set_prefill_overlap(ec_ctx* ctx, int32_t on);
  *                   only when C = 0)
  * Bumps the epoch. */
 ec_status cache_rebuild(ec_ctx* ctx, int32_t budget_bp, void* new_slot_pool, uint64_t bytes);
+
+/* The slot count C = floor(budget_bp * L * E / 10000) that cache_rebuild
+ * would choose for budget_bp, and the slot-pool bytes it needs (C *
+ * expert_bytes), so that a caller can size the new pool; either output may be
+ * NULL. After a rebuild, ec_get_stats reports the C in use (ec_stats.slots).
+ * EC_EINVAL for a NULL ctx or a budget outside 0..10000. */
+ec_status ec_rebuild_slots(const ec_ctx* ctx, int32_t budget_bp, int32_t* slots, uint64_t* slot_pool_bytes);
 
 /* Expert-bank files ("Implementation notes": weights stored ahead of time in the
  * runtime's expert-bank layout are loaded without discovery or repacking, with

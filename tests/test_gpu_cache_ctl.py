@@ -203,7 +203,9 @@ def test_invalid_id_sets_device_error():
     ctx = make_ctx(sc, pool)
     bad = torch.tensor([[3, 99]], dtype=torch.int32, device="cuda")
     EC.expert_cache_step(ctx, 0, bad, 1)
-    st = ctx.stats()
+    with pytest.raises(EC.ECError):
+        ctx.stats()
+    st = ctx.stats(allow_bad_ids=True)
     assert st["device_error"] == 1 and st["steps"] == 0
     with pytest.raises(EC.ECError):
         EC.binding.check(EC.lib().ec_get_stats(ctx.handle, EC.binding.ctypes.byref(EC.binding.ec_stats()), 0),
