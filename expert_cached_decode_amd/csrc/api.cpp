@@ -778,6 +778,7 @@ ec_status ec_get_stats(ec_ctx* x, ec_stats* o, int32_t reset) {
     o->slots = x->C;
     o->clock = clk;
     o->host_only = x->host_only ? 1 : 0;
+    o->host_branch = x->host_branch ? 1 : 0;
     if (reset) {
         launch_fill_i32((int32_t*)x->st.stats, 0, 2ll * x->L * ST_N, x->side);
         HIPCHK(x, hipStreamSynchronize(x->side));

@@ -142,7 +142,9 @@ typedef struct ec_stats {
     int32_t slots;        /* current C */
     uint64_t clock;       /* LRU clock: expert_cache_step calls so far */
     int32_t host_only;    /* 1: the host pool is not device-accessible (see ec_create) */
-    int32_t reserved;
+    int32_t host_branch;  /* 1: decode steps are launched with the host branch (some step can
+                             have host-side experts: BP < BH, K or C below U_max, or host-only
+                             mode); 0: every routed expert is cache-side */
 } ec_stats;
 
 typedef struct ec_ctx ec_ctx;

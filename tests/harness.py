@@ -1,5 +1,8 @@
 """Test-side plumbing: build contexts over seeded expert banks, run the HIP path,
 run the oracle on the same inputs, compare. Inputs come from gen/ only."""
+from collections import OrderedDict
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 import gen
@@ -54,11 +57,47 @@ def make_ctx(cfg, pool, L=None, C=None, K=None, bp=None, bh=None, T=None, prefil
                       host_threads=threads, prefill_max_tokens=prefill, pool_layers=pool_layers)
 
 
+_EXPERTS = OrderedDict()  # (seed, dtype, H, I, sigma, layer, expert) -> logical matrices, LRU
+_EXPERT_CACHE_BYTES = 8 << 30
+
+
+def _nbytes(m):
+    return sum(sum(a.nbytes for a in v) if isinstance(v, tuple) else v.nbytes for v in m.values())
+
+
+def expert_mats(cfg, layer, e):
+    """Logical matrices of one expert from gen/, cached (the draws are pure functions of the key)."""
+    key = (cfg.seed, cfg.wdtype, cfg.H, cfg.I, cfg.sigma, layer, e)
+    m = _EXPERTS.get(key)
+    if m is None:
+        m = gen.expert_logical(cfg, layer, e)
+        _EXPERTS[key] = m
+        total = sum(_nbytes(v) for v in _EXPERTS.values())
+        while total > _EXPERT_CACHE_BYTES and len(_EXPERTS) > 1:
+            total -= _nbytes(_EXPERTS.popitem(last=False)[1])
+    else:
+        _EXPERTS.move_to_end(key)
+    return m
+
+
+def prefetch_experts(cfg, layer, experts, threads=8):
+    """Draw the given experts of a layer on host threads (gen's C calls release the GIL)."""
+    todo = [e for e in dict.fromkeys(int(e) for e in experts)
+            if (cfg.seed, cfg.wdtype, cfg.H, cfg.I, cfg.sigma, layer, e) not in _EXPERTS]
+    with ThreadPoolExecutor(threads) as ex:
+        mats = list(ex.map(lambda e: gen.expert_logical(cfg, layer, e), todo))
+    for e, m in zip(todo, mats):
+        _EXPERTS[(cfg.seed, cfg.wdtype, cfg.H, cfg.I, cfg.sigma, layer, e)] = m
+    total = sum(_nbytes(v) for v in _EXPERTS.values())
+    while total > _EXPERT_CACHE_BYTES and len(_EXPERTS) > 1:
+        total -= _nbytes(_EXPERTS.popitem(last=False)[1])
+
+
 def oracle_layer(cfg, layer, x, logits, layer_period=0, tokens=None):
     """fp64 oracle output rows for one layer: x [T,H] (bf16 bits or f32), logits [T,E]."""
     from oracle import moe
     src_layer = layer % layer_period if layer_period else layer
-    get = lambda e: gen.expert_logical(cfg, src_layer, e)
+    get = lambda e: expert_mats(cfg, src_layer, e)
     out, ids, w = moe.moe_tokens(cfg.wdtype, widen_x(cfg, x), logits, cfg.k, get, tokens=tokens)
     return out, ids, w
 

@@ -69,6 +69,7 @@ def run_trace(cfg, steps, p=None, T=None, C=None, K=None, bp=None, bh=None, rebu
         if s in rebuild:
             torch.cuda.synchronize()
             newC = ctx.rebuild(rebuild[s])
+            assert newC == budget_slots(cfg.L, cfg.E, rebuild[s])  # the library's C, the reading's formula
             sim.rebuild(newC)
         for l in range(cfg.L):
             if fused:
@@ -153,6 +154,15 @@ def test_budget_zero_and_tiny_caches():
     run_trace(TINY.with_(L=2), 40, C=0)
     run_trace(TINY.with_(L=2), 40, C=1, K=2, bp=1000, bh=1000)
     run_trace(TINY.with_(L=3, k=4), 40, T=3, C=5, K=64, bp=700, bh=1000)
+
+
+def test_slot_table_beyond_registers():
+    """C > 5120: the control kernel holds 5120 slot entries in registers and reads the rest of the
+    table from memory in the victim scan (also after a rebuild that grows the cache past it)."""
+    c = STRESS.with_(T=1, slots=6000)
+    run_trace(c, 40, T=1, K=64, bp=700, bh=1000)
+    run_trace(c, 40, T=1, K=64, bp=1000, bh=1000, fused=True, rebuild={8: 10000})
+    run_trace(STRESS, 8, T=16, C=8000, p=0.3)
 
 
 def test_max_pairs_and_wide_expert_table():

@@ -126,40 +126,43 @@ def test_gate_up_forms(wd, H, I, T):
     ctx.close()
 
 
-@pytest.mark.parametrize("split", [(300, 1000, 40), (1000, 1000, 40), (2000, 1000, 40), (300, 1000, 0),
-                                   (1000, 1000, 1024)])
-def test_output_independent_of_split_and_capacity(split):
-    """Same inputs, different BP:BH and cache sizes: outputs agree with the oracle (and so with each other)."""
+@pytest.mark.parametrize("wd,split", [(BF16, (300, 1000, 40)), (BF16, (1000, 1000, 40)), (BF16, (2000, 1000, 40)),
+                                      (BF16, (300, 1000, 0)), (BF16, (1000, 1000, 1024)),
+                                      (MXFP4, (1000, 1000, 24)), (MXFP4, (2000, 1000, 64)),
+                                      (MXFP4, (300, 1000, 24))])
+def test_output_independent_of_split_and_capacity(wd, split):
+    """Same inputs, different BP:BH and cache sizes: outputs agree with the oracle (and so with each
+    other). MXFP4 at BP >= BH runs without the host branch (its down GEMV form merges no host terms)."""
     bp, bh, C = split
-    cfg = QWEN_DECODE.with_(L=4, slots=C, bp=bp, bh=bh, K=8)
+    base = QWEN_DECODE if wd == BF16 else DSV4_DECODE.with_(H=1024, I=1024)
+    cfg = base.with_(L=4, slots=C, bp=bp, bh=bh, K=base.k)
     pool = make_pool(cfg)
     ctx = make_ctx(cfg, pool)
     outs, logits = run_decode(cfg, ctx, 12, 4, 1, lambda s, l: s in (0, 5, 11) and l in (0, 3))
     check_against_oracle(cfg, outs, 1e-2)
     st = ctx.stats()
-    ref = sim_counts(cfg, logits, 4, 1, C, 8, bp, bh)
+    assert st["host_branch"] == (0 if (bp >= bh and C >= cfg.k) else 1)
+    ref = sim_counts(cfg, logits, 4, 1, C, cfg.K, bp, bh)
     assert {k: st[k] for k in ref} == ref
     ctx.close()
 
 
 def test_mxfp4_host_split_ratios():
+    """Full DeepSeek-V4-Flash expert shapes (H 4096, I 2048, MXFP4) on three layers at BP:BH 300, 1000
+    and 2000 : 1000; the last two run without the host branch. Every kept output against the oracle."""
     cfg = DSV4_DECODE.with_(L=3, slots=192)
     pool = make_pool(cfg)
-    res = {}
     for bp in (300, 1000, 2000):
         ctx = make_ctx(cfg, pool, bp=bp, bh=1000)
         outs, logits = run_decode(cfg, ctx, 6, 3, 1, lambda s, l: s in (1, 5))
-        res[bp] = outs
         st = ctx.stats()
+        assert st["host_branch"] == (1 if bp < 1000 else 0)
         ref = sim_counts(cfg, logits, 3, 1, 192, cfg.K, bp, 1000)
         assert {k: st[k] for k in ref} == ref
         if bp == 300:
             assert ref["host"] > 0
         ctx.close()
-    check_against_oracle(cfg, res[300], 1e-2)
-    for bp in (1000, 2000):
-        for key in res[300]:
-            assert row_rel_err(res[bp][key][0], res[300][key][0]) <= 2e-2
+        check_against_oracle(cfg, outs, 1e-2)
 
 
 def test_batch16_mxfp4():
@@ -171,38 +174,6 @@ def test_batch16_mxfp4():
         toks = [0, 7, 15]
         ref, _, _ = oracle_layer(cfg, l, x, lg, tokens=toks)
         assert row_rel_err(got[toks], ref) <= 1e-2
-    ctx.close()
-
-
-@pytest.mark.slow
-def test_qwen_decode_full_size_sampled():
-    """The full bf16 workload (40 layers, 64.4 GB pinned expert bank, 3072 slots) on sampled outputs."""
-    cfg = QWEN_DECODE
-    pool = make_pool(cfg)
-    ctx = make_ctx(cfg, pool)
-    steps = 48
-    outs, logits = run_decode(cfg, ctx, steps, cfg.L, 1, lambda s, l: (s * 7 + l) % 97 == 0)
-    check_against_oracle(cfg, outs, 1e-2, max_checks=12)
-    st = ctx.stats()
-    ref = sim_counts(cfg, logits, cfg.L, 1, cfg.slots, cfg.K, cfg.bp, cfg.bh)
-    assert {k: st[k] for k in ref} == ref
-    ctx.close()
-
-
-def test_dsv4_decode_full_size_sampled():
-    """The full MXFP4 workload as the bench runs it: 43 layers, 2752 slots (25%), BP:BH 300:1000 (most
-    misses on the host branch), host pool of 16 layers (layer l reads pool layer l % 16, all drawn as
-    layer 0), sampled outputs against the oracle and every decision against the simulator."""
-    cfg = DSV4_DECODE
-    pool = make_pool(cfg, L=16, layer_period=1)
-    ctx = make_ctx(cfg, pool, pool_layers=16)
-    steps = 20
-    outs, logits = run_decode(cfg, ctx, steps, cfg.L, 1, lambda s, l: (s * 11 + l) % 89 == 0)
-    check_against_oracle(cfg, outs, 1e-2, layer_period=1, max_checks=8)
-    st = ctx.stats()
-    ref = sim_counts(cfg, logits, cfg.L, 1, cfg.slots, cfg.K, cfg.bp, cfg.bh)
-    assert {k: st[k] for k in ref} == ref
-    assert st["host"] > 0 and st["fills"] > 0
     ctx.close()
 
 
@@ -291,25 +262,6 @@ def test_calibration_in_host_only_mode_reports_no_link():
     del pageable
 
 
-def test_stress_decode_full_size_sampled():
-    """Stress shapes as the bench runs them: 43 MXFP4 layers, 4096 slots, K = 64, batch 16 (up to 96
-    unique experts a layer step, so misses beyond K go to the host branch), 16-layer host pool;
-    sampled token rows against the oracle and every decision against the simulator."""
-    cfg = STRESS
-    pool = make_pool(cfg, L=16, layer_period=1)
-    ctx = make_ctx(cfg, pool, pool_layers=16)
-    steps = 4
-    outs, logits = run_decode(cfg, ctx, steps, cfg.L, cfg.T, lambda s, l: (s, l) in ((1, 7), (3, 42)))
-    for (s, l), (got, x, lg) in sorted(outs.items()):
-        toks = [0, 9, 15]
-        ref, _, _ = oracle_layer(cfg, l, x, lg, layer_period=1, tokens=toks)
-        assert row_rel_err(got[toks], ref) <= 1e-2, (s, l)
-    st = ctx.stats()
-    ref = sim_counts(cfg, logits, cfg.L, cfg.T, cfg.slots, cfg.K, cfg.bp, cfg.bh)
-    assert {k: st[k] for k in ref} == ref
-    ctx.close()
-
-
 def test_decode_outputs_across_rebuilds():
     """cache_rebuild at safe points (40% -> 15% -> 40% of the experts, cold each time, clock going
     on): outputs keep matching the oracle and decisions the simulator rebuilt at the same steps."""
@@ -343,3 +295,29 @@ def test_decode_outputs_across_rebuilds():
     occ = sorted((int(k) for k in sk if k >= 0))
     assert occ == sorted(l * cfg.E + e for (l, e) in sim.resid.keys())
     ctx.close()
+
+
+def test_decode_from_a_bank_file(tmp_path):
+    """Fast start ("Elastic edge resource management", "Implementation notes"): the expert bank is
+    written as a bank file in its final layout, read back with parallel direct I/O into pinned
+    memory, and that memory serves as the host pool of a decode with fills and the host branch.
+    Outputs against the oracle (whose weights come from gen/, not from the file)."""
+    import expert_cached_decode_amd as EC
+    cfg = QWEN_DECODE.with_(L=3, E=64, slots=40, bp=500, bh=1000)
+    src = gen.pool_array(cfg)
+    shape = EC.make_shape(cfg.L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.wdtype)
+    path = str(tmp_path / "bank.ecb")
+    EC.bank_write(path, shape, cfg.L, src.ctypes.data, src.nbytes)
+    pinned = EC.PinnedBuffer(src.nbytes)
+    sec, mode = EC.bank_read(path, shape, cfg.L, pinned.ptr, pinned.nbytes, threads=8)
+    print("bank file of %.2f GB read in %.3f s (mode %d)" % (src.nbytes / 1e9, sec, mode))
+    del src
+    ctx = make_ctx(cfg, pinned)
+    outs, logits = run_decode(cfg, ctx, 8, cfg.L, 1, lambda s, l: True)
+    check_against_oracle(cfg, outs, 1e-2)
+    st = ctx.stats()
+    ref = sim_counts(cfg, logits, cfg.L, 1, cfg.slots, cfg.K, cfg.bp, cfg.bh)
+    assert {k: st[k] for k in ref} == ref
+    assert st["fills"] > 0 and st["host"] > 0
+    ctx.close()
+    pinned.close()
