@@ -142,6 +142,7 @@ class PinnedBuffer:
         p = c_vp()
         rc = self._hip.hipHostMalloc(ctypes.byref(p), max(int(nbytes), 1), 0)
         if rc != 0 or not p.value:
+            self._hip.hipGetLastError()  # the failure is reported here, not by a later HIP call
             raise MemoryError("hipHostMalloc(%d) failed with %d" % (nbytes, rc))
         self.ptr = p.value
         self.nbytes = int(nbytes)

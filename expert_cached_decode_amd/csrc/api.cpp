@@ -284,6 +284,7 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
     if (!out || !dev_ws || !pinned_ws || !host_pool) return fail(nullptr, EC_EINVAL, "NULL argument");
     if (((uintptr_t)dev_ws & 255) || ((uintptr_t)pinned_ws & 255))
         return fail(nullptr, EC_EINVAL, "workspaces must be 256-byte aligned");
+    (void)hipGetLastError(); // an error left by an earlier, unrelated HIP call is not this call's
     int dev = 0;
     hipDeviceProp_t prop;
     if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
