@@ -13,8 +13,8 @@
 // ranking pass over their candidates), bitmap dedup and prefix popcounts in LDS,
 // ballot/popcount block scans for the miss and cache-side lists, and the
 // victims from the slot table read once into registers (issued before the
-// routing, whose latency it then hides): q rounds of block-wide argmin over
-// the unique LRU keys.
+// routing, whose latency it then hides), selected in one pass whose cost does
+// not grow with the number of misses (select_victims).
 #include "ec_internal.h"
 
 namespace ec {
@@ -307,6 +307,191 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// ---------------------------------------------------------------------------
+// K-LRU victims in one pass over the slot table ("Implementation notes": one scan yields the K
+// least-recently-used candidates, whatever the number of misses). The victims are the q smallest
+// LRU keys of the untouched slots (keys are unique; excluded slots carry ~0). The block does not
+// take q rounds of a minimum; instead:
+//   1. every thread takes the minimum of its keys;
+//   2. the q-th smallest of those thread minima, mu, is found by sorting each wavefront's minima
+//      (a bitonic network across the lanes) and merging the sorted lists in one wavefront. Exactly
+//      q threads hold a key <= mu, so at least q keys are <= mu and every thread whose minimum is
+//      above mu holds none of them;
+//   3. the keys <= mu (the candidates: at most q times the keys per thread, usually little more
+//      than q) are collected in LDS, and each candidate's rank is the number of smaller
+//      candidates: rank r < q makes it victim r, oldest first.
+// The cost is a few block barriers and work proportional to the table and to the candidates, not
+// to q. Should the candidates not fit in LDS (only with slot tables beyond the registers), a
+// bisection over key values first narrows mu to the exact q-th smallest key.
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m), hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// One key per lane sorted ascending in lane order (bitonic network, 21 compare-exchange steps).
+__device__ __forceinline__ uint64_t wave_sort_u64(uint64_t v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t o = shfl_xor_u64(v, j);
+            const bool keep_min = ((lane & j) == 0) == ((lane & k) == 0);
+            v = keep_min ? (o < v ? o : v) : (o > v ? o : v);
+        }
+    return v;
+}
+
+// The 64 smallest of two ascending lane-ordered lists, ascending: the elementwise minimum of a and
+// b reversed is bitonic and holds exactly them; one bitonic merge sorts it.
+__device__ __forceinline__ uint64_t merge_lower64(uint64_t a, uint64_t b) {
+    const int lane = lane_id();
+    const uint32_t blo = (uint32_t)__shfl((int)(uint32_t)b, 63 - lane), bhi = (uint32_t)__shfl((int)(uint32_t)(b >> 32), 63 - lane);
+    const uint64_t br = ((uint64_t)bhi << 32) | blo;
+    uint64_t v = a < br ? a : br;
+#pragma unroll
+    for (int j = 32; j > 0; j >>= 1) {
+        const uint64_t o = shfl_xor_u64(v, j);
+        v = (lane & j) == 0 ? (o < v ? o : v) : (o > v ? o : v);
+    }
+    return v;
+}
+
+// LDS of the victim selection (kept in the kernel's static shared memory). With SR register keys per
+// thread, at most q * SR <= 64 * SR keys are candidates (see above).
+template <int NT, int SR>
+struct VictimLds {
+    static constexpr int kCand = 64 * SR;
+    uint64_t sel[NT / 64][64]; // each wavefront's sorted thread minima
+    uint64_t key[kCand];
+    int32_t slot[kCand];
+    int32_t occ[kCand];
+    uint64_t mu;
+    int32_t ncand;
+    int32_t part[NT / 64];
+};
+
+// Slot keys beyond the registers (tables larger than NT * SR): slot s with its exclusion applied.
+struct MemSlots {
+    const uint64_t* lru;
+    const int32_t* key;
+    const uint32_t* hit_bits; // LDS bitmap of the layer's experts hit in this step
+    int layer, E, first;      // slots [first, C) are read from memory
+};
+
+__device__ __forceinline__ uint64_t excluded_slot(uint64_t key, int occ, int s, int C, int l, int E,
+                                                  const uint32_t* hit_bits);
+
+__device__ __forceinline__ uint64_t mem_key(const MemSlots& m, int s, int& occ) {
+    occ = m.key[s];
+    return excluded_slot(m.lru[s], occ, 0, 1, m.layer, m.E, m.hit_bits);
+}
+
+// The LRU key of slot s as a victim candidate: ~0 (never chosen) when s is past C or its occupant
+// (key l * E + e) is an expert of this layer routed in this step (bit e of hit_bits). Written
+// without branches: the LDS read is always made (index clamped) and the key selected.
+__device__ __forceinline__ uint64_t excluded_slot(uint64_t key, int occ, int s, int C, int l, int E,
+                                                  const uint32_t* hit_bits) {
+    const uint32_t e = (uint32_t)(occ - l * E);
+    const uint32_t ec = e < (uint32_t)E ? e : 0u;
+    const bool hit = e < (uint32_t)E && ((hit_bits[ec >> 5] >> (ec & 31)) & 1u);
+    return (s >= C || hit) ? ~0ull : key;
+}
+
+// Victims 0..q-1 into vslot / vocc (LDS), oldest first. pk / po: the thread's SR register keys
+// (slot tid + NT p; excluded ones ~0) and occupants; mem: slots from mem.first on, when C is larger.
+// Called by all NT threads with the same q >= 1 (at most 64); ends with a block barrier.
+template <int NT, int SR, bool MEM>
+__device__ void select_victims(const uint64_t (&pk)[SR], const int (&po)[SR], int q, int C, const MemSlots& mem,
+                               VictimLds<NT, SR>& L, int32_t* vslot, int32_t* vocc) {
+    constexpr int kW = NT / 64;
+    constexpr int kVictimCand = VictimLds<NT, SR>::kCand;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    // 1. the thread's minimum key
+    uint64_t tmin = ~0ull;
+#pragma unroll
+    for (int p = 0; p < SR; ++p) tmin = pk[p] < tmin ? pk[p] : tmin;
+    if constexpr (MEM) {
+        for (int s = mem.first + tid; s < C; s += NT) {
+            int occ;
+            const uint64_t k = mem_key(mem, s, occ);
+            tmin = k < tmin ? k : tmin;
+        }
+    }
+    // 2. mu = the q-th smallest thread minimum
+    L.sel[wave][lane] = wave_sort_u64(tmin);
+    __syncthreads();
+    if (wave == 0) {
+        uint64_t best = L.sel[0][lane];
+#pragma unroll
+        for (int w2 = 1; w2 < kW; ++w2) best = merge_lower64(best, L.sel[w2][lane]);
+        const uint32_t mlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, q - 1);
+        const uint32_t mhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(best >> 32), q - 1);
+        if (lane == 0) { L.mu = ((uint64_t)mhi << 32) | mlo; L.ncand = 0; }
+    }
+    __syncthreads();
+    uint64_t mu = L.mu;
+    // 3. candidates (keys <= mu, never an excluded one) in LDS; ranks among them
+    auto count_le = [&](uint64_t x) { // block-wide number of keys <= x (excluded keys never count)
+        int c = 0;
+#pragma unroll
+        for (int p = 0; p < SR; ++p) c += (pk[p] <= x && pk[p] != ~0ull) ? 1 : 0;
+        if constexpr (MEM) {
+            for (int s = mem.first + tid; s < C; s += NT) {
+                int occ;
+                const uint64_t k = mem_key(mem, s, occ);
+                c += (k <= x && k != ~0ull) ? 1 : 0;
+            }
+        }
+        c = (int)wave_sum_f((float)c); // exact: counts stay far below 2^24
+        __syncthreads();
+        if (lane == 0) L.part[wave] = c;
+        __syncthreads();
+        int tot = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < kW; ++w2) tot += L.part[w2];
+        return tot;
+    };
+    if constexpr (MEM) {
+        // candidates that would not fit: bisect to the exact q-th smallest key (count == q)
+        if (count_le(mu) > kVictimCand) {
+            uint64_t lo = 0, hi = mu; // count_le(hi) >= q
+            while (lo < hi) {
+                const uint64_t mid = lo + (hi - lo) / 2;
+                if (count_le(mid) >= q) hi = mid; else lo = mid + 1;
+            }
+            mu = lo;
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < SR; ++p) {
+        if (pk[p] <= mu && pk[p] != ~0ull) {
+            const int i = atomicAdd(&L.ncand, 1);
+            if (i < kVictimCand) { L.key[i] = pk[p]; L.slot[i] = tid + NT * p; L.occ[i] = po[p]; }
+        }
+    }
+    if constexpr (MEM) {
+        for (int s = mem.first + tid; s < C; s += NT) {
+            int occ;
+            const uint64_t k = mem_key(mem, s, occ);
+            if (k <= mu && k != ~0ull) {
+                const int i = atomicAdd(&L.ncand, 1);
+                if (i < kVictimCand) { L.key[i] = k; L.slot[i] = s; L.occ[i] = occ; }
+            }
+        }
+    }
+    __syncthreads();
+    const int nc = min(L.ncand, kVictimCand);
+    for (int i = tid; i < nc; i += NT) {
+        const uint64_t k = L.key[i];
+        int r = 0;
+        for (int j = 0; j < nc; ++j) r += L.key[j] < k ? 1 : 0;
+        if (r < q) { vslot[r] = L.slot[i]; vocc[r] = L.occ[i]; }
+    }
+    __syncthreads();
+}
+
 // Exclusive block scan of a flag (ballot + popcount; NT threads).
 template <int NT>
 __device__ int block_scan_flag(bool f, int* s_wtot, int* total) {
@@ -390,7 +575,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(const float* logits, const int3
     __shared__ int32_t s_off[kMaxPairs + 1];
     __shared__ int32_t s_first[kMaxPairs];
     __shared__ int32_t s_g[kMaxPairs];
-    __shared__ uint64_t s_wmin[2][kCtlWaves];
+    __shared__ VictimLds<NT, kSlotRegs> s_vl;
     __shared__ int32_t s_vslot[kMaxK];
     __shared__ int32_t s_vocc[kMaxK];
     __shared__ int32_t s_wtot[2 * kCtlWaves];
@@ -573,49 +758,15 @@ __global__ __launch_bounds__(NT) void ctl_kernel(const float* logits, const int3
     qq = min(qq, (int64_t)(C - h));
     const int q = qq > 0 ? (int)qq : 0;
 
-    // 5. victims: the q oldest slots not hit in this step (empty slots first, in slot
-    //    order), selected from the slot table read once above: q rounds of block-wide
-    //    argmin over the unique LRU keys (each round takes the smallest key above the
-    //    previous one), the owner of each minimum records its slot and occupant.
+    // 5. victims: the q oldest slots not hit in this step (empty slots first, in slot order),
+    //    in one pass over the slot table read above (select_victims); slots past C and slots
+    //    hit in this step are not candidates
     if (q > 0) {
 #pragma unroll
-        for (int p = 0; p < kSlotRegs; ++p) { // slots past C and slots hit in this step are not candidates
-            const uint32_t e = (uint32_t)(po[p] - l * E); // occupant in this layer?
-            const bool past = tid + kCtlThreads * p >= C;
-            if (past || (e < (uint32_t)E && ((s_bits[e >> 5] >> (e & 31)) & 1u))) pk[p] = ~0ull;
-        }
-        // each thread's smallest key (above lo), kept across rounds: only the owner of a
-        // round's minimum has to look again
-        auto local_min = [&](uint64_t lo, uint64_t& mine, int& ms, int& mo) {
-            mine = ~0ull; ms = -1; mo = -1;
-#pragma unroll
-            for (int p = 0; p < kSlotRegs; ++p)
-                if (pk[p] >= lo && pk[p] < mine) { mine = pk[p]; ms = tid + kCtlThreads * p; mo = po[p]; }
-            for (int s = tid + kCtlThreads * kSlotRegs; s < C; s += kCtlThreads) { // tables beyond the registers
-                uint64_t key = slot_lru[s];
-                const int occ = slot_key[s];
-                const uint32_t e = (uint32_t)(occ - l * E);
-                if (e < (uint32_t)E && ((s_bits[e >> 5] >> (e & 31)) & 1u)) key = ~0ull;
-                if (key >= lo && key < mine) { mine = key; ms = s; mo = occ; }
-            }
-        };
-        uint64_t mine;
-        int ms, mo;
-        local_min(0, mine, ms, mo);
-        for (int rr = 0; rr < q; ++rr) {
-            const uint64_t wm = wave_min_u64(mine);
-            if (lane == 0) s_wmin[rr & 1][wave] = wm;
-            __syncthreads();
-            uint64_t gm = ~0ull;
-#pragma unroll
-            for (int w2 = 0; w2 < kCtlWaves; ++w2) gm = s_wmin[rr & 1][w2] < gm ? s_wmin[rr & 1][w2] : gm;
-            if (mine == gm) { // keys are unique: one owner
-                s_vslot[rr] = ms;
-                s_vocc[rr] = mo;
-                local_min(gm + 1, mine, ms, mo);
-            }
-        }
-        __syncthreads();
+        for (int p = 0; p < kSlotRegs; ++p) pk[p] = excluded_slot(pk[p], po[p], tid + kCtlThreads * p, C, l, E, s_bits);
+        const MemSlots mem{slot_lru, slot_key, s_bits, l, E, kCtlThreads * kSlotRegs};
+        if (C > kCtlThreads * kSlotRegs) select_victims<NT, kSlotRegs, true>(pk, po, q, C, mem, s_vl, s_vslot, s_vocc);
+        else select_victims<NT, kSlotRegs, false>(pk, po, q, C, mem, s_vl, s_vslot, s_vocc);
     }
     if (tid < a.K) a.sb.victims[tid] = tid < q ? s_vslot[tid] : -1;
     if (tid < a.K && tid >= q) { a.sb.fills[tid] = -1; a.sb.evicted[tid] = -1; }
@@ -753,7 +904,7 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
     __shared__ int32_t s_ci[64];
     __shared__ int32_t s_res[256];
     __shared__ uint32_t s_bits[8];
-    __shared__ uint64_t s_wmin[2][kWaves];
+    __shared__ VictimLds<NT, kSlotRegs> s_vl;
     __shared__ int32_t s_vslot[kMaxK];
     __shared__ int32_t s_vocc[kMaxK];
     __shared__ int32_t s_q;
@@ -859,37 +1010,12 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
     __syncthreads();
     const int q = s_q;
 
-    // 5. victims: q rounds of block-wide argmin over the unique LRU keys of the untouched slots
+    // 5. victims in one pass over the slot table held in registers (select_victims)
     if (q > 0) {
 #pragma unroll
-        for (int p = 0; p < kSlotRegs; ++p) { // slots past C and slots hit in this step are not candidates
-            const uint32_t e = (uint32_t)(po[p] - l * E);
-            const bool past = tid + NT * p >= C;
-            if (past || (e < (uint32_t)E && ((s_bits[e >> 5] >> (e & 31)) & 1u))) pk[p] = ~0ull;
-        }
-        auto local_min = [&](uint64_t lo, uint64_t& mine, int& ms, int& mo) {
-            mine = ~0ull; ms = -1; mo = -1;
-#pragma unroll
-            for (int p = 0; p < kSlotRegs; ++p)
-                if (pk[p] >= lo && pk[p] < mine) { mine = pk[p]; ms = tid + NT * p; mo = po[p]; }
-        };
-        uint64_t mine;
-        int ms, mo;
-        local_min(0, mine, ms, mo);
-        for (int rr = 0; rr < q; ++rr) {
-            const uint64_t wm = wave_min_u64(mine);
-            if (lane == 0) s_wmin[rr & 1][wave] = wm;
-            __syncthreads();
-            uint64_t gm = ~0ull;
-#pragma unroll
-            for (int w2 = 0; w2 < kWaves; ++w2) gm = s_wmin[rr & 1][w2] < gm ? s_wmin[rr & 1][w2] : gm;
-            if (mine == gm) { // keys are unique: one owner
-                s_vslot[rr] = ms;
-                s_vocc[rr] = mo;
-                local_min(gm + 1, mine, ms, mo);
-            }
-        }
-        __syncthreads();
+        for (int p = 0; p < kSlotRegs; ++p) pk[p] = excluded_slot(pk[p], po[p], tid + NT * p, C, l, E, s_bits);
+        const MemSlots none{nullptr, nullptr, nullptr, 0, 0, C};
+        select_victims<NT, kSlotRegs, false>(pk, po, q, C, none, s_vl, s_vslot, s_vocc);
     }
     if (wave != 0) return;
 

@@ -409,7 +409,7 @@ __device__ __noinline__ void wait_host_branch(const uint32_t* hseq, const uint32
                                               int32_t* err) {
     if (threadIdx.x == 0) {
         const uint32_t want = *hseq;
-        const bool relay = blockIdx.x == 0 && blockIdx.y == 0;
+        const bool relay = blockIdx.x == 0;
         const uint32_t* flag = relay ? host_done : hseen;
         uint32_t it = 0;
         while (relay ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != want
@@ -428,7 +428,7 @@ __device__ __noinline__ void wait_host_branch(const uint32_t* hseq, const uint32
 
 // ---------------------------------------------------------------------------
 // Down GEMV + exact merge. A block of four wavefronts owns 4 R output rows h of
-// one token t (grid: H / (4 R) x T). For each group of G of the token's pairs,
+// one token t (grid: H / (4 R) * T blocks, mapped to (rows, token) below). For each group of G of the token's pairs,
 // the block first issues
 // the loads of its weight rows W_down,e(t,j)[h] (the group's indices come from
 // one vector load), then the group's activation vectors act[t,j]: staged in
@@ -450,13 +450,19 @@ __device__ __noinline__ void wait_host_branch(const uint32_t* hseq, const uint32
 template <int WDT, int NCH, int R, int G, bool HOST, bool FULL, bool STAGE>
 __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, const float* wts, const void* actp,
                                                    const uint8_t* slots, uint64_t expert_bytes, int H, int I, int k,
-                                                   DecodeArgs a) {
+                                                   int T, DecodeArgs a) {
     constexpr int EPC = Fmt<WDT>::EPC;
     constexpr int AB = WDT == EC_DT_F32 ? 4 : 2; // bytes per activation element
     constexpr int QB = EPC * AB / 16;            // 16-byte quads per chunk
     extern __shared__ uint4 s_q[];               // [G][I * AB / 16]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int row0 = (blockIdx.x * 4 + wave) * R;
+    // Linear block b -> (row block bx, token t). Workgroups are dealt to the eight XCDs in turn
+    // (b mod 8); the row blocks of one XCD take all T tokens in consecutive turns, so the weight
+    // rows an expert shared by several tokens streams are read from HBM once and then served by
+    // that XCD's L2. With one token bx = b. (H / (4 R) is a multiple of 8.)
+    const int bs = blockIdx.x >> 3;
+    const int bx = 8 * (bs / T) + (blockIdx.x & 7), t = bs - (bs / T) * T;
+    const int row0 = (bx * 4 + wave) * R;
     const int IQ = I * AB / 16;
     const int rbi = row_bytes<WDT>(I), n16 = rbi >> 4;
     const uint64_t down_off = 2ull * I * row_bytes<WDT>(H) + (uint64_t)row0 * rbi;
@@ -465,7 +471,6 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
     // issued first: whether the step has host-side pairs (read again only in the epilogue)
     const int nhost = HOST ? a.counts[CNT_HOST] : 0;
     {
-        const int t = blockIdx.y; // one token per grid row: tokens run in parallel
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -591,7 +596,7 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
         for (int r = 0; r < R; ++r) hs[r] = 0.f;
         if (!HOST) { // a host-side pair without the host branch: its term is missing, flag it
             const bool stale = __ballot(lane < k && rw0 < 0) != 0ull; // whole wavefront votes
-            if (stale && blockIdx.x == 0 && tid == 0) atomicOr(a.err, 4);
+            if (stale && bx == 0 && tid == 0) atomicOr(a.err, 4);
         }
         if (HOST) {
             if (nhost > 0) wait_host_branch(a.hseq, a.host_done, a.hseen, a.err);
@@ -756,10 +761,10 @@ void launch_gu(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev) {
 
 template <int WDT, int NCH, int R, int G, bool STAGE>
 static void down_go2(const DecodeArgs& a, bool full, hipStream_t s) {
-    const dim3 blk(256), grid(a.H / (4 * R), a.T);
+    const dim3 blk(256), grid(a.H / (4 * R) * a.T);
     const size_t lds = STAGE ? (size_t)G * a.I * (WDT == EC_DT_F32 ? 4 : 2) : 0;
 #define EC_D1(HOST, FULL) EC_LAUNCH((down_kernel<WDT, NCH, R, G, HOST, FULL, STAGE>), grid, blk, lds, s, a.rewritten, \
-                                  a.w, (const void*)a.act, (const uint8_t*)a.slots, a.expert_bytes, a.H, a.I, a.k, a)
+                                  a.w, (const void*)a.act, (const uint8_t*)a.slots, a.expert_bytes, a.H, a.I, a.k, a.T, a)
     if constexpr (WDT != EC_DT_F32) { // f32 (small test shapes) only takes the guarded form
         if (full) {
             if (a.host_pairs) EC_D1(true, true); else EC_D1(false, true);
