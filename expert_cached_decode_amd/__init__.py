@@ -6,4 +6,5 @@ package is its Python binding.
 from .binding import (EC_DT_BF16, EC_DT_F32, EC_DT_MXFP4, Context, ECError, PinnedBuffer,  # noqa: F401
                       bank_read, bank_write, cache_rebuild, expert_cache_step, last_step, layout, lib, make_shape,
                       moe_decode_block,
-                      moe_decode_layer, moe_gate_logits, moe_prefill_layer, moe_route, workspace_size)
+                      moe_decode_layer, moe_decode_layer_static, moe_gate_logits, moe_prefill_layer, moe_route,
+                      workspace_size)

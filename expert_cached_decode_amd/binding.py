@@ -57,7 +57,8 @@ EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec
            "ec_set_bandwidth", "moe_route", "expert_cache_step", "moe_decode_layer", "moe_prefill_layer",
            "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
            "ec_kernel_timing", "ec_kernel_time", "ec_calibrate_bandwidth", "moe_gate_logits",
-           "moe_decode_block", "ec_bank_write", "ec_bank_read", "ec_last_step", "ec_rebuild_slots"]
+           "moe_decode_block", "ec_bank_write", "ec_bank_read", "ec_last_step", "ec_rebuild_slots",
+           "moe_decode_layer_static"]
 KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
@@ -83,6 +84,7 @@ def lib():
         L.expert_cache_step.argtypes = [c_vp, c_i32, c_vp, c_i32, P(ec_step_view), c_vp]
         L.ec_last_step.argtypes = [c_vp, P(ec_step_view)]
         L.moe_decode_layer.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]
+        L.moe_decode_layer_static.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]
         L.moe_prefill_layer.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]
         L.ec_set_prefill_overlap.argtypes = [c_vp, c_i32]
         L.cache_rebuild.argtypes = [c_vp, c_i32, c_vp, c_u64]
@@ -196,6 +198,12 @@ def last_step(ctx):
 
 def moe_decode_layer(ctx, layer, x, logits, T, out, stream=None):
     check(lib().moe_decode_layer(ctx.handle, layer, _ptr(x), _ptr(logits), T, _ptr(out), _stream(stream)),
+          ctx.handle)
+
+
+def moe_decode_layer_static(ctx, layer, x, logits, T, out, stream=None):
+    """moe_decode_layer with the step buffers in the library's static device scratch (allocates nothing)."""
+    check(lib().moe_decode_layer_static(ctx.handle, layer, _ptr(x), _ptr(logits), T, _ptr(out), _stream(stream)),
           ctx.handle)
 
 

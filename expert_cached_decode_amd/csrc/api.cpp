@@ -47,6 +47,14 @@ struct ec_ctx {
     DevState st{};
     StepBufs sb{};
     float* act = nullptr;
+    // moe_decode_layer_static: the same step buffers laid over the library's static device scratch
+    int device = 0;
+    void* static_base = nullptr;  // device address of the scratch array on this context's device
+    uint64_t static_bytes = 0;    // bytes of it this context's step buffers take
+    std::string static_err;       // why the static variant is unavailable (empty when it is)
+    StepBufs static_sb{};
+    float* static_act = nullptr;
+    StepBufs last_sb{};           // the buffers of the last step call (ec_last_step)
     float* gate_logits = nullptr; // [T_max][E] router logits of moe_decode_block
     // host branch: pinned mailbox, partial sums and doorbell, with their device-visible addresses
     int32_t* mb_pinned = nullptr;
@@ -197,6 +205,26 @@ static ec_status check_config(const ec_config* c) {
     return EC_OK;
 }
 
+// The per-step buffers of a decode step (route, cache control, GEMV activations), carved from d.
+static void carve_step(const ec_ctx* x, Carve& d, StepBufs& sb, float*& act) {
+    const int n = x->nmax, U = x->Umax;
+    sb.ids = d.take<int32_t>(n);
+    sb.w = d.take<float>(n);
+    sb.uniq = d.take<int32_t>(U);
+    sb.counts = d.take<int32_t>(CNT_N);
+    sb.pos = d.take<int32_t>(n);
+    sb.cls = d.take<int32_t>(U);
+    sb.slot = d.take<int32_t>(U);
+    sb.fills = d.take<int32_t>(kMaxK);
+    sb.victims = d.take<int32_t>(kMaxK);
+    sb.evicted = d.take<int32_t>(kMaxK);
+    sb.host_list = d.take<int32_t>(U);
+    sb.rewritten = d.take<int32_t>(n);
+    sb.gpu_desc = d.take<int4>(U);
+    sb.tok_pairs = d.take<int32_t>(n);
+    act = d.take<float>((uint64_t)n * x->I);
+}
+
 // Carve the device and pinned workspaces (base pointers may be NULL for sizing).
 static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, uint64_t* pin_bytes) {
     const int LE = x->L * x->E;
@@ -215,25 +243,11 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     x->st.stats = words ? reinterpret_cast<unsigned long long*>(words + 4) : nullptr;
     x->st.err = d.take<int32_t>(1);
     x->probe_sink = d.take<uint32_t>(4);
-    const int n = x->nmax, U = x->Umax;
-    x->sb.ids = d.take<int32_t>(n);
-    x->sb.w = d.take<float>(n);
-    x->sb.uniq = d.take<int32_t>(U);
-    x->sb.counts = d.take<int32_t>(CNT_N);
-    x->sb.pos = d.take<int32_t>(n);
-    x->sb.cls = d.take<int32_t>(U);
-    x->sb.slot = d.take<int32_t>(U);
-    x->sb.fills = d.take<int32_t>(kMaxK);
-    x->sb.victims = d.take<int32_t>(kMaxK);
-    x->sb.evicted = d.take<int32_t>(kMaxK);
-    x->sb.host_list = d.take<int32_t>(U);
-    x->sb.rewritten = d.take<int32_t>(n);
-    x->sb.gpu_desc = d.take<int4>(U);
-    x->sb.tok_pairs = d.take<int32_t>(n);
+    const int n = x->nmax;
+    carve_step(x, d, x->sb, x->act);
     x->gate_logits = d.take<float>((uint64_t)x->Tmax * x->E);
     const uint64_t xbytes = (uint64_t)x->Tmax * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
     const uint64_t mb_bytes = mailbox_ints(n) * 4 + xbytes;
-    x->act = d.take<float>((uint64_t)n * x->I);
     prefill_carve(x->pf, d, x->cfg.prefill_max_tokens, x->E, x->k, x->H, x->I, x->lay.layer_bytes);
     *dev_bytes = (d.off + 255) & ~255ull;
     Carve p(pin);
@@ -308,6 +322,29 @@ ec_status ec_create(const ec_config* c, void* dev_ws, uint64_t dev_ws_bytes, voi
         return fail(nullptr, EC_ENOSPC, "slot pool smaller than cache_slots * expert_bytes");
     }
     carve(x, (uint8_t*)dev_ws, (uint8_t*)pinned_ws, &need_dev, &need_pin);
+    x->last_sb = x->sb;
+    x->device = dev;
+    {
+        // the static variant's step buffers: the same layout over the library's device scratch
+        Carve sz(nullptr);
+        StepBufs tmp{};
+        float* tmp_act = nullptr;
+        carve_step(x, sz, tmp, tmp_act);
+        x->static_bytes = (sz.off + 255) & ~255ull;
+        hipError_t e = hipSuccess;
+        void* base = static_scratch_ptr(dev, &e);
+        if (!base) {
+            (void)hipGetLastError();
+            x->static_err = std::string("static device scratch unavailable: ") + hipGetErrorString(e);
+        } else if (x->static_bytes > kStaticScratchBytes) {
+            x->static_err = "the step buffers of this context need " + std::to_string(x->static_bytes) +
+                            " bytes; the static device scratch holds " + std::to_string(kStaticScratchBytes);
+        } else {
+            x->static_base = base;
+            Carve sc((uint8_t*)base);
+            carve_step(x, sc, x->static_sb, x->static_act);
+        }
+    }
     void* ws_dev = nullptr;
     if (hipHostGetDevicePointer(&ws_dev, pinned_ws, 0) != hipSuccess || !ws_dev) {
         (void)hipGetLastError();
@@ -416,9 +453,10 @@ static CtlArgs ctl_args(ec_ctx* x, int layer, int T) {
 
 static void fill_view(ec_ctx* x, ec_step_view* v) {
     if (!v) return;
-    v->uniq = x->sb.uniq; v->counts = x->sb.counts; v->pos = x->sb.pos; v->cls = x->sb.cls;
-    v->slot = x->sb.slot; v->fills = x->sb.fills; v->victims = x->sb.victims; v->evicted = x->sb.evicted;
-    v->host_list = x->sb.host_list; v->rewritten = x->sb.rewritten;
+    const StepBufs& b = x->last_sb;
+    v->uniq = b.uniq; v->counts = b.counts; v->pos = b.pos; v->cls = b.cls;
+    v->slot = b.slot; v->fills = b.fills; v->victims = b.victims; v->evicted = b.evicted;
+    v->host_list = b.host_list; v->rewritten = b.rewritten;
 }
 
 ec_status expert_cache_step(ec_ctx* x, int32_t layer, const int32_t* ids, int32_t T, ec_step_view* out,
@@ -431,6 +469,7 @@ ec_status expert_cache_step(ec_ctx* x, int32_t layer, const int32_t* ids, int32_
     a.ids_in = ids;
     launch_ctl(a, (hipStream_t)stream);
     HIPCHK(x, hipGetLastError());
+    x->last_sb = x->sb;
     fill_view(x, out);
     return EC_OK;
 }
@@ -491,7 +530,7 @@ static void host_branch_poll(ec_ctx* x) {
 }
 
 static ec_status decode_layer(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
-                              hipStream_t s, int residual);
+                              hipStream_t s, int residual, const StepBufs& sb, float* act);
 
 ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
                            void* stream) {
@@ -499,7 +538,23 @@ ec_status moe_decode_layer(ec_ctx* x, int32_t layer, const void* xin, const floa
     if (layer < 0 || layer >= x->L) return fail(x, EC_EINVAL, "layer out of range");
     if (T < 1 || T > x->Tmax) return fail(x, EC_EINVAL, "need 1 <= T <= max_tokens");
     if (!xin || !logits || !out) return fail(x, EC_EINVAL, "NULL pointer");
-    return decode_layer(x, layer, xin, logits, T, out, (hipStream_t)stream, 0);
+    return decode_layer(x, layer, xin, logits, T, out, (hipStream_t)stream, 0, x->sb, x->act);
+}
+
+ec_status moe_decode_layer_static(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
+                                  void* stream) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    if (layer < 0 || layer >= x->L) return fail(x, EC_EINVAL, "layer out of range");
+    if (T < 1 || T > x->Tmax) return fail(x, EC_EINVAL, "need 1 <= T <= max_tokens");
+    if (!xin || !logits || !out) return fail(x, EC_EINVAL, "NULL pointer");
+    if (!x->static_base) return fail(x, x->static_bytes > kStaticScratchBytes ? EC_ENOSPC : EC_EHIP, x->static_err);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != x->device)
+        return fail(x, EC_ESTATE, "the current device is not the context's device");
+    hipStream_t s = (hipStream_t)stream;
+    static_scratch_clear_once(x->device, x->static_base, s);
+    HIPCHK(x, hipGetLastError());
+    return decode_layer(x, layer, xin, logits, T, out, s, 0, x->static_sb, x->static_act);
 }
 
 ec_status moe_gate_logits(const void* w_router, const void* xin, int32_t x_dtype, int32_t T, int32_t E, int32_t H,
@@ -524,14 +579,14 @@ ec_status moe_decode_block(ec_ctx* x, int32_t layer, const void* xin, const void
     hipStream_t s = (hipStream_t)stream;
     launch_gate(w_router, xin, x->wdt == EC_DT_F32, T, x->E, x->H, x->gate_logits, s);
     HIPCHK(x, hipGetLastError());
-    return decode_layer(x, layer, xin, x->gate_logits, T, out, s, 1);
+    return decode_layer(x, layer, xin, x->gate_logits, T, out, s, 1, x->sb, x->act);
 }
 
 static ec_status decode_layer(ec_ctx* x, int32_t layer, const void* xin, const float* logits, int32_t T, void* out,
-                              hipStream_t s, int residual) {
-    const int n = T * x->k;
+                              hipStream_t s, int residual, const StepBufs& sb, float* act) {
     const uint64_t xbytes = (uint64_t)T * x->H * (x->wdt == EC_DT_F32 ? 4 : 2);
     CtlArgs a = ctl_args(x, layer, T);
+    a.sb = sb;
     a.logits = logits;
     a.x = xin;
     a.x_bytes = (int32_t)xbytes;
@@ -541,11 +596,12 @@ static ec_status decode_layer(ec_ctx* x, int32_t layer, const void* xin, const f
     // with kernel timing on, each kernel stamps its timer pair from its own dispatch
     launch_ctl(a, s, timer_next(x, 0));
     HIPCHK(x, hipGetLastError());
+    x->last_sb = sb;
     DecodeArgs d{};
-    d.pool = x->host_pool_dev; d.slots = x->slot_pool; d.counts = x->sb.counts; d.fills = x->sb.fills;
-    d.victims = x->sb.victims; d.gpu_desc = x->sb.gpu_desc;
-    d.tok_pairs = x->sb.tok_pairs; d.rewritten = x->sb.rewritten; d.w = x->sb.w;
-    d.x = xin; d.act = x->act; d.y_host = x->y_host_dev;
+    d.pool = x->host_pool_dev; d.slots = x->slot_pool; d.counts = sb.counts; d.fills = sb.fills;
+    d.victims = sb.victims; d.gpu_desc = sb.gpu_desc;
+    d.tok_pairs = sb.tok_pairs; d.rewritten = sb.rewritten; d.w = sb.w;
+    d.x = xin; d.act = act; d.y_host = x->y_host_dev;
     d.out = out; d.expert_bytes = x->lay.expert_bytes;
     d.layer = layer % x->P; d.E = x->E; d.k = x->k; d.T = T; d.H = x->H; d.I = x->I; d.wdtype = x->wdt; d.U_max = x->Umax;
     d.host_pairs = x->host_branch ? 1 : 0;

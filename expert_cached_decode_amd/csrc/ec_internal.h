@@ -100,6 +100,12 @@ struct CtlArgs {
     uint32_t* doorbell;  // pinned (device-visible): [0] sequence of the last mailbox written
 };
 
+// The library's static device scratch (static_scratch.hip): the per-step buffers and activations of
+// moe_decode_layer_static. 4 MiB per device.
+constexpr uint64_t kStaticScratchBytes = 4ull << 20;
+void* static_scratch_ptr(int device, hipError_t* err);
+void static_scratch_clear_once(int device, void* ptr, hipStream_t s);
+
 // Launchers (defined in the .hip files).
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 void launch_ctl(const CtlArgs& a, hipStream_t s, const hipEvent_t* ev = nullptr);

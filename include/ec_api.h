@@ -249,6 +249,22 @@ ec_status ec_last_step(const ec_ctx* ctx, ec_step_view* out);
 ec_status moe_decode_layer(ec_ctx* ctx, int32_t layer, const void* x, const float* logits, int32_t T,
                            void* out, void* stream);
 
+/* moe_decode_layer for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, results and kernels; the per-step buffers (routing, cache
+ * decisions, activations) live in the library's static device scratch instead
+ * of the context's workspace: one 4 MiB array per GPU, set up by ec_create
+ * and kept until the process ends. The call allocates nothing.
+ * ec_last_step then returns pointers into that scratch.
+ * EC_ENOSPC when this context's step buffers need more than the scratch holds
+ * (max_tokens * top_k * inter activations and the decision buffers); EC_ESTATE
+ * when the current device is not the context's. All calls on one GPU share the
+ * array, which keeps the last call's contents: calls that can overlap on one
+ * GPU (other contexts, other streams) race and must be serialised by the
+ * caller. */
+ec_status moe_decode_layer_static(ec_ctx* ctx, int32_t layer, const void* x, const float* logits, int32_t T,
+                                  void* out, void* stream);
+
 /* Router logits, the step before top-k ("Why personal MoE is hard": a router
  * scores the E experts of a layer for each token):
  *   logits[t][e] = sum_h w_router[e][h] * x[t][h], fp32 accumulation.
