@@ -392,6 +392,18 @@ def main():
             result["rebuild_recovery"] = bench_rebuild_recovery(wl.ctx, cfg)
     if not args.no_peaks:
         result["peaks"] = bench_peaks()
+        gub, dnb = gemv_bytes(cfg)
+        side = cfg.k * cfg.T  # cache-side experts of an all-hit batch-1 layer step
+        sizes = {"d9_layer_step": side * (gub + dnb), "gate_up": side * gub, "down": side * dnb}
+        if args.workload == "qwen":
+            from gen.configs import DSV4_DECODE
+            g4, d4 = gemv_bytes(DSV4_DECODE)
+            sizes["d9_layer_step_mxfp4_dsv4"] = DSV4_DECODE.k * (g4 + d4)
+        ceil = bench_burst_ceilings(sizes)
+        result["peaks"]["hbm_burst"] = ceil
+        result["roofline"]["burst_ceiling"] = ceil["d9_layer_step"]
+        result["roofline"]["frac_of_burst_ceiling"] = round(
+            result["roofline"]["frac"] / ceil["d9_layer_step"]["frac"], 4)
     if prefill_T:
         result["prefill"] = bench_prefill(wl, QWEN_PREFILL, args.prefill_chunks)
     if not args.no_cpu:
@@ -460,6 +472,25 @@ def bench_cache_ctl_alone():
     out = bench_cache_ctl(ctx, cfg)
     ctx.close()
     pool.close()
+    return out
+
+
+def bench_burst_ceilings(sizes, buf_gib=8, reps=100):
+    """HBM read ceiling of one-shot bursts of the given byte counts (ec_hbm_read_probe): each burst reads
+    distinct memory of an 8 GiB buffer (never resident in the 256 MB last-level cache), timed by an event
+    pair its own dispatch stamps; median of `reps`."""
+    import torch
+    import expert_cached_decode_amd as EC
+    buf = torch.ones(buf_gib << 30, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name, b in sizes.items():
+        med, best, got = EC.binding.hbm_read_probe(buf, b, reps)
+        out[name] = {"bytes": int(got), "us_median": round(med, 3), "us_best": round(best, 3),
+                     "GBs": round(got / (med * 1e-6) / 1e9, 1), "frac": round(got / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        log("HBM burst ceiling %s: %.1f MB in %.2f us (median of %d) -> %.0f GB/s, %.1f%% of 8 TB/s"
+            % (name, got / 1e6, med, reps, out[name]["GBs"], 100 * out[name]["frac"]))
+    del buf
+    torch.cuda.empty_cache()
     return out
 
 

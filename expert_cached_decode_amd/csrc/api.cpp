@@ -651,6 +651,42 @@ ec_status ec_kernel_time(ec_ctx* x, int32_t kind, double* total_ms, uint64_t* la
     return EC_OK;
 }
 
+ec_status ec_hbm_read_probe(const void* dev_buf, uint64_t buf_bytes, uint64_t burst_bytes, int32_t reps, void* stream,
+                            double* median_us, double* best_us, uint64_t* bytes_read) {
+    if (!dev_buf || reps < 1 || reps > 100000) return fail(nullptr, EC_EINVAL, "need a buffer and 1 <= reps <= 100000");
+    if (burst_bytes < (1u << 20) || burst_bytes > buf_bytes / 4)
+        return fail(nullptr, EC_EINVAL, "need 1 MiB <= burst_bytes <= buf_bytes / 4");
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t ev[2];
+    if (hipEventCreate(&ev[0]) != hipSuccess) return fail(nullptr, EC_EHIP, "event creation failed");
+    if (hipEventCreate(&ev[1]) != hipSuccess) {
+        (void)hipEventDestroy(ev[0]);
+        return fail(nullptr, EC_EHIP, "event creation failed");
+    }
+    std::vector<float> ms;
+    uint64_t off = 0, got = 0;
+    const uint64_t stride = (burst_bytes + (1ull << 20)) & ~((1ull << 20) - 1); // distinct, 1 MiB aligned
+    hipError_t e = hipSuccess;
+    for (int r = -8; r < reps && e == hipSuccess; ++r) {
+        if (off + stride > buf_bytes) off = 0;
+        got = launch_hbm_burst((const uint8_t*)dev_buf + off, burst_bytes, s, ev);
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+        float t = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[0], ev[1]);
+        if (r >= 0) ms.push_back(t);
+        off += stride;
+    }
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (e != hipSuccess) return fail(nullptr, EC_EHIP, std::string("hbm probe: ") + hipGetErrorString(e));
+    std::sort(ms.begin(), ms.end());
+    if (median_us) *median_us = 1e3 * ms[ms.size() / 2];
+    if (best_us) *best_us = 1e3 * ms[0];
+    if (bytes_read) *bytes_read = got;
+    return EC_OK;
+}
+
 ec_status ec_set_prefill_overlap(ec_ctx* x, int32_t on) {
     if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
     x->prefill_overlap = on ? 1 : 0;

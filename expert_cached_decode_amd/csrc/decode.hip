@@ -644,6 +644,30 @@ __global__ __launch_bounds__(256) void link_probe_kernel(const uint8_t* src, uin
     if (acc == 0x9e3779b9u && bytes == 1) sink[0] = acc;
 }
 
+// HBM burst probe (measurement support): block b issues all its loads at once, eight 16-byte loads
+// per thread over 32 KiB at base + 32 KiB b, and discards them (a store only for an impossible
+// checksum of an impossible size, so nothing is written): one launch is one burst of the size the
+// decode GEMVs stream per layer step.
+constexpr uint64_t kBurstBlockBytes = 8 * 256 * 16;
+__global__ __launch_bounds__(256) void hbm_burst_kernel(const uint8_t* base, uint64_t bytes, uint32_t* sink) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(base + (uint64_t)blockIdx.x * kBurstBlockBytes) + threadIdx.x;
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(p + 256 * i);
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    if (acc == 0x9e3779b9u && bytes == 1) sink[0] = acc;
+}
+
+uint64_t launch_hbm_burst(const uint8_t* base, uint64_t bytes, hipStream_t s, const hipEvent_t* ev) {
+    const LaunchEvents le(ev);
+    const uint64_t blocks = bytes / kBurstBlockBytes;
+    EC_LAUNCH(hbm_burst_kernel, dim3((unsigned)blocks), dim3(256), 0, s, base, bytes,
+              reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(base)));
+    return blocks * kBurstBlockBytes;
+}
+
 void launch_link_probe(const uint8_t* src_dev, uint64_t bytes, uint32_t* sink, hipStream_t s) {
     const uint64_t blocks = (bytes + kFillChunk - 1) / kFillChunk;
     hipLaunchKernelGGL(link_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src_dev, bytes, sink);

@@ -370,6 +370,20 @@ ec_status ec_kernel_timing(ec_ctx* ctx, int32_t on);
  * kind since timing was switched on (or last reset). Synchronises. */
 ec_status ec_kernel_time(ec_ctx* ctx, int32_t kind, double* total_ms, uint64_t* launches, int32_t reset);
 
+/* HBM read ceiling of a one-shot burst (measurement support, beside the
+ * kernel timing): launches that each issue every load of `burst_bytes` at once
+ * (32 KiB per workgroup, 16-byte nontemporal loads, the data discarded), the
+ * shape of the decode GEMVs' per-layer weight stream. Successive bursts read
+ * distinct 1 MiB-aligned regions of `dev_buf` (dev, `buf_bytes`; give it far
+ * more than the 256 MB last-level cache so that no burst is served from it).
+ * `reps` timed bursts follow 8 untimed ones; each is timed by an event pair its
+ * own dispatch stamps on `stream`. Outputs (any may be NULL): median and best
+ * microseconds per burst, and the bytes one burst reads (burst_bytes rounded
+ * down to 32 KiB). Synchronises; nothing is written to dev_buf.
+ * EC_EINVAL unless 1 MiB <= burst_bytes <= buf_bytes / 4 and 1 <= reps <= 100000. */
+ec_status ec_hbm_read_probe(const void* dev_buf, uint64_t buf_bytes, uint64_t burst_bytes, int32_t reps, void* stream,
+                            double* median_us, double* best_us, uint64_t* bytes_read);
+
 #ifdef __cplusplus
 }
 #endif
