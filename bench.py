@@ -133,6 +133,8 @@ class DecodeWorkload:
         self.lg_stage = torch.empty((L, T, cfg.E), dtype=torch.float32, device="cuda")
         self.outs = torch.empty((L, T, cfg.H), dtype=torch.int16, device="cuda")
         self.graph = None
+        self.prime_us = 0  # queue primer ahead of each step of a kernel pass (0: none)
+        self.enqueue_us = 0.0
 
     def token_layers(self, xsrc, lsrc, strm):
         import expert_cached_decode_amd as EC
@@ -175,15 +177,32 @@ class DecodeWorkload:
 
     def kernel_pass(self, steps):
         """Eager pass over the given steps with each decode kernel stamping a HIP event pair from its
-        own dispatch on the launch stream; per-kind (us per launch, launches) and the pass's stats."""
+        own dispatch on the launch stream; per-kind (us per launch, launches) and the pass's stats.
+        With prime_us set, each step's launches are queued behind a primer of that many us, so its
+        kernels run back to back as in a graph replay (the host's launch cost per kernel exceeds the
+        short kernels' durations: unprimed, each would start on an idle queue)."""
         import torch
+        import expert_cached_decode_amd as EC
         stream = torch.cuda.current_stream()
         torch.cuda.synchronize()
         self.ctx.stats(reset=True)
         self.ctx.kernel_timing(True)
+        self.enqueue_us = 0.0
+        pending = 0
         for s in steps:
             i = s % self.n_inputs
+            if pending + self.cfg.L > 1024:
+                # the library holds 1024 event pairs per kernel kind and drains them (synchronising)
+                # when they run out: drain here, between steps, rather than inside a primed step
+                for k in ("ctl", "fill", "gate_up", "down"):
+                    self.ctx.kernel_time(k)
+                pending = 0
+            pending += self.cfg.L
+            if self.prime_us:
+                EC.binding.queue_delay(self.prime_us, stream)
+            t0 = time.perf_counter()
             self.token_layers(self.xs[i], self.logits[i], stream)
+            self.enqueue_us = max(self.enqueue_us, 1e6 * (time.perf_counter() - t0))
         torch.cuda.synchronize()
         st = self.ctx.stats(reset=True)
         assert st["device_error"] == 0
@@ -216,30 +235,41 @@ class DecodeWorkload:
                         "frac": round(dn_b / (dn_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
                "ctl_us_per_launch": round(kt["ctl"][0], 3),
                "timing": "HIP event pair stamped by each launch's own dispatch on its stream "
-                         "(hipExtLaunchKernelGGL), eager pass"}
+                         "(hipExtLaunchKernelGGL), eager pass" + (
+                             ", each step queued behind a %d us primer (ec_queue_delay; host enqueue %.0f us "
+                             "per step at most)" % (self.prime_us, self.enqueue_us) if self.prime_us
+                             else ", unprimed (kernels may start on an idle queue)")}
+        if self.prime_us and self.enqueue_us > self.prime_us:
+            log("warning: a step took %.0f us to enqueue, longer than the %d us primer" % (self.enqueue_us, self.prime_us))
         log("%s D9 (%s): gate/up %.2f + down %.2f us = %.2f us for %.1f MB -> %.0f GB/s, %.1f%% of 8 TB/s; ctl %.2f us"
             % (cfg.name, leg, gu_us, dn_us, gu_us + dn_us, (gu_b + dn_b) / 1e6, gbs, 100 * gbs / HBM_PEAK_GBS,
                kt["ctl"][0]))
         return out
 
-    def all_hit(self, s0, window=8, reps=4):
+    def all_hit(self, s0, window=8, reps=4, eager_only=False):
         """All-hit leg: a cold rebuild to the configured budget, one warm pass over `window` steps
         (they touch at most window * L * k <= C distinct experts, so nothing is evicted), then the
         same steps again: every routed expert is a hit, nothing is filled, so no expert byte read in
         the timed steps was written moments before (each pass streams window * L * k experts, far more
         than the 256 MB last-level cache holds). Returns the D9 roofline of an eager kernel pass and
-        the tok/s of graph replays of the same warm steps."""
+        the tok/s of graph replays of the same warm steps (eager_only: the kernel pass alone, with an
+        eager warm pass, so that no graph is launched)."""
         cfg = self.cfg
         window = min(window, cfg.slots // (cfg.L * cfg.k * cfg.T))
         if window < 1:
             return None
         self.ctx.rebuild(self.budget_bp)
-        self.capture()
-        for s in range(s0, s0 + window):
-            self.step(s)
+        if eager_only:
+            self.kernel_pass(range(s0, s0 + window))
+        else:
+            self.capture()
+            for s in range(s0, s0 + window):
+                self.step(s)
         kt, st = self.kernel_pass([s0 + (i % window) for i in range(window * reps)])
         assert st["misses"] == 0 and st["fills"] == 0 and st["host"] == 0, st
         out = self.d9(kt, st, "all-hit: warm cache, every routed expert a hit, no fills")
+        if eager_only:
+            return out
         ms = []
         for r in range(reps):
             m, st2 = self.timed(s0, window)
@@ -291,6 +321,11 @@ def main():
     ap.add_argument("--prefill-chunks", type=int, default=4)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc runs)")
+    ap.add_argument("--prime-us", type=int, default=3000,
+                    help="kernel passes: queue each step's launches behind a primer of this many us (0: off)")
+    ap.add_argument("--counters-only", action="store_true",
+                    help="for rocprofv3 --pmc runs: eager decode steps only (W warm-up, then --timing-steps "
+                         "timed, then the all-hit window), no graph replays and no other leg; prints the D9 lines")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
@@ -319,12 +354,20 @@ def main():
     period = 1 if cfg.wdtype == MXFP4 else 0
     prefill_T = QWEN_PREFILL.T if (args.workload == "qwen" and not args.no_prefill) else 0
     wl = DecodeWorkload(cfg, P, period, n_inputs, prefill_T=prefill_T, host_threads=args.host_threads)
+    wl.prime_us = args.prime_us
     ctx = wl.ctx
     # measured BP and BH (MB/s): applied with --bpbh calibrate, else reported only
     bp_meas, bh_meas = ctx.calibrate_bandwidth(min(32, cfg.E // 4), apply=(args.bpbh == "calibrate"))
     log("calibration: BP %d MB/s over the link, BH %d MB/s on the host branch%s"
         % (bp_meas, bh_meas, " (applied)" if args.bpbh == "calibrate" else ""))
     bp_used, bh_used = (bp_meas, bh_meas) if args.bpbh == "calibrate" else (cfg.bp, cfg.bh)
+    if args.counters_only:
+        wl.kernel_pass(range(W))
+        log("counters: %d eager warm-up steps done" % W)
+        wl.d9(*wl.kernel_pass(range(W, W + TS)), "workload: eager steps continuing the warm-up")
+        wl.all_hit(W + TS, eager_only=True)
+        wl.close()
+        return
     text += ", BP:BH %d:%d%s" % (bp_used, bh_used, " (measured)" if args.bpbh == "calibrate" else "")
 
     # headline: W warm-up steps, then exactly K timed steps (graph replays)
@@ -401,9 +444,16 @@ def main():
             sizes["d9_layer_step_mxfp4_dsv4"] = DSV4_DECODE.k * (g4 + d4)
         ceil = bench_burst_ceilings(sizes)
         result["peaks"]["hbm_burst"] = ceil
-        result["roofline"]["burst_ceiling"] = ceil["d9_layer_step"]
-        result["roofline"]["frac_of_burst_ceiling"] = round(
-            result["roofline"]["frac"] / ceil["d9_layer_step"]["frac"], 4)
+        # D9 is two dependent streams (down reads what gate/up writes): its ceiling is a gate/up-sized
+        # burst followed by a down-sized one; one burst of all the bytes is the bound of a fused form
+        two = ceil["gate_up"]["us_median"] + ceil["down"]["us_median"]
+        two_frac = sizes["d9_layer_step"] / (two * 1e-6) / 1e9 / HBM_PEAK_GBS
+        result["roofline"]["burst_ceiling"] = {
+            "two_dependent_bursts": {"us": round(two, 3), "frac": round(two_frac, 4)},
+            "one_burst": ceil["d9_layer_step"]}
+        result["roofline"]["frac_of_burst_ceiling"] = round(result["roofline"]["frac"] / two_frac, 4)
+        log("D9 all-hit at %.1f%% of 8 TB/s = %.1f%% of its two-burst ceiling (%.2f us, %.1f%%)"
+            % (100 * result["roofline"]["frac"], 100 * result["roofline"]["frac_of_burst_ceiling"], two, 100 * two_frac))
     if prefill_T:
         result["prefill"] = bench_prefill(wl, QWEN_PREFILL, args.prefill_chunks)
     if not args.no_cpu:
@@ -412,14 +462,14 @@ def main():
     del wl, ctx
     torch.cuda.empty_cache()
     if args.workload == "qwen" and not args.no_extra:
-        result["dsv4_decode"] = bench_dsv4_legs()
+        result["dsv4_decode"] = bench_dsv4_legs(prime_us=args.prime_us)
         result["cache_ctl_stress"] = bench_cache_ctl_alone()
         if args.cold_start_gb > 0:
             result["cold_start"] = bench_cold_start(cfg, args.cold_start_gb)
     print(json.dumps(result), flush=True)
 
 
-def bench_dsv4_legs(ratios=((300, 1000), (1000, 1000)), warm=32, steps=64, timing_steps=16):
+def bench_dsv4_legs(ratios=((300, 1000), (1000, 1000)), warm=32, steps=64, timing_steps=16, prime_us=0):
     """The DeepSeek-V4-Flash-shaped MXFP4 decode (43 layers, top-6 of 256, H 4096, I 2048, 2752
     slots = 25%, p = 0.6) at BP:BH 300:1000 (most misses on the host branch) and 1000:1000 (every
     miss filled, no host branch): tok/s of graph replays from a cold cache after `warm` steps, and
@@ -431,6 +481,7 @@ def bench_dsv4_legs(ratios=((300, 1000), (1000, 1000)), warm=32, steps=64, timin
     cfg = DSV4_DECODE
     n_inputs = warm + steps + timing_steps
     wl = DecodeWorkload(cfg, 4, 1, n_inputs)
+    wl.prime_us = prime_us
     out = {"workload": "DeepSeek-V4-Flash-shaped MXFP4 decode, batch 1, 43 layers, 2752 slots (25%), "
                        "60% step-to-step routing overlap, 4 pinned pool layers", "legs": {}}
     for bp, bh in ratios:
@@ -478,17 +529,20 @@ def bench_cache_ctl_alone():
 def bench_burst_ceilings(sizes, buf_gib=8, reps=100):
     """HBM read ceiling of one-shot bursts of the given byte counts (ec_hbm_read_probe): each burst reads
     distinct memory of an 8 GiB buffer (never resident in the 256 MB last-level cache), timed by an event
-    pair its own dispatch stamps; median of `reps`."""
+    pair its own dispatch stamps; median of `reps`. Bursts queued back to back behind a primer (as the
+    primed kernel pass runs the decode kernels), and, for reference, each on an idle queue."""
     import torch
     import expert_cached_decode_amd as EC
     buf = torch.ones(buf_gib << 30, dtype=torch.uint8, device="cuda")
     out = {}
     for name, b in sizes.items():
-        med, best, got = EC.binding.hbm_read_probe(buf, b, reps)
+        med, best, got = EC.binding.hbm_read_probe(buf, b, reps, queued=True)
+        imed, _, _ = EC.binding.hbm_read_probe(buf, b, reps, queued=False)
         out[name] = {"bytes": int(got), "us_median": round(med, 3), "us_best": round(best, 3),
-                     "GBs": round(got / (med * 1e-6) / 1e9, 1), "frac": round(got / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        log("HBM burst ceiling %s: %.1f MB in %.2f us (median of %d) -> %.0f GB/s, %.1f%% of 8 TB/s"
-            % (name, got / 1e6, med, reps, out[name]["GBs"], 100 * out[name]["frac"]))
+                     "GBs": round(got / (med * 1e-6) / 1e9, 1), "frac": round(got / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "idle_queue_us_median": round(imed, 3)}
+        log("HBM burst ceiling %s: %.1f MB in %.2f us (median of %d, queued) -> %.0f GB/s, %.1f%% of 8 TB/s; "
+            "%.2f us from an idle queue" % (name, got / 1e6, med, reps, out[name]["GBs"], 100 * out[name]["frac"], imed))
     del buf
     torch.cuda.empty_cache()
     return out

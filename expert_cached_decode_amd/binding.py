@@ -58,7 +58,7 @@ EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec
            "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
            "ec_kernel_timing", "ec_kernel_time", "ec_calibrate_bandwidth", "moe_gate_logits",
            "moe_decode_block", "ec_bank_write", "ec_bank_read", "ec_last_step", "ec_rebuild_slots",
-           "moe_decode_layer_static", "ec_hbm_read_probe"]
+           "moe_decode_layer_static", "ec_hbm_read_probe", "ec_queue_delay"]
 KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
@@ -95,8 +95,9 @@ def lib():
         L.ec_debug_state.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp]
         L.ec_kernel_timing.argtypes = [c_vp, c_i32]
         L.ec_kernel_time.argtypes = [c_vp, c_i32, ctypes.POINTER(ctypes.c_double), P(c_u64), c_i32]
-        L.ec_hbm_read_probe.argtypes = [c_vp, c_u64, c_u64, c_i32, c_vp, ctypes.POINTER(ctypes.c_double),
+        L.ec_hbm_read_probe.argtypes = [c_vp, c_u64, c_u64, c_i32, c_i32, c_vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double), P(c_u64)]
+        L.ec_queue_delay.argtypes = [c_vp, ctypes.c_uint32]
         L.ec_calibrate_bandwidth.argtypes = [c_vp, c_i32, c_i32, P(ctypes.c_uint32), P(ctypes.c_uint32)]
         L.moe_gate_logits.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
         L.moe_decode_block.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]
@@ -356,12 +357,20 @@ class Context:
             pass
 
 
-def hbm_read_probe(buf, burst_bytes, reps=100, stream=None):
-    """(median us, best us, bytes per burst) of one-shot HBM read bursts over a device tensor (ec_hbm_read_probe)."""
+def hbm_read_probe(buf, burst_bytes, reps=100, queued=True, stream=None):
+    """(median us, best us, bytes per burst) of one-shot HBM read bursts over a device tensor
+    (ec_hbm_read_probe): queued behind a primer and run back to back, or each on an idle queue."""
     med, best, got = ctypes.c_double(), ctypes.c_double(), c_u64()
-    check(lib().ec_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), burst_bytes, reps, _stream(stream),
-                                  ctypes.byref(med), ctypes.byref(best), ctypes.byref(got)))
+    check(lib().ec_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), burst_bytes, reps,
+                                  1 if queued else 0, _stream(stream), ctypes.byref(med), ctypes.byref(best),
+                                  ctypes.byref(got)))
     return med.value, best.value, got.value
+
+
+def queue_delay(us, stream=None):
+    """Hold `stream` for about `us` microseconds (ec_queue_delay), so that launches queued behind it
+    run back to back."""
+    check(lib().ec_queue_delay(_stream(stream), int(us)))
 
 
 def memcpy_async(dst, src, nbytes, stream=None):

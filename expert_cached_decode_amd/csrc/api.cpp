@@ -651,34 +651,66 @@ ec_status ec_kernel_time(ec_ctx* x, int32_t kind, double* total_ms, uint64_t* la
     return EC_OK;
 }
 
-ec_status ec_hbm_read_probe(const void* dev_buf, uint64_t buf_bytes, uint64_t burst_bytes, int32_t reps, void* stream,
-                            double* median_us, double* best_us, uint64_t* bytes_read) {
-    if (!dev_buf || reps < 1 || reps > 100000) return fail(nullptr, EC_EINVAL, "need a buffer and 1 <= reps <= 100000");
+static hipError_t wall_clock_khz(int* khz) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+    if (e == hipSuccess && *khz <= 0) e = hipErrorInvalidValue;
+    return e;
+}
+
+ec_status ec_queue_delay(void* stream, uint32_t us) {
+    if (us > 1000000) return fail(nullptr, EC_EINVAL, "need us <= 1000000");
+    int khz = 0;
+    hipError_t e = wall_clock_khz(&khz);
+    if (e == hipSuccess) {
+        launch_queue_delay((uint64_t)us * (uint64_t)khz / 1000u, (hipStream_t)stream);
+        e = hipGetLastError();
+    }
+    if (e != hipSuccess) return fail(nullptr, EC_EHIP, std::string("queue delay: ") + hipGetErrorString(e));
+    return EC_OK;
+}
+
+ec_status ec_hbm_read_probe(const void* dev_buf, uint64_t buf_bytes, uint64_t burst_bytes, int32_t reps, int32_t queued,
+                            void* stream, double* median_us, double* best_us, uint64_t* bytes_read) {
+    if (!dev_buf || reps < 1 || reps > 1000) return fail(nullptr, EC_EINVAL, "need a buffer and 1 <= reps <= 1000");
     if (burst_bytes < (1u << 20) || burst_bytes > buf_bytes / 4)
         return fail(nullptr, EC_EINVAL, "need 1 MiB <= burst_bytes <= buf_bytes / 4");
     hipStream_t s = (hipStream_t)stream;
-    hipEvent_t ev[2];
-    if (hipEventCreate(&ev[0]) != hipSuccess) return fail(nullptr, EC_EHIP, "event creation failed");
-    if (hipEventCreate(&ev[1]) != hipSuccess) {
-        (void)hipEventDestroy(ev[0]);
-        return fail(nullptr, EC_EHIP, "event creation failed");
+    const int n = reps + 8; // 8 untimed bursts first
+    std::vector<hipEvent_t> ev;
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 2 * n && e == hipSuccess; ++i) {
+        hipEvent_t v;
+        e = hipEventCreate(&v);
+        if (e == hipSuccess) ev.push_back(v);
     }
-    std::vector<float> ms;
     uint64_t off = 0, got = 0;
     const uint64_t stride = (burst_bytes + (1ull << 20)) & ~((1ull << 20) - 1); // distinct, 1 MiB aligned
-    hipError_t e = hipSuccess;
-    for (int r = -8; r < reps && e == hipSuccess; ++r) {
+    if (queued && e == hipSuccess) {
+        // the host queues every burst while the primer holds the stream (about 25 us per launch)
+        int khz = 0;
+        e = wall_clock_khz(&khz);
+        if (e == hipSuccess) {
+            launch_queue_delay((2000ull + 25ull * n) * (uint64_t)khz / 1000u, s);
+            e = hipGetLastError();
+        }
+    }
+    for (int r = 0; r < n && e == hipSuccess; ++r) {
         if (off + stride > buf_bytes) off = 0;
-        got = launch_hbm_burst((const uint8_t*)dev_buf + off, burst_bytes, s, ev);
+        got = launch_hbm_burst((const uint8_t*)dev_buf + off, burst_bytes, s, &ev[2 * r]);
         e = hipGetLastError();
-        if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
-        float t = 0.f;
-        if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[0], ev[1]);
-        if (r >= 0) ms.push_back(t);
+        if (e == hipSuccess && !queued) e = hipEventSynchronize(ev[2 * r + 1]);
         off += stride;
     }
-    (void)hipEventDestroy(ev[0]);
-    (void)hipEventDestroy(ev[1]);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    std::vector<float> ms;
+    for (int r = 8; r < n && e == hipSuccess; ++r) {
+        float t = 0.f;
+        e = hipEventElapsedTime(&t, ev[2 * r], ev[2 * r + 1]);
+        ms.push_back(t);
+    }
+    for (hipEvent_t v : ev) (void)hipEventDestroy(v);
     if (e != hipSuccess) return fail(nullptr, EC_EHIP, std::string("hbm probe: ") + hipGetErrorString(e));
     std::sort(ms.begin(), ms.end());
     if (median_us) *median_us = 1e3 * ms[ms.size() / 2];

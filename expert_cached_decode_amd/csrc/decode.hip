@@ -668,6 +668,19 @@ uint64_t launch_hbm_burst(const uint8_t* base, uint64_t bytes, hipStream_t s, co
     return blocks * kBurstBlockBytes;
 }
 
+// Queue primer (measurement support): one lane holds the stream until the device's constant-rate
+// real-time counter has advanced by `ticks`, sleeping between reads, so the host can queue a timed
+// pass behind it; the kernel ends on time whatever the rest of the device does.
+__global__ void queue_delay_kernel(uint64_t ticks) {
+    if (threadIdx.x != 0) return;
+    const uint64_t t0 = wall_clock64();
+    while ((uint64_t)wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(32);
+}
+
+void launch_queue_delay(uint64_t ticks, hipStream_t s) {
+    hipLaunchKernelGGL(queue_delay_kernel, dim3(1), dim3(64), 0, s, ticks);
+}
+
 void launch_link_probe(const uint8_t* src_dev, uint64_t bytes, uint32_t* sink, hipStream_t s) {
     const uint64_t blocks = (bytes + kFillChunk - 1) / kFillChunk;
     hipLaunchKernelGGL(link_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src_dev, bytes, sink);

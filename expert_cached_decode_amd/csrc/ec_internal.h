@@ -139,6 +139,7 @@ struct DecodeArgs {
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s, const hipEvent_t* ev = nullptr);
 void launch_link_probe(const uint8_t* src_dev, uint64_t bytes, uint32_t* sink, hipStream_t s);
 uint64_t launch_hbm_burst(const uint8_t* base, uint64_t bytes, hipStream_t s, const hipEvent_t* ev);
+void launch_queue_delay(uint64_t ticks, hipStream_t s);
 void launch_gate(const void* wr, const void* x, bool f32, int T, int E, int H, float* logits, hipStream_t s);
 void launch_gu(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev = nullptr);
 void launch_down(const DecodeArgs& a, hipStream_t s, const hipEvent_t* ev = nullptr);

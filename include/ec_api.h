@@ -370,6 +370,15 @@ ec_status ec_kernel_timing(ec_ctx* ctx, int32_t on);
  * kind since timing was switched on (or last reset). Synchronises. */
 ec_status ec_kernel_time(ec_ctx* ctx, int32_t kind, double* total_ms, uint64_t* launches, int32_t reset);
 
+/* Queue primer (measurement support): enqueues on `stream` one small kernel
+ * that holds it for about `us` microseconds of the device's constant-rate
+ * real-time clock, then ends. Launches the host queues behind it meet a busy
+ * queue, so each kernel of a timed pass starts right behind its predecessor (as
+ * in a graph replay) instead of waking an idle queue; without a primer a pass
+ * whose kernels are shorter than the host's per-launch cost times each kernel
+ * from an idle queue. Asynchronous. EC_EINVAL unless us <= 1000000. */
+ec_status ec_queue_delay(void* stream, uint32_t us);
+
 /* HBM read ceiling of a one-shot burst (measurement support, beside the
  * kernel timing): launches that each issue every load of `burst_bytes` at once
  * (32 KiB per workgroup, 16-byte nontemporal loads, the data discarded), the
@@ -377,12 +386,14 @@ ec_status ec_kernel_time(ec_ctx* ctx, int32_t kind, double* total_ms, uint64_t* 
  * distinct 1 MiB-aligned regions of `dev_buf` (dev, `buf_bytes`; give it far
  * more than the 256 MB last-level cache so that no burst is served from it).
  * `reps` timed bursts follow 8 untimed ones; each is timed by an event pair its
- * own dispatch stamps on `stream`. Outputs (any may be NULL): median and best
+ * own dispatch stamps on `stream`. `queued` != 0: all bursts are queued behind a
+ * primer (ec_queue_delay) and run back to back; 0: each burst is launched on an
+ * idle queue and waited for. Outputs (any may be NULL): median and best
  * microseconds per burst, and the bytes one burst reads (burst_bytes rounded
  * down to 32 KiB). Synchronises; nothing is written to dev_buf.
- * EC_EINVAL unless 1 MiB <= burst_bytes <= buf_bytes / 4 and 1 <= reps <= 100000. */
-ec_status ec_hbm_read_probe(const void* dev_buf, uint64_t buf_bytes, uint64_t burst_bytes, int32_t reps, void* stream,
-                            double* median_us, double* best_us, uint64_t* bytes_read);
+ * EC_EINVAL unless 1 MiB <= burst_bytes <= buf_bytes / 4 and 1 <= reps <= 1000. */
+ec_status ec_hbm_read_probe(const void* dev_buf, uint64_t buf_bytes, uint64_t burst_bytes, int32_t reps, int32_t queued,
+                            void* stream, double* median_us, double* best_us, uint64_t* bytes_read);
 
 #ifdef __cplusplus
 }

@@ -128,3 +128,36 @@ def test_chained_block_graph_matches_eager():
     for u, v in zip(st_e[:3], st_g[:3]):
         assert np.array_equal(u, v)
     assert st_e[3] == st_g[3]
+
+
+def test_stale_graph_after_epoch_change_is_flagged_not_addressed():
+    """A graph captured while the host branch was compiled out (BP >= BH and the cache holds a whole
+    step), replayed after ec_set_bandwidth switched the branch on: the control step now sends misses
+    to the host, and the captured down GEMV, which has no host branch, must skip those pairs (never
+    address a slot from a negative id) and raise the device error that names the epoch change."""
+    import torch
+    import expert_cached_decode_amd as EC
+    cfg = QWEN_DECODE.with_(L=2, slots=48)
+    L = cfg.L
+    pool = make_pool(cfg)
+    logits, x = inputs(cfg, 1, L)
+    ctx = make_ctx(cfg, pool, C=48, bp=1000, bh=1000)
+    assert ctx.stats()["host_branch"] == 0
+    e0 = ctx.epoch()
+    outs = torch.empty((L, 1, cfg.H), dtype=torch.int16, device="cuda")
+    g, cap = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cap):
+        for l in range(L):
+            EC.moe_decode_layer(ctx, l, x[0, l], logits[0, l], 1, outs[l], cap)
+    torch.cuda.synchronize()
+    ctx.set_bandwidth(0, 1000)  # no fills: every miss of the cold cache is a host-side pair
+    assert ctx.epoch() != e0 and ctx.stats()["host_branch"] == 1
+    g.replay()
+    torch.cuda.synchronize()
+    with pytest.raises(EC.ECError, match="epoch"):
+        ctx.stats()
+    s = EC.binding.ec_stats()
+    assert EC.lib().ec_get_stats(ctx.handle, EC.binding.ctypes.byref(s), 0) == -7
+    assert s.device_error & 4
+    ctx.close()
