@@ -321,7 +321,7 @@ def main():
     ap.add_argument("--prefill-chunks", type=int, default=4)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc runs)")
-    ap.add_argument("--prime-us", type=int, default=3000,
+    ap.add_argument("--prime-us", type=int, default=6000,
                     help="kernel passes: queue each step's launches behind a primer of this many us (0: off)")
     ap.add_argument("--counters-only", action="store_true",
                     help="for rocprofv3 --pmc runs: eager decode steps only (W warm-up, then --timing-steps "
