@@ -92,9 +92,13 @@ float dot_row(int wdt, const uint8_t* row, const uint8_t* srow, const float* v, 
 #define EC_BF16_TARGET __attribute__((target("avx512f,avx512bw,avx512vl,avx512bf16")))
 
 bool host_has_bf16_dot() {
+#ifdef EC_HOST_NO_BF16_DOT // test builds that exercise the AVX2 path on a host with the bf16 unit
+    return false;
+#else
     static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
                            __builtin_cpu_supports("avx512bf16");
     return ok;
+#endif
 }
 
 // dot of n bf16 weights with n bf16 activations (n a multiple of 64); products exact in fp32
