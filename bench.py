@@ -621,8 +621,21 @@ def bench_measured_split(wl, steps):
            "miss_rate": round(st["misses"] / max(st["hits"] + st["misses"], 1), 4),
            "fills_per_step": round(st["fills"] / steps, 3), "host_per_step": round(st["host"] / steps, 3)}
     out["token_bound"] = token_bound(cfg, st, steps, bp, bh, out["tok_s"])
+    # the host's view of the same steps: time per host job (doorbell seen to sums published) and
+    # per handoff of the decode loop (sums published to the next layer step's doorbell)
+    jobs, gaps = max(st["host_jobs"], 1), max(st["host_gaps"], 1)
+    host_bytes = st["host"] * cfg.expert_bytes
+    out["host_side"] = {"jobs": st["host_jobs"], "us_per_job": round(st["host_busy_us"] / jobs, 2),
+                        "experts_per_job": round(st["host"] / jobs, 3),
+                        "GBs_while_busy": round(host_bytes / max(st["host_busy_us"], 1e-9) / 1e3, 1),
+                        "handoffs": st["host_gaps"], "us_per_handoff": round(st["host_gap_us"] / gaps, 2),
+                        "us_per_layer_step": round(1e3 * ms / cfg.L, 2)}
     log("measured split BP:BH %d:%d: %.2f tok/s, fills/step %.2f, host/step %.2f; per-token bound %.2f tok/s"
         % (bp, bh, out["tok_s"], out["fills_per_step"], out["host_per_step"], out["token_bound"]["tok_s"]))
+    hs = out["host_side"]
+    log("measured split, host side: %.1f us per job (%.2f experts, %.0f GB/s while busy), %.1f us per handoff, "
+        "%.1f us per layer step" % (hs["us_per_job"], hs["experts_per_job"], hs["GBs_while_busy"],
+                                     hs["us_per_handoff"], hs["us_per_layer_step"]))
     return out
 
 

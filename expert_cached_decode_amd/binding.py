@@ -49,7 +49,8 @@ class ec_step_view(ctypes.Structure):
 class ec_stats(ctypes.Structure):
     _fields_ = [("steps", c_u64), ("hits", c_u64), ("misses", c_u64), ("fills", c_u64), ("host", c_u64),
                 ("evictions", c_u64), ("device_error", c_i32), ("slots", c_i32), ("clock", c_u64),
-                ("host_only", c_i32), ("host_branch", c_i32)]
+                ("host_only", c_i32), ("host_branch", c_i32), ("host_jobs", c_u64), ("host_busy_us", ctypes.c_double),
+                ("host_gaps", c_u64), ("host_gap_us", ctypes.c_double)]
 
 
 _lib = None

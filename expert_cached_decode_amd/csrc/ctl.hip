@@ -916,6 +916,14 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
     const int ec = tid < E ? tid : E - 1;
     const float lv = logits[ec];                          // logit of expert tid
     const int rres = resid[(int64_t)l * E + ec];          // residency of expert tid
+    // the state words before the slot table: the fill count and the mailbox (steps 4 and 4b)
+    // need them, the slot table only the victim scan after them (loads complete in order)
+    const uint64_t clk = words[0];
+    const uint32_t bp = reinterpret_cast<const uint32_t*>(words + 1)[0];
+    const uint32_t bh = reinterpret_cast<const uint32_t*>(words + 1)[1];
+    const uint32_t hs = reinterpret_cast<const uint32_t*>(words + 2)[0];
+    unsigned long long* stats = reinterpret_cast<unsigned long long*>(words + 4);
+    const unsigned long long st_v = stats[(int64_t)l * ST_N + (lane < ST_N ? lane : 0)];
     uint64_t pk[kSlotRegs];
     int po[kSlotRegs];
 #pragma unroll
@@ -924,12 +932,6 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
         pk[p] = slot_lru[s < C ? s : 0];
         po[p] = slot_key[s < C ? s : 0];
     }
-    const uint64_t clk = words[0];
-    const uint32_t bp = reinterpret_cast<const uint32_t*>(words + 1)[0];
-    const uint32_t bh = reinterpret_cast<const uint32_t*>(words + 1)[1];
-    const uint32_t hs = reinterpret_cast<const uint32_t*>(words + 2)[0];
-    unsigned long long* stats = reinterpret_cast<unsigned long long*>(words + 4);
-    const unsigned long long st_v = stats[(int64_t)l * ST_N + (lane < ST_N ? lane : 0)];
     // output pointers of the argument block, fetched now (the empty asm keeps the compiler from
     // sinking their loads past the first routing stage, where the block barrier would wait for them)
     asm volatile("" ::"s"(a.sb.ids), "s"(a.sb.w), "s"(a.sb.uniq), "s"(a.sb.counts), "s"(a.sb.pos), "s"(a.sb.cls),
@@ -1006,6 +1008,39 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
         qq = min(qq, a.K);
         qq = min(qq, C - h);
         if (lane == 0) s_q = qq > 0 ? qq : 0;
+
+        // 4b. the host list is fixed once q is (the misses past the first q, in unique order):
+        //     the mailbox is published and the doorbell rung here, before victim selection, so
+        //     the host starts on its experts while the GPU finishes the step, fills and streams.
+        //     Mailbox in pinned host memory: [counts 8][host_list n][rewritten n][w n][x bytes],
+        //     n = k; rewritten holds -(1 + host index) for host-side pairs (0 for the others,
+        //     whose slots the host does not use); the wavefront's stores are made visible
+        //     system-wide before lane 0 rings.
+        const int q0 = qq > 0 ? qq : 0;
+        if (a.host_branch && m - q0 > 0) {
+            const int n = k;
+            int32_t* mb = a.sb.mailbox;
+            if (lane == 0) {
+                mb[CNT_U] = k; mb[CNT_H] = h; mb[CNT_M] = m; mb[CNT_Q] = q0; mb[CNT_HOST] = m - q0;
+                mb[CNT_GPU] = k - (m - q0); mb[6] = 1; mb[7] = l;
+            }
+            const bool host_r = valid && miss && midx >= q0;
+            if (host_r) mb[CNT_N + (midx - q0)] = u;
+            const int hv = host_r ? -(1 + midx - q0) : 0;
+            const int rwh = __builtin_amdgcn_ds_bpermute(pos * 4, hv);
+            if (lane < n) {
+                mb[CNT_N + n + lane] = rwh;
+                reinterpret_cast<float*>(mb)[CNT_N + 2 * n + lane] = wj;
+            }
+            const uint4* xs = reinterpret_cast<const uint4*>(a.x);
+            uint4* xd = reinterpret_cast<uint4*>(mb + CNT_N + 3 * n + ((4 - (3 * n) % 4) % 4));
+            for (int i = lane; i < a.x_bytes / 16; i += 64) xd[i] = xs[i];
+            __threadfence_system();
+            if (lane == 0) {
+                reinterpret_cast<uint32_t*>(words + 2)[0] = hs + 1;
+                __hip_atomic_store(a.doorbell, hs + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
     }
     __syncthreads();
     const int q = s_q;
@@ -1060,7 +1095,7 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
     if (valid) a.sb.tok_pairs[lane] = pr;
     if (valid && cls != CLS_HOST) a.sb.gpu_desc[g] = make_int4(slot_r, lane, 1, pr);
 
-    // 8. counts, stats, clock; mailbox for the host branch
+    // 8. counts, stats, clock (the mailbox went out after step 4)
     if (lane == 0) {
         int32_t* c = a.sb.counts;
         c[CNT_U] = k; c[CNT_H] = h; c[CNT_M] = m; c[CNT_Q] = q; c[CNT_HOST] = m - q; c[CNT_GPU] = n_gpu;
@@ -1072,29 +1107,6 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
                                    : lane == ST_MISSES ? (unsigned long long)m : lane == ST_FILLS ? (unsigned long long)q
                                    : lane == ST_HOST ? (unsigned long long)(m - q) : (unsigned long long)n_ev;
         stats[(int64_t)l * ST_N + lane] = st_v + d;
-    }
-    if (a.host_branch && m - q > 0) {
-        // mailbox in pinned host memory: [counts 8][host_list n][rewritten n][w n][x bytes], n = k;
-        // the wavefront's stores are made visible system-wide before lane 0 rings the doorbell
-        const int n = k;
-        int32_t* mb = a.sb.mailbox;
-        if (lane == 0) {
-            mb[CNT_U] = k; mb[CNT_H] = h; mb[CNT_M] = m; mb[CNT_Q] = q; mb[CNT_HOST] = m - q; mb[CNT_GPU] = n_gpu;
-            mb[6] = 1; mb[7] = l;
-        }
-        if (valid && cls == CLS_HOST) mb[CNT_N + (-slot_r - 1)] = u;
-        if (lane < n) {
-            mb[CNT_N + n + lane] = rw;
-            reinterpret_cast<float*>(mb)[CNT_N + 2 * n + lane] = wj;
-        }
-        const uint4* xs = reinterpret_cast<const uint4*>(a.x);
-        uint4* xd = reinterpret_cast<uint4*>(mb + CNT_N + 3 * n + ((4 - (3 * n) % 4) % 4));
-        for (int i = lane; i < a.x_bytes / 16; i += 64) xd[i] = xs[i];
-        __threadfence_system();
-        if (lane == 0) {
-            reinterpret_cast<uint32_t*>(words + 2)[0] = hs + 1;
-            __hip_atomic_store(a.doorbell, hs + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
     }
 }
 

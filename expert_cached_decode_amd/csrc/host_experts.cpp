@@ -4,9 +4,11 @@
 // FreeToken edge-MoE write-up, "Bandwidth-adaptive execution" (decode): the
 // misses not filled into the GPU cache are executed directly on the CPU,
 // leaving residency unchanged; host and GPU partial sums are merged exactly.
-// Work is split over worker threads by (expert, block of rows): first the
-// gate/up rows (activations of every token routed to the expert), then the
-// down rows, so each weight byte is read from host memory once per step.
+// Work is split over worker threads by (expert, block of rows): the gate/up
+// rows of every host-list expert (activations of every token routed to it),
+// then the down rows, each expert's down rows as soon as its own gate/up rows
+// are done (no barrier across experts), so each weight byte is read from host
+// memory once per step.
 // bf16 and MXFP4 rows use the host's AVX-512 bf16 dot unit when it has one
 // (the SwiGLU activations are then rounded to bf16, as on the GPU), else AVX2.
 #include "host_experts.h"
@@ -18,6 +20,7 @@
 #include <cmath>
 #include <condition_variable>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -172,7 +175,10 @@ struct HostPool {
     std::vector<uint16_t> act_b;             // [T*k][I] SwiGLU activations rounded to bf16 (bf16 dot path)
     bool bf16dot = false;                    // bf16/MXFP4 weights on a host with the bf16 dot unit
     int n1 = 0, n2 = 0;
-    std::atomic<int> next1{0}, next2{0}, done1{0}, done2{0}, arrived{0};
+    std::atomic<int> next1{0}, next2{0}, arrived{0};
+    // per host-list expert: its gate/up tasks not yet finished (a down task of the expert waits
+    // for zero; the tasks it waits for have all been claimed, so the wait ends)
+    std::unique_ptr<std::atomic<int>[]> left1{new std::atomic<int>[1024]};
     int nworkers = 0;
     // Rows per task, gate/up and down alike: the power of two (8 to 256) giving at most 512 KiB of
     // gate + up weight codes per task. Measured on the box's 14 workers at a fixed 300:1000 split:
@@ -210,12 +216,12 @@ struct HostPool {
                     if (bf16dot) act_b[(uint64_t)p * I + i] = bf16_rne(hv);
                 }
             }
-            done1.fetch_add(1, std::memory_order_release);
+            left1[e].fetch_sub(1, std::memory_order_release);
         }
-        while (done1.load(std::memory_order_acquire) < n1) std::this_thread::yield();
-        // phase 2: down rows -> y
+        // phase 2: down rows -> y, each task once its expert's activations are complete
         for (int t; (t = next2.fetch_add(1)) < n2;) {
             const int e = task_expert[n1 + t], r0 = task_r0[n1 + t];
+            while (left1[e].load(std::memory_order_acquire) > 0) _mm_pause();
             const uint8_t* base = j.expert_base[e];
             const uint8_t* d = base + 2ull * I * rbH;
             const uint8_t* dsc = base + 3ull * I * rbH + 2ull * I * (H / 32);
@@ -224,7 +230,6 @@ struct HostPool {
                     j.y[((uint64_t)(p / j.k) * H + h) * j.k + p % j.k] =
                         dot_row_any(j.wdtype, d + h * rbI, dsc + (uint64_t)h * (I / 32), j.act + (uint64_t)p * I,
                                     bf16dot ? act_b.data() + (uint64_t)p * I : nullptr, I);
-            done2.fetch_add(1, std::memory_order_release);
         }
     }
 
@@ -298,7 +303,9 @@ void host_pool_run(HostPool* p, const HostJob& j) {
     for (int e = 0; e < j.n_experts; ++e)
         for (int r = 0; r < j.H; r += p->rows) { p->task_expert.push_back(e); p->task_r0.push_back(r); }
     p->n2 = (int)p->task_expert.size() - p->n1;
-    p->next1 = 0; p->next2 = 0; p->done1 = 0; p->done2 = 0; p->arrived = 0;
+    const int per_expert = (j.I + p->rows - 1) / p->rows;
+    for (int e = 0; e < j.n_experts; ++e) p->left1[e].store(per_expert, std::memory_order_relaxed);
+    p->next1 = 0; p->next2 = 0; p->arrived = 0;
     {
         std::lock_guard<std::mutex> lk(p->mu);
         p->generation.fetch_add(1, std::memory_order_release);

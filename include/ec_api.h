@@ -110,7 +110,8 @@ typedef struct ec_config {
     int32_t victim_k;      /* K victim candidates per step (1..64); 0 = min(64, U_max) */
     uint32_t bp_mbps;      /* BP: expert transfer bandwidth (integer, any unit) */
     uint32_t bh_mbps;      /* BH: host expert processing bandwidth (>= 1, same unit) */
-    int32_t host_threads;  /* host branch worker threads; 0 = the host's hardware threads less 2 (1..32) */
+    int32_t host_threads;  /* host branch threads (the polling thread included); 0 = the CPUs the
+                              process may run on less 4 (1..32) */
     int32_t prefill_max_tokens; /* 0 = no prefill; else T_max for moe_prefill_layer */
     int32_t pool_layers;   /* layers the host pool holds (0 = L). With P < L, layer l reads its
                               experts from pool layer l mod P: the bytes moved per fill, host
@@ -145,6 +146,14 @@ typedef struct ec_stats {
     int32_t host_branch;  /* 1: decode steps are launched with the host branch (some step can
                              have host-side experts: BP < BH, K or C below U_max, or host-only
                              mode); 0: every routed expert is cache-side */
+    /* host branch, measured on the host: jobs run; their total time from the doorbell seen to
+     * the partial sums published; and the handoffs of the decode loop (a doorbell within 1 ms
+     * of the previous publication: the GPU saw the sums, finished the layer step and rang for
+     * the next one), their count and total time */
+    uint64_t host_jobs;
+    double host_busy_us;
+    uint64_t host_gaps;
+    double host_gap_us;
 } ec_stats;
 
 typedef struct ec_ctx ec_ctx;
