@@ -59,7 +59,7 @@ EXPORTS = ["ec_strerror", "ec_last_error", "ec_layout", "ec_workspace_size", "ec
            "ec_set_prefill_overlap", "cache_rebuild", "ec_epoch", "ec_get_stats", "ec_debug_state",
            "ec_kernel_timing", "ec_kernel_time", "ec_calibrate_bandwidth", "moe_gate_logits",
            "moe_decode_block", "ec_bank_write", "ec_bank_read", "ec_last_step", "ec_rebuild_slots",
-           "moe_decode_layer_static", "ec_hbm_read_probe", "ec_queue_delay"]
+           "moe_decode_layer_static", "ec_hbm_read_probe", "ec_queue_delay", "ec_host_branch_test_hooks"]
 KERNEL_KINDS = {"ctl": 0, "fill": 1, "gate_up": 2, "down": 3}
 
 
@@ -99,6 +99,7 @@ def lib():
         L.ec_hbm_read_probe.argtypes = [c_vp, c_u64, c_u64, c_i32, c_i32, c_vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double), P(c_u64)]
         L.ec_queue_delay.argtypes = [c_vp, ctypes.c_uint32]
+        L.ec_host_branch_test_hooks.argtypes = [c_vp, c_i32, ctypes.c_uint32]
         L.ec_calibrate_bandwidth.argtypes = [c_vp, c_i32, c_i32, P(ctypes.c_uint32), P(ctypes.c_uint32)]
         L.moe_gate_logits.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]
         L.moe_decode_block.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp]
@@ -319,6 +320,11 @@ class Context:
         check(lib().ec_kernel_time(self.handle, KERNEL_KINDS[kind], ctypes.byref(ms), ctypes.byref(n),
                                    1 if reset else 0), self.handle)
         return ms.value, n.value
+
+    def host_branch_test_hooks(self, pause_host, wait_polls=0):
+        """Test support: pause the host branch and/or bound the GPU's wait for it
+        (ec_host_branch_test_hooks)."""
+        check(lib().ec_host_branch_test_hooks(self.handle, 1 if pause_host else 0, int(wait_polls)), self.handle)
 
     def epoch(self):
         return lib().ec_epoch(self.handle)

@@ -72,6 +72,9 @@ struct ec_ctx {
     // sums published, and the handoff gaps between a job's publication and the next doorbell
     uint64_t host_jobs = 0, host_gaps = 0;
     double host_busy_us = 0, host_gap_us = 0;
+    // test support for the host branch's failure path (ec_host_branch_test_hooks)
+    std::atomic<bool> host_paused{false};
+    uint32_t host_wait_polls = kHostWaitPolls;
     std::atomic<bool> stop{false};
     std::vector<float> host_act;
     HostJob job{};
@@ -522,7 +525,7 @@ static void host_branch_poll(ec_ctx* x) {
     bool have_done = false;
     while (!x->stop.load(std::memory_order_relaxed)) {
         const uint32_t sq = __atomic_load_n(&x->doorbell[0], __ATOMIC_ACQUIRE);
-        if (sq != last) {
+        if (sq != last && !x->host_paused.load(std::memory_order_acquire)) {
             const auto t0 = clk::now();
             {
                 std::lock_guard<std::mutex> lk(x->pool_mu);
@@ -628,6 +631,7 @@ static ec_status decode_layer(ec_ctx* x, int32_t layer, const void* xin, const f
     d.host_pairs = x->host_branch ? 1 : 0;
     d.host_done = x->doorbell_dev + kDone; d.hseq = x->st.hseq; d.hseen = x->st.hseen; d.err = x->st.err;
     d.residual = residual;
+    d.wait_polls = x->host_wait_polls;
     if (x->C > 0 && !x->host_only) launch_fill(d, x->K, s, timer_next(x, 1));
     launch_gu(d, s, timer_next(x, 2));
     HIPCHK(x, hipGetLastError());
@@ -737,6 +741,13 @@ ec_status ec_hbm_read_probe(const void* dev_buf, uint64_t buf_bytes, uint64_t bu
     if (median_us) *median_us = 1e3 * ms[ms.size() / 2];
     if (best_us) *best_us = 1e3 * ms[0];
     if (bytes_read) *bytes_read = got;
+    return EC_OK;
+}
+
+ec_status ec_host_branch_test_hooks(ec_ctx* x, int32_t pause_host, uint32_t wait_polls) {
+    if (!x) return fail(nullptr, EC_EINVAL, "ctx is NULL");
+    x->host_wait_polls = wait_polls ? wait_polls : kHostWaitPolls;
+    x->host_paused.store(pause_host != 0, std::memory_order_release);
     return EC_OK;
 }
 

@@ -400,13 +400,13 @@ __global__ __launch_bounds__(256) void gu_kernel(const int32_t* counts, const in
 // other blocks poll. Every block then acquires at system scope, so the partial sums
 // the host wrote before publishing are seen. The waits are bounded: past the limit
 // the device error flag gets bit 1 and the kernel goes on (the output is then wrong,
-// and ec_get_stats reports it), so no wave can spin forever.
-constexpr uint32_t kHostWaitPolls = 1u << 22;
+// and ec_get_stats reports it), so no wave can spin forever. The bound (polls) is an argument:
+// kHostWaitPolls unless a test lowers it.
 
 // (out of line, the polling loop stays out of the GEMV's registers; its arguments are plain
 // pointers so that the kernel's argument block is not copied to private memory)
 __device__ __noinline__ void wait_host_branch(const uint32_t* hseq, const uint32_t* host_done, uint32_t* hseen,
-                                              int32_t* err) {
+                                              int32_t* err, uint32_t limit) {
     if (threadIdx.x == 0) {
         const uint32_t want = *hseq;
         const bool relay = blockIdx.x == 0;
@@ -414,7 +414,7 @@ __device__ __noinline__ void wait_host_branch(const uint32_t* hseq, const uint32
         uint32_t it = 0;
         while (relay ? __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != want
                      : __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
-            if (++it > kHostWaitPolls) {
+            if (++it > limit) {
                 atomicOr(err, 2);
                 break;
             }
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
             if (stale && bx == 0 && tid == 0) atomicOr(a.err, 4);
         }
         if (HOST) {
-            if (nhost > 0) wait_host_branch(a.hseq, a.host_done, a.hseen, a.err);
+            if (nhost > 0) wait_host_branch(a.hseq, a.host_done, a.hseen, a.err, a.wait_polls);
             // lane j < k carries pair j's host-side term (zero for cache-side pairs)
             const bool hj = lane < k && rw0 < 0;
             const float wj = w0;

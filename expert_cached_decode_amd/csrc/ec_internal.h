@@ -135,7 +135,9 @@ struct DecodeArgs {
     uint32_t* hseen;           // device: last finished sequence, relayed by block 0 of the down GEMV
     int32_t* err;              // device error flags
     int32_t residual;          // 1: out = x + merged output (chained MoE block)
+    uint32_t wait_polls;       // bound on the down GEMV's polls for the host's partial sums
 };
+constexpr uint32_t kHostWaitPolls = 1u << 22; // default wait bound (seconds of polling)
 void launch_fill(const DecodeArgs& a, int K, hipStream_t s, const hipEvent_t* ev = nullptr);
 void launch_link_probe(const uint8_t* src_dev, uint64_t bytes, uint32_t* sink, hipStream_t s);
 uint64_t launch_hbm_burst(const uint8_t* base, uint64_t bytes, hipStream_t s, const hipEvent_t* ev);

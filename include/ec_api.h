@@ -379,6 +379,17 @@ ec_status ec_kernel_timing(ec_ctx* ctx, int32_t on);
  * kind since timing was switched on (or last reset). Synchronises. */
 ec_status ec_kernel_time(ec_ctx* ctx, int32_t kind, double* total_ms, uint64_t* launches, int32_t reset);
 
+/* Test support for the host branch's failure path. pause_host != 0: the host
+ * stops answering doorbells (the mailbox waits) until called again with 0.
+ * wait_polls bounds how often the down GEMV polls for the host's partial sums
+ * in launches made after this call (0: the default 4194304, seconds of
+ * polling; a graph captured earlier keeps the bound it was captured with).
+ * With a paused host and a small bound, a step with host-side experts ends
+ * without their partial sums (its output is then wrong) and sets device error
+ * bit 2, which ec_get_stats reports as EC_EDEVICE: the failure path runs
+ * without any wait that could last. EC_EINVAL on a NULL ctx. */
+ec_status ec_host_branch_test_hooks(ec_ctx* ctx, int32_t pause_host, uint32_t wait_polls);
+
 /* Queue primer (measurement support): enqueues on `stream` one small kernel
  * that holds it for about `us` microseconds of the device's constant-rate
  * real-time clock, then ends. Launches the host queues behind it meet a busy

@@ -321,3 +321,27 @@ def test_decode_from_a_bank_file(tmp_path):
     assert st["fills"] > 0 and st["host"] > 0
     ctx.close()
     pinned.close()
+
+
+def test_host_wait_bound_flags_missing_partials():
+    """The host branch's failure path, forced from the host: with the host paused and the down
+    GEMV's wait for the host's partial sums bounded to 64 polls, a step with a host-side expert
+    ends without them, every workgroup finishes, and ec_get_stats reports device error bit 2."""
+    import torch
+    import expert_cached_decode_amd as EC
+    cfg = TINY  # BP:BH 500:1000: a cold step's two misses are one fill and one host-side expert
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool)
+    assert ctx.stats()["host_branch"] == 1
+    logits = torch.from_numpy(gen.decode_logits(cfg, steps=2)).cuda()
+    out = empty_out(cfg, 1)
+    ctx.host_branch_test_hooks(True, 64)
+    EC.moe_decode_layer(ctx, 0, x_to_device(cfg, gen.decode_x(cfg, 0, 0)), logits[0, 0], 1, out)
+    torch.cuda.synchronize()
+    with pytest.raises(EC.ECError, match="did not deliver"):
+        ctx.stats()
+    s = EC.binding.ec_stats()
+    assert EC.lib().ec_get_stats(ctx.handle, EC.binding.ctypes.byref(s), 1) == -7
+    assert s.device_error & 2 and s.host == 1
+    ctx.host_branch_test_hooks(False, 0)
+    ctx.close()
