@@ -872,12 +872,12 @@ __global__ __launch_bounds__(NT) void ctl_kernel(const float* logits, const int3
         const uint4* xs = reinterpret_cast<const uint4*>(a.x);
         uint4* xd = reinterpret_cast<uint4*>(mb + CNT_N + 3 * n + ((4 - (3 * n) % 4) % 4));
         for (int i = tid; i < a.x_bytes / 16; i += kCtlThreads) xd[i] = xs[i];
-        __threadfence_system();
+        __threadfence_system(); // each thread's mailbox stores are complete before the barrier
         __syncthreads();
         if (tid == 0) {
             const uint32_t sq = *a.st.hseq + 1;
             *a.st.hseq = sq;
-            __hip_atomic_store(a.doorbell, sq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(a.doorbell, sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }
 }
@@ -1035,10 +1035,10 @@ __global__ __launch_bounds__(256) void ctl1_kernel(const float* logits, const in
             const uint4* xs = reinterpret_cast<const uint4*>(a.x);
             uint4* xd = reinterpret_cast<uint4*>(mb + CNT_N + 3 * n + ((4 - (3 * n) % 4) % 4));
             for (int i = lane; i < a.x_bytes / 16; i += 64) xd[i] = xs[i];
-            __threadfence_system();
+            __threadfence_system(); // the mailbox's stores are complete before the doorbell is
             if (lane == 0) {
                 reinterpret_cast<uint32_t*>(words + 2)[0] = hs + 1;
-                __hip_atomic_store(a.doorbell, hs + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(a.doorbell, hs + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             }
         }
     }
