@@ -170,13 +170,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     constexpr int NB = FIRST ? 2 : 1;
     __shared__ uint16_t sA[BM * LDSP];
     __shared__ uint16_t sB[NB][BN * LDSP];
-    const int tt = blockIdx.x;
+    // Block b -> (M tile tt, N tile). Workgroups are dealt to the eight XCDs in turn (b mod 8):
+    // XCD x takes the M tiles 16 j + 2 x + {0, 1} (consecutive tiles, mostly one expert's) and runs
+    // all N tiles of one M tile back to back, so the tile's A rows (gathered tokens or activations)
+    // and the expert's weight rows are fetched into that XCD's L2 once instead of once per XCD.
+    const int NT = (FIRST ? a.I : a.H) / BN;
+    const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
+    const int tt = 16 * (bi / (2 * NT)) + 2 * xcd + (bi / NT) % 2;
     if (tt >= a.toff[a.E]) return;
     const int e = tile_expert(a.toff, a.E, tt);
     const int mt = tt - a.toff[e];
     const int rows = a.cnt[e] - mt * BM;  // valid rows in this tile (>= 1)
     const int g0 = a.off[e] + mt * BM;    // first grouped row
-    const int n0 = blockIdx.y * BN;
+    const int n0 = (bi % NT) * BN;
     const int K = FIRST ? a.H : a.I;
     const uint8_t* ebase = a.wbuf + (uint64_t)e * a.expert_bytes;
     const uint8_t* Wm[2] = {ebase + a.off_a, ebase + a.off_b};
@@ -356,17 +362,20 @@ hipError_t prefill_layer(PrefillState& p, const PrefillCall& c) {
     g.cnt = p.cnt; g.off = p.off; g.toff = p.toff; g.perm = p.perm;
     g.E = c.E; g.k = c.k; g.H = c.H; g.I = c.I;
     const int max_tiles = (n + BM - 1) / BM + c.E;
+    // 1-D grids: 16 M tiles (two per XCD) x all N tiles per round of 16 (see the kernel's mapping)
+    const unsigned rounds = (unsigned)((max_tiles + 15) / 16);
+    const dim3 grid1(rounds * 16 * (c.I / BN)), grid2(rounds * 16 * (c.H / BN));
     if (c.wdtype == EC_DT_MXFP4)
-        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_MXFP4, true>), dim3(max_tiles, c.I / BN), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_MXFP4, true>), grid1, dim3(256), 0, s, g);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_BF16, true>), dim3(max_tiles, c.I / BN), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_BF16, true>), grid1, dim3(256), 0, s, g);
     GemmArgs g2 = g;
     if (c.wdtype == EC_DT_MXFP4) {
         g2.off_a = hi; g2.off_sa = 3 * hi / 2 + 2 * hi / 32;
-        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_MXFP4, false>), dim3(max_tiles, c.H / BN), dim3(256), 0, s, g2);
+        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_MXFP4, false>), grid2, dim3(256), 0, s, g2);
     } else {
         g2.off_a = 4 * hi;
-        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_BF16, false>), dim3(max_tiles, c.H / BN), dim3(256), 0, s, g2);
+        hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_BF16, false>), grid2, dim3(256), 0, s, g2);
     }
     hipLaunchKernelGGL(combine_kernel, dim3(c.T, (c.H + 255) / 256), dim3(256), 0, s, p.y, p.w, c.k, c.H,
                        (uint16_t*)c.out);
