@@ -266,7 +266,7 @@ static void carve(ec_ctx* x, uint8_t* dev, uint8_t* pin, uint64_t* dev_bytes, ui
     Carve p(pin);
     x->doorbell = p.take<uint32_t>(2 * kDone);
     x->mb_pinned = p.take<int32_t>((mb_bytes + 3) / 4);
-    x->y_host_pinned = p.take<float>((uint64_t)x->Tmax * x->H);
+    x->y_host_pinned = p.take<float>((uint64_t)n * x->H);
     *pin_bytes = (p.off + 255) & ~255ull;
 }
 
@@ -509,7 +509,6 @@ static void host_branch_run(ec_ctx* x) {
     for (int h = 0; h < nhost; ++h)
         j.expert_base[h] = x->host_pool + ((uint64_t)(layer % x->P) * x->E + mb[CNT_N + h]) * x->lay.expert_bytes;
     j.rewritten = mb + CNT_N + n;
-    j.w = reinterpret_cast<const float*>(mb + CNT_N + 2 * n);
     j.T = T; j.k = x->k; j.H = x->H; j.I = x->I; j.wdtype = x->wdt;
     j.x = mb + mailbox_ints(n);
     j.y = x->y_host_pinned;
@@ -844,8 +843,8 @@ ec_status ec_calibrate_bandwidth(ec_ctx* x, int32_t probe_experts, int32_t apply
         std::vector<int32_t> rw(per);
         for (int i = 0; i < per; ++i) rw[i] = -(1 + i);
         std::vector<uint8_t> xz((size_t)per * x->H * 4, 0);
-        std::vector<float> ones(per, 1.f), ysink((size_t)per * x->H);
-        j.rewritten = rw.data(); j.w = ones.data(); j.T = per; j.k = 1; j.H = x->H; j.I = x->I; j.wdtype = x->wdt;
+        std::vector<float> ysink((size_t)per * x->H);
+        j.rewritten = rw.data(); j.T = per; j.k = 1; j.H = x->H; j.I = x->I; j.wdtype = x->wdt;
         j.x = xz.data(); j.y = ysink.data(); j.act = x->host_act.data();
         double best_s = 1e30;
         std::lock_guard<std::mutex> lk(x->pool_mu);

@@ -435,10 +435,10 @@ __device__ __noinline__ void wait_host_branch(const uint32_t* hseq, const uint32
 // LDS (STAGE: each is read from L2 once per block instead of once per row) or
 // loaded into registers right behind the weights. Each lane accumulates
 // w[t,j] * (its slice of W_down[h] . act[t,j]) in j order; one wave reduction
-// per row gives the cache-side sum. When the token has host-side pairs (HOST),
-// the host's sum over them (in ascending j, written to pinned memory as one
-// float per output row) is added to it: every pair of the token enters
-// out[t][h] exactly once. The block reads its 4 R host sums with one access
+// per row gives the cache-side sum. Host-side pairs (HOST) add
+// w[t,j] * y_host[t,j][h] through a second fixed-order wave reduction, so every
+// pair of the token enters out[t][h] exactly once; the block reads the host's
+// partial sums of its 4 R rows (k adjacent per row) with one contiguous access
 // over the host link and shares them through LDS. A host-side pair's weight
 // row is replaced by a dummy row of the activation buffer (always allocated,
 // at least one weight row long) so that every load of a group is issued back
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
     constexpr int AB = WDT == EC_DT_F32 ? 4 : 2; // bytes per activation element
     constexpr int QB = EPC * AB / 16;            // 16-byte quads per chunk
     extern __shared__ uint4 s_q[];               // [G][I * AB / 16]
-    __shared__ float s_hsum[HOST ? 4 * R : 1];   // the host's sums for the block's rows
+    __shared__ float s_hy[HOST ? 4 * R * kMaxTopK : 1]; // the host's partial sums of the block's rows
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // Linear block b -> (row block bx, token t). Workgroups are dealt to the eight XCDs in turn
     // (b mod 8); the row blocks of one XCD take all T tokens in consecutive turns, so the weight
@@ -607,17 +607,20 @@ __global__ __launch_bounds__(256) void down_kernel(const int32_t* rewritten, con
             // block 0 waits whenever the step has host-side pairs: it relays the host's sequence
             if (th || (nhost > 0 && blockIdx.x == 0)) wait_host_branch(a.hseq, a.host_done, a.hseen, a.err, a.wait_polls);
             if (th) {
-                // the host's sums for the block's 4 R rows: one read over the host link, then LDS
-                if (tid < 4 * R) s_hsum[tid] = a.y_host[(int64_t)t * H + bx * 4 * R + tid];
+                // the host's partial sums of the block's 4 R rows (k adjacent per row, 4 R k contiguous
+                // floats): one read over the host link into LDS; lane j < k then carries pair j's term
+                const float* yb = a.y_host + ((int64_t)t * H + bx * 4 * R) * k;
+                for (int i = tid; i < 4 * R * k; i += 256) s_hy[i] = yb[i];
                 __syncthreads();
+                const bool hj = lane < k && rw0 < 0;
 #pragma unroll
-                for (int r = 0; r < R; ++r) hs[r] = s_hsum[wave * R + r];
+                for (int r = 0; r < R; ++r) hs[r] = hj ? w0 * s_hy[(wave * R + r) * k + min(lane, k - 1)] : 0.f;
             }
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float y = wave_sum(acc[r]);
-            if (HOST) y += hs[r];
+            if (HOST) y += wave_sum(hs[r]);
             if (lane == 0) {
                 const int64_t o = (int64_t)t * H + row0 + r;
                 if (WDT == EC_DT_F32) {

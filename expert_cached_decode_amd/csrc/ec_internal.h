@@ -125,7 +125,7 @@ struct DecodeArgs {
     const float* w;
     const void* x;
     float* act;            // [T_max*k][I] SwiGLU activations of cache-side pairs
-    const float* y_host;   // [T_max][H] the host side of the merge, pinned (device-visible address)
+    const float* y_host;   // [T_max][H][k] host partials, pinned (device-visible address)
     void* out;
     uint64_t expert_bytes;
     int32_t layer, E, k, T, H, I, wdtype, U_max; // layer: the host-pool layer the fills read

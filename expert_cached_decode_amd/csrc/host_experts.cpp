@@ -4,20 +4,17 @@
 // FreeToken edge-MoE write-up, "Bandwidth-adaptive execution" (decode): the
 // misses not filled into the GPU cache are executed directly on the CPU,
 // leaving residency unchanged; host and GPU partial sums are merged exactly.
-// Work is split over worker threads in two phases of (expert, block of rows)
-// tasks. Gate/up: the activations of every token routed to the expert. Down:
-// the down rows' products with those activations, as soon as the expert's own
-// gate/up rows are done (no barrier across experts); the last down task to
-// finish a block of output rows sums the block over each token's host-side
-// pairs in ascending j, w[t,j] * f_e(x_t)[h], so the GPU reads one sum per
-// output element. Each weight byte is read from host memory once per step.
+// Work is split over worker threads by (expert, block of rows): the gate/up
+// rows of every host-list expert (activations of every token routed to it),
+// then the down rows, each expert's down rows as soon as its own gate/up rows
+// are done (no barrier across experts), so each weight byte is read from host
+// memory once per step.
 // bf16 and MXFP4 rows use the host's AVX-512 bf16 dot unit when it has one
 // (the SwiGLU activations are then rounded to bf16, as on the GPU), else AVX2.
 #include "host_experts.h"
 
 #include <immintrin.h>
 
-#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cmath>
@@ -164,9 +161,6 @@ inline float dot_row_any(int wdt, const uint8_t* row, const uint8_t* srow, const
 
 } // namespace
 
-// blocks of output rows (H / rows, rows >= 8): H up to 16384
-constexpr int kMaxRowBlocks = 2048;
-
 struct HostPool {
     std::vector<std::thread> threads;
     std::mutex mu;
@@ -175,13 +169,8 @@ struct HostPool {
     std::atomic<bool> stop{false};
     const HostJob* job = nullptr;
     // phase bookkeeping
-    std::vector<int> task_expert, task_r0;   // phase-1 task table
+    std::vector<int> task_expert, task_r0;   // phase-1 and phase-2 task tables
     std::vector<std::vector<int>> pairs_of;  // host index -> pairs
-    std::vector<int> host_tokens;            // tokens with host-side pairs, ascending
-    std::vector<std::vector<int>> tok_pairs; // per entry of host_tokens: its host-side pairs, ascending
-    std::vector<float> ydot;                 // [T*k][H] down row . activations of host-side pairs
-    // per block of output rows: its down tasks not yet finished (the last one sums the block)
-    std::unique_ptr<std::atomic<int>[]> left2{new std::atomic<int>[kMaxRowBlocks]};
     std::vector<float> xf;                   // [T][H] activations widened to f32
     std::vector<uint16_t> act_b;             // [T*k][I] SwiGLU activations rounded to bf16 (bf16 dot path)
     bool bf16dot = false;                    // bf16/MXFP4 weights on a host with the bf16 dot unit
@@ -229,32 +218,18 @@ struct HostPool {
             }
             left1[e].fetch_sub(1, std::memory_order_release);
         }
-        // phase 2: tasks of (expert, block of output rows): the down row . activations of each of
-        // the expert's pairs into ydot, once the expert's activations are complete; the last task
-        // to finish a row block sums that block for every token with host-side pairs, over the
-        // token's host-side pairs in ascending j, into y
+        // phase 2: down rows -> y, each task once its expert's activations are complete
         for (int t; (t = next2.fetch_add(1)) < n2;) {
-            const int e = task_expert[n1 + t], r0 = task_r0[n1 + t], r1 = std::min(r0 + rows, H);
+            const int e = task_expert[n1 + t], r0 = task_r0[n1 + t];
             while (left1[e].load(std::memory_order_acquire) > 0) _mm_pause();
             const uint8_t* base = j.expert_base[e];
             const uint8_t* d = base + 2ull * I * rbH;
             const uint8_t* dsc = base + 3ull * I * rbH + 2ull * I * (H / 32);
-            for (int h = r0; h < r1; ++h)
+            for (int h = r0; h < r0 + rows && h < H; ++h)
                 for (int p : pairs_of[e])
-                    ydot[(uint64_t)p * H + h] =
+                    j.y[((uint64_t)(p / j.k) * H + h) * j.k + p % j.k] =
                         dot_row_any(j.wdtype, d + h * rbI, dsc + (uint64_t)h * (I / 32), j.act + (uint64_t)p * I,
                                     bf16dot ? act_b.data() + (uint64_t)p * I : nullptr, I);
-            const int rb = r0 / rows;
-            if (left2[rb].fetch_sub(1, std::memory_order_acq_rel) != 1) continue;
-            for (size_t ti = 0; ti < host_tokens.size(); ++ti) {
-                const std::vector<int>& tp = tok_pairs[ti]; // ascending j
-                float* yt = j.y + (uint64_t)host_tokens[ti] * H;
-                for (int h = r0; h < r1; ++h) {
-                    float acc = 0.f;
-                    for (int p : tp) acc = std::fma(j.w[p], ydot[(uint64_t)p * H + h], acc);
-                    yt[h] = acc;
-                }
-            }
         }
     }
 
@@ -306,21 +281,11 @@ void host_pool_run(HostPool* p, const HostJob& j) {
     if (j.n_experts <= 0) return;
     p->job = &j;
     p->pairs_of.assign(j.n_experts, {});
-    p->host_tokens.clear();
     for (int i = 0; i < j.T * j.k; ++i)
         if (j.rewritten[i] < 0) {
             int h = -j.rewritten[i] - 1;
-            if (h >= j.n_experts) continue;
-            p->pairs_of[h].push_back(i);
-            const int t = i / j.k;
-            if (p->host_tokens.empty() || p->host_tokens.back() != t) {
-                p->host_tokens.push_back(t);
-                if (p->tok_pairs.size() < p->host_tokens.size()) p->tok_pairs.emplace_back();
-                p->tok_pairs[p->host_tokens.size() - 1].clear();
-            }
-            p->tok_pairs[p->host_tokens.size() - 1].push_back(i);
+            if (h < j.n_experts) p->pairs_of[h].push_back(i);
         }
-    p->ydot.resize((size_t)j.T * j.k * j.H);
     // bf16 and MXFP4 weights meet bf16 activations in the bf16 dot unit when the host has one:
     // x is bf16 already, the SwiGLU activations are rounded to bf16 as on the GPU
     p->bf16dot = j.wdtype != 0 && host_has_bf16_dot();
@@ -335,14 +300,9 @@ void host_pool_run(HostPool* p, const HostJob& j) {
     for (int e = 0; e < j.n_experts; ++e)
         for (int r = 0; r < j.I; r += p->rows) { p->task_expert.push_back(e); p->task_r0.push_back(r); }
     p->n1 = (int)p->task_expert.size();
-    int with_pairs = 0;
-    for (int e = 0; e < j.n_experts; ++e) {
-        if (p->pairs_of[e].empty()) continue;
-        ++with_pairs;
+    for (int e = 0; e < j.n_experts; ++e)
         for (int r = 0; r < j.H; r += p->rows) { p->task_expert.push_back(e); p->task_r0.push_back(r); }
-    }
     p->n2 = (int)p->task_expert.size() - p->n1;
-    for (int rb = 0; rb * p->rows < j.H; ++rb) p->left2[rb].store(with_pairs, std::memory_order_relaxed);
     const int per_expert = (j.I + p->rows - 1) / p->rows;
     for (int e = 0; e < j.n_experts; ++e) p->left1[e].store(per_expert, std::memory_order_relaxed);
     p->next1 = 0; p->next2 = 0; p->arrived = 0;

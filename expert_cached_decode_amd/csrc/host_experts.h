@@ -11,12 +11,10 @@ struct HostJob {
     const uint8_t* expert_base[1024]; // per host-list index: expert start in the host pool
     int n_experts;
     const int32_t* rewritten; // [T*k] slot or -(1 + host index)
-    const float* w;           // [T*k] routing weights
     int T, k, H, I, wdtype;
     const void* x;            // [T][H] f32 (wdtype f32) or bf16
-    float* y;                 // [T][H] written for tokens with host-side pairs only: the host side
-                              // of the merge, sum over the token's host-side pairs j in ascending
-                              // j of w[t,j] * f_e(x_t)[h] (fp32, one fused multiply-add per pair)
+    float* y;                 // [T][H][k] written for host-side pairs (t, j) only (the k partial
+                              // sums of one output element are adjacent for the merge)
     float* act;               // scratch [T*k][I]
 };
 
