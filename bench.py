@@ -328,7 +328,7 @@ def main():
                          "timed, then the all-hit window), no graph replays and no other leg; prints the D9 lines")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

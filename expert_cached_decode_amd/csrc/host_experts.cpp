@@ -181,7 +181,7 @@ struct HostPool {
     std::unique_ptr<std::atomic<int>[]> left1{new std::atomic<int>[1024]};
     int nworkers = 0;
     // Rows per task, gate/up and down alike: the power of two (8 to 256) giving at most 512 KiB of
-    // gate + up weight codes per task. Measured on the box's 14 workers at a fixed 300:1000 split:
+    // gate + up weight codes per task. Measured on a 16-core host with 14 workers at a fixed 300:1000 split:
     // 64 rows best for bf16 rows of 2048 (about 2% over 32 and 128), 128 for MXFP4 rows of 4096
     // (12% over 32); 8-row tasks lost 20-35%.
     int rows = 32;
