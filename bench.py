@@ -189,7 +189,7 @@ class DecodeWorkload:
         self.ctx.kernel_timing(True)
         self.enqueue_us = 0.0
         pending = 0
-        for s in steps:
+        for n_step, s in enumerate(steps):
             i = s % self.n_inputs
             if pending + self.cfg.L > 1024:
                 # the library holds 1024 event pairs per kernel kind and drains them (synchronising)
@@ -202,7 +202,8 @@ class DecodeWorkload:
                 EC.binding.queue_delay(self.prime_us, stream)
             t0 = time.perf_counter()
             self.token_layers(self.xs[i], self.logits[i], stream)
-            self.enqueue_us = max(self.enqueue_us, 1e6 * (time.perf_counter() - t0))
+            if n_step > 0:  # the first step of a pass also pays Python's own warm-up
+                self.enqueue_us = max(self.enqueue_us, 1e6 * (time.perf_counter() - t0))
         torch.cuda.synchronize()
         st = self.ctx.stats(reset=True)
         assert st["device_error"] == 0
@@ -321,7 +322,7 @@ def main():
     ap.add_argument("--prefill-chunks", type=int, default=4)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc runs)")
-    ap.add_argument("--prime-us", type=int, default=6000,
+    ap.add_argument("--prime-us", type=int, default=8000,
                     help="kernel passes: queue each step's launches behind a primer of this many us (0: off)")
     ap.add_argument("--counters-only", action="store_true",
                     help="for rocprofv3 --pmc runs: eager decode steps only (W warm-up, then --timing-steps "
