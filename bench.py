@@ -324,6 +324,9 @@ def main():
                     help="also run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc runs)")
     ap.add_argument("--prime-us", type=int, default=8000,
                     help="kernel passes: queue each step's launches behind a primer of this many us (0: off)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="for profiler runs: the prefill leg alone (no calibration and no decode leg); "
+                         "prints its JSON")
     ap.add_argument("--counters-only", action="store_true",
                     help="for rocprofv3 --pmc runs: eager decode steps only (W warm-up, then --timing-steps "
                          "timed, then the all-hit window), no graph replays and no other leg; prints the D9 lines")
@@ -357,6 +360,12 @@ def main():
     wl = DecodeWorkload(cfg, P, period, n_inputs, prefill_T=prefill_T, host_threads=args.host_threads)
     wl.prime_us = args.prime_us
     ctx = wl.ctx
+    if args.prefill_only:
+        if not prefill_T:
+            sys.exit("--prefill-only needs the qwen workload with prefill on")
+        print(json.dumps({"prefill": bench_prefill(wl, QWEN_PREFILL, args.prefill_chunks)}), flush=True)
+        wl.close()
+        return
     # measured BP and BH (MB/s): applied with --bpbh calibrate, else reported only
     bp_meas, bh_meas = ctx.calibrate_bandwidth(min(32, cfg.E // 4), apply=(args.bpbh == "calibrate"))
     log("calibration: BP %d MB/s over the link, BH %d MB/s on the host branch%s"
@@ -916,18 +925,30 @@ def bench_prefill(wl, pcfg, chunks, link_layers=8):
     torch.cuda.synchronize()
     t_off = a.elapsed_time(b) / 1e3
     ctx.set_prefill_overlap(True)
+    # compute alone: layer 0 again and again once its buffer holds it (no upload on the path)
+    EC.moe_prefill_layer(ctx, 0, xs[0], lgs[0], T, out, compute, ctx.copy_stream)
+    torch.cuda.synchronize()
+    reps = 10
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        EC.moe_prefill_layer(ctx, 0, xs[0], lgs[0], T, out, compute, ctx.copy_stream)
+    b.record()
+    torch.cuda.synchronize()
+    compute_ms = a.elapsed_time(b) / reps
     del xs, lgs, out
     s_chunk = float(np.median(times))
     bound = cfg.L * lb / (link_gbs * 1e9)
     log("prefill: %.3f s per 8192-token chunk (double buffer off: %.3f s); raw copies of the same bytes take %.3f s "
-        "at %.1f GB/s sustained over %d layers (single layer copy %.1f GB/s)"
-        % (s_chunk, t_off, bound, link_gbs, link_layers, link_single))
+        "at %.1f GB/s sustained over %d layers (single layer copy %.1f GB/s); compute alone %.3f ms per layer"
+        % (s_chunk, t_off, bound, link_gbs, link_layers, link_single, compute_ms))
     return {"s_per_chunk": round(s_chunk, 4), "tokens": T, "layers": cfg.L, "chunks_timed": len(times),
             "bytes_per_chunk": cfg.L * lb, "link_GBs_sustained": round(link_gbs, 2),
             "link_GBs_single_layer": round(link_single, 2), "link_layers_timed": link_layers,
             "link_copy_s": round(bound, 4), "ratio_to_link_copy": round(s_chunk / bound, 4),
             "chunk_link_GBs": round(cfg.L * lb / s_chunk / 1e9, 2),
-            "s_per_chunk_no_double_buffer": round(t_off, 4), "tok_s": round(T / s_chunk, 1)}
+            "s_per_chunk_no_double_buffer": round(t_off, 4), "tok_s": round(T / s_chunk, 1),
+            "compute_ms_per_layer": round(compute_ms, 4)}
 
 
 def bench_cpu(cfg, logits, P, period, budget_s=12.0, cache_bytes=6 << 30):

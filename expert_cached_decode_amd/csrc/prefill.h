@@ -15,6 +15,7 @@ struct PrefillState {
     int32_t* ids = nullptr;  // [Tp*k]
     float* w = nullptr;      // [Tp*k]
     int32_t* cnt = nullptr;  // [E]
+    int32_t* segc = nullptr; // [ceil(Tp*k / 512)][E] per-segment counts, then their column prefix sums
     int32_t* off = nullptr;  // [E+1] row offsets of each expert's group
     int32_t* toff = nullptr; // [E+1] tile offsets (64-row tiles)
     int32_t* perm = nullptr; // [Tp*k] grouped row -> pair index t*k+j

@@ -29,7 +29,6 @@ constexpr int AQ = BM * BK / 8 / 256, BQ = BN * BK / 8 / 256; // 16-byte chunks 
 static_assert(AQ * 256 * 8 == BM * BK && BQ * 256 * 8 == BN * BK, "tile chunks per thread");
 
 void launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
-void launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -38,9 +37,42 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // ---- grouping ---------------------------------------------------------------
-__global__ void count_kernel(const int32_t* ids, int n, int32_t* cnt) {
-    int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) atomicAdd(&cnt[ids[i]], 1);
+// A stable counting sort of the n = T k pairs by expert, in segments of kSeg pairs (one
+// wavefront each): per-segment counts, a scan down each expert's column of segments (which
+// also gives the counts), and a placement pass in which each wavefront ranks its pairs among
+// the pairs of the same expert in pair order. Every expert's rows then list its pairs in
+// ascending pair index.
+constexpr int kSeg = 512;
+
+__global__ __launch_bounds__(64) void seg_count_kernel(const int32_t* ids, int n, int E, int32_t* segc) {
+    extern __shared__ int32_t s_h[]; // [E]
+    const int lane = threadIdx.x, sg = blockIdx.x;
+    for (int e = lane; e < E; e += 64) s_h[e] = 0;
+    __syncthreads();
+    const int i1 = min(n, (sg + 1) * kSeg);
+    for (int i = sg * kSeg + lane; i < i1; i += 64) atomicAdd(&s_h[ids[i]], 1);
+    __syncthreads();
+    for (int e = lane; e < E; e += 64) segc[(int64_t)sg * E + e] = s_h[e];
+}
+
+// cnt[e] = pairs routed to e; segc[s][e] becomes the number of those in segments before s.
+// One wavefront per expert: 64 segments at a time, a wave prefix sum by row shifts and broadcasts.
+__global__ __launch_bounds__(64) void seg_scan_kernel(int32_t* segc, int nseg, int E, int32_t* cnt) {
+    const int e = blockIdx.x, lane = threadIdx.x;
+    int run = 0;
+    for (int s0 = 0; s0 < nseg; s0 += 64) {
+        const int sg = s0 + lane;
+        const int c = sg < nseg ? segc[(int64_t)sg * E + e] : 0;
+        int v = c; // inclusive scan over the wavefront
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(v, o);
+            if (lane >= o) v += u;
+        }
+        if (sg < nseg) segc[(int64_t)sg * E + e] = run + v - c;
+        run += __shfl(v, 63);
+    }
+    if (lane == 0) cnt[e] = run;
 }
 
 // off[e] = rows before expert e; toff[e] = BM-row tiles before expert e
@@ -78,22 +110,36 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* cnt, int E, i
     if (t == 0) { off[E] = tc; toff[E] = tt; }
 }
 
-// block e: stable compaction of the pairs routed to expert e
-__global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int n, const int32_t* off, int32_t* perm) {
-    __shared__ int s_w[4];
-    const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int base = off[e];
-    for (int i0 = 0; i0 < n; i0 += 256) {
-        const int i = i0 + threadIdx.x;
-        const bool f = i < n && ids[i] == e;
-        const uint64_t b = __ballot(f);
-        if (lane == 0) s_w[wave] = __popcll(b);
-        __syncthreads();
-        int pre = 0, tot = 0;
-        for (int w2 = 0; w2 < 4; ++w2) { pre += w2 < wave ? s_w[w2] : 0; tot += s_w[w2]; }
-        if (f) perm[base + pre + __popcll(b & ((1ull << lane) - 1ull))] = i;
-        base += tot;
-        __syncthreads();
+// Pair i of segment s routed to expert e goes to row off[e] + (pairs of e in earlier segments)
+// + (pairs of e before i in s). The wavefront takes its segment 64 pairs at a time: lanes holding
+// the same expert find each other with one ballot per bit of the expert id, each lane's rank among
+// them is a popcount, and the group's lowest lane then advances the expert's next row in LDS.
+__global__ __launch_bounds__(64) void seg_place_kernel(const int32_t* ids, int n, int E, const int32_t* segc,
+                                                        const int32_t* off, int32_t* perm) {
+    extern __shared__ int32_t s_run[]; // [E] next row of each expert
+    const int lane = threadIdx.x, sg = blockIdx.x;
+    for (int e = lane; e < E; e += 64) s_run[e] = off[e] + segc[(int64_t)sg * E + e];
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int i1 = min(n, (sg + 1) * kSeg);
+    for (int i0 = sg * kSeg; i0 < i1; i0 += 64) {
+        __syncthreads(); // the previous round's updates (and the initial rows) are visible
+        const int i = i0 + lane;
+        const bool v = i < i1;
+        const int e = v ? ids[i] : 0;
+        uint64_t m = __ballot(v); // lanes with this lane's expert
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        const int row = v ? s_run[e] + __popcll(m & below) : 0;
+        __syncthreads(); // every lane has read its expert's row before the leaders advance it
+        if (v) {
+            perm[row] = i;
+            if ((m & below) == 0) s_run[e] += __popcll(m);
+        }
     }
 }
 
@@ -170,19 +216,25 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
     constexpr int NB = FIRST ? 2 : 1;
     __shared__ uint16_t sA[BM * LDSP];
     __shared__ uint16_t sB[NB][BN * LDSP];
-    // Block b -> (M tile tt, N tile). Workgroups are dealt to the eight XCDs in turn (b mod 8):
-    // XCD x takes the M tiles 16 j + 2 x + {0, 1} (consecutive tiles, mostly one expert's) and runs
-    // all N tiles of one M tile back to back, so the tile's A rows (gathered tokens or activations)
-    // and the expert's weight rows are fetched into that XCD's L2 once instead of once per XCD.
+    // Block b -> (M tile, N tile). The work items (expert e, N tile n, M tile m of e) are ordered
+    // e, then n, then m, and cut into eight contiguous ranges, one per XCD (workgroups are dealt
+    // to the XCDs in turn, b mod 8). An XCD thus runs the M tiles of one (expert, N tile) back to
+    // back, so the weight tile is fetched from HBM once and served to its other M tiles by that
+    // XCD's L2, and the N tiles of one expert follow one another, so its A rows (gathered tokens
+    // or activations) stay in that L2 too.
     const int NT = (FIRST ? a.I : a.H) / BN;
-    const int xcd = blockIdx.x & 7, bi = blockIdx.x >> 3;
-    const int tt = 16 * (bi / (2 * NT)) + 2 * xcd + (bi / NT) % 2;
-    if (tt >= a.toff[a.E]) return;
-    const int e = tile_expert(a.toff, a.E, tt);
-    const int mt = tt - a.toff[e];
+    const int total = a.toff[a.E] * NT;   // (M tile, N tile) items of this call
+    const int per = (total + 7) >> 3;     // items per XCD
+    const int bi = blockIdx.x >> 3;
+    const int item = (blockIdx.x & 7) * per + bi;
+    if (bi >= per || item >= total) return;
+    const int e = tile_expert(a.toff, a.E, item / NT); // toff[e] * NT <= item < toff[e + 1] * NT
+    const int mts = a.toff[e + 1] - a.toff[e];          // M tiles of expert e
+    const int r = item - a.toff[e] * NT;
+    const int mt = r % mts;
     const int rows = a.cnt[e] - mt * BM;  // valid rows in this tile (>= 1)
     const int g0 = a.off[e] + mt * BM;    // first grouped row
-    const int n0 = (bi % NT) * BN;
+    const int n0 = (r / mts) * BN;
     const int K = FIRST ? a.H : a.I;
     const uint8_t* ebase = a.wbuf + (uint64_t)e * a.expert_bytes;
     const uint8_t* Wm[2] = {ebase + a.off_a, ebase + a.off_b};
@@ -264,13 +316,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs a) {
             }
 }
 
-// out[t][h] = sum_j w[t,j] * y[t*k+j][h], j in order
+// out[t][h] = sum_j w[t,j] * y[t*k+j][h], j in order; four adjacent outputs per thread (H is a
+// multiple of 64), so each thread has its k 16-byte loads in flight at once
 __global__ __launch_bounds__(256) void combine_kernel(const float* y, const float* w, int k, int H, uint16_t* out) {
-    const int t = blockIdx.x, h = blockIdx.y * 256 + threadIdx.x;
+    const int t = blockIdx.x, h = (blockIdx.y * 256 + threadIdx.x) * 4;
     if (h >= H) return;
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc = fmaf(w[t * k + j], y[((uint64_t)t * k + j) * H + h], acc);
-    out[(uint64_t)t * H + h] = f32_to_bf16_rne(acc);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j = 0; j < k; ++j) {
+        const float wj = w[t * k + j];
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + ((uint64_t)t * k + j) * H + h));
+        a0 = fmaf(wj, v[0], a0);
+        a1 = fmaf(wj, v[1], a1);
+        a2 = fmaf(wj, v[2], a2);
+        a3 = fmaf(wj, v[3], a3);
+    }
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(a2) | ((uint32_t)f32_to_bf16_rne(a3) << 16);
+    *reinterpret_cast<uint2*>(out + (uint64_t)t * H + h) = make_uint2(lo, hi);
 }
 
 // ---- host orchestration --------------------------------------------------------
@@ -283,6 +345,7 @@ void prefill_carve(PrefillState& p, Carve& d, int Tp, int E, int k, int H, int I
     p.ids = d.take<int32_t>(n);
     p.w = d.take<float>(n);
     p.cnt = d.take<int32_t>(E);
+    p.segc = d.take<int32_t>((n + kSeg - 1) / kSeg * (uint64_t)E);
     p.off = d.take<int32_t>(E + 1);
     p.toff = d.take<int32_t>(E + 1);
     p.perm = d.take<int32_t>(n);
@@ -342,10 +405,12 @@ hipError_t prefill_layer(PrefillState& p, const PrefillCall& c) {
     const int n = c.T * c.k;
     hipStream_t s = c.compute;
     launch_route(c.logits, c.T, c.E, c.k, p.ids, p.w, s);
-    launch_fill_i32(p.cnt, 0, c.E, s);
-    hipLaunchKernelGGL(count_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p.ids, n, p.cnt);
+    const int nseg = (n + kSeg - 1) / kSeg;
+    const size_t hist_lds = (size_t)c.E * sizeof(int32_t);
+    hipLaunchKernelGGL(seg_count_kernel, dim3(nseg), dim3(64), hist_lds, s, p.ids, n, c.E, p.segc);
+    hipLaunchKernelGGL(seg_scan_kernel, dim3(c.E), dim3(64), 0, s, p.segc, nseg, c.E, p.cnt);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, p.cnt, c.E, p.off, p.toff);
-    hipLaunchKernelGGL(place_kernel, dim3(c.E), dim3(256), 0, s, p.ids, n, p.off, p.perm);
+    hipLaunchKernelGGL(seg_place_kernel, dim3(nseg), dim3(64), hist_lds, s, p.ids, n, c.E, p.segc, p.off, p.perm);
     GemmArgs g{};
     g.wbuf = p.buf[b];
     g.expert_bytes = c.expert_bytes;
@@ -361,10 +426,11 @@ hipError_t prefill_layer(PrefillState& p, const PrefillCall& c) {
     g.y = p.y;
     g.cnt = p.cnt; g.off = p.off; g.toff = p.toff; g.perm = p.perm;
     g.E = c.E; g.k = c.k; g.H = c.H; g.I = c.I;
-    const int max_tiles = (n + BM - 1) / BM + c.E;
-    // 1-D grids: 16 M tiles (two per XCD) x all N tiles per round of 16 (see the kernel's mapping)
-    const unsigned rounds = (unsigned)((max_tiles + 15) / 16);
-    const dim3 grid1(rounds * 16 * (c.I / BN)), grid2(rounds * 16 * (c.H / BN));
+    // 1-D grids: eight ranges (one per XCD) of at most ceil(max_tiles * NT / 8) items each (see the
+    // kernel's mapping); blocks past the call's items exit
+    const int64_t max_tiles = (n + BM - 1) / BM + c.E;
+    const dim3 grid1((unsigned)(8 * ((max_tiles * (c.I / BN) + 7) / 8))),
+        grid2((unsigned)(8 * ((max_tiles * (c.H / BN) + 7) / 8)));
     if (c.wdtype == EC_DT_MXFP4)
         hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_MXFP4, true>), grid1, dim3(256), 0, s, g);
     else
@@ -377,7 +443,7 @@ hipError_t prefill_layer(PrefillState& p, const PrefillCall& c) {
         g2.off_a = 4 * hi;
         hipLaunchKernelGGL((grouped_gemm_kernel<EC_DT_BF16, false>), grid2, dim3(256), 0, s, g2);
     }
-    hipLaunchKernelGGL(combine_kernel, dim3(c.T, (c.H + 255) / 256), dim3(256), 0, s, p.y, p.w, c.k, c.H,
+    hipLaunchKernelGGL(combine_kernel, dim3(c.T, (c.H + 1023) / 1024), dim3(256), 0, s, p.y, p.w, c.k, c.H,
                        (uint16_t*)c.out);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipEventRecord(p.done[b], s)) != hipSuccess) return e;
