@@ -83,3 +83,18 @@ def test_prefill_mxfp4_one_layer():
     o, x, lg = res[0]
     check_rows(cfg, 0, o, x, lg, [0, 5, 100, 511])
     ctx.close()
+
+
+@pytest.mark.parametrize("E,k,T", [(300, 5, 777), (37, 3, 171), (1024, 8, 64)])
+def test_prefill_grouping_odd_shapes(E, k, T):
+    """Expert counts that are not powers of two (the placement ranks lanes by one ballot per bit of
+    the expert id) and pair counts T k that are not multiples of the 512-pair segments or of a
+    wavefront: every checked row must still meet the oracle, which it cannot if a pair is placed
+    under the wrong expert or twice."""
+    cfg = QWEN_PREFILL.with_(L=1, E=E, k=k, K=k, H=256, I=128)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool, C=0, T=1, prefill=T)
+    (o, x, lg), = run_prefill(cfg, ctx, [0], T)
+    rng = np.random.default_rng(E + T)
+    check_rows(cfg, 0, o, x, lg, sorted(set([0, T - 1] + list(rng.choice(T, min(T, 24), replace=False)))))
+    ctx.close()
