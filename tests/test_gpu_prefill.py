@@ -85,13 +85,14 @@ def test_prefill_mxfp4_one_layer():
     ctx.close()
 
 
-@pytest.mark.parametrize("E,k,T", [(300, 5, 777), (37, 3, 171), (1024, 8, 64)])
-def test_prefill_grouping_odd_shapes(E, k, T):
+@pytest.mark.parametrize("E,k,T,H", [(300, 5, 777, 256), (37, 3, 171, 320), (1024, 8, 64, 256)])
+def test_prefill_grouping_odd_shapes(E, k, T, H):
     """Expert counts that are not powers of two (the placement ranks lanes by one ballot per bit of
     the expert id) and pair counts T k that are not multiples of the 512-pair segments or of a
     wavefront: every checked row must still meet the oracle, which it cannot if a pair is placed
-    under the wrong expert or twice."""
-    cfg = QWEN_PREFILL.with_(L=1, E=E, k=k, K=k, H=256, I=128)
+    under the wrong expert or twice. H = 320 takes the down GEMM's 64-wide N tiles (H is not a
+    multiple of 128)."""
+    cfg = QWEN_PREFILL.with_(L=1, E=E, k=k, K=k, H=H, I=128)
     pool = make_pool(cfg)
     ctx = make_ctx(cfg, pool, C=0, T=1, prefill=T)
     (o, x, lg), = run_prefill(cfg, ctx, [0], T)
