@@ -26,6 +26,7 @@ typedef float f2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BK = 64, LDSP = BK + 8; // LDS row pitch in bf16 elements
+constexpr int CPR = BK / 8;           // 16-byte chunks per tile row
 constexpr int AQ = BM * BK / 8 / 256; // 16-byte chunks per thread of an A tile
 static_assert(AQ * 256 * 8 == BM * BK, "tile chunks per thread");
 // N tile width: 64 for the gate/up GEMM (two weight tiles share the A tile), 128 for the down
@@ -164,7 +165,7 @@ template <int WDT, int BQ>
 __device__ __forceinline__ void load_b(const uint8_t* W, const uint8_t* Ws, int K, int n0, int k0, u32x4 (&r)[BQ]) {
 #pragma unroll
     for (int q = 0; q < BQ; ++q) {
-        const int c = threadIdx.x + 256 * q, row = c >> 3, col = (c & 7) * 8;
+        const int c = threadIdx.x + 256 * q, row = c / CPR, col = (c % CPR) * 8;
         if constexpr (WDT == EC_DT_BF16) {
             r[q] = *reinterpret_cast<const u32x4*>(W + ((uint64_t)(n0 + row) * K + k0 + col) * 2);
         } else {
@@ -188,7 +189,7 @@ template <int NQ>
 __device__ __forceinline__ void store_lds(uint16_t* lds, const u32x4 (&r)[NQ]) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const int c = threadIdx.x + 256 * q, row = c >> 3, col = (c & 7) * 8;
+        const int c = threadIdx.x + 256 * q, row = c / CPR, col = (c % CPR) * 8;
         *reinterpret_cast<u32x4*>(lds + row * LDSP + col) = r[q];
     }
 }
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(256, 3) void grouped_gemm_kernel(GemmArgs a) {
     const uint16_t* arow[AQ];
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
-        const int c = threadIdx.x + 256 * q, r = c >> 3;
+        const int c = threadIdx.x + 256 * q, r = c / CPR;
         const int rr = r < rows ? r : 0;
         if (FIRST) arow[q] = a.x + (uint64_t)(a.perm[g0 + rr] / a.k) * a.H;
         else arow[q] = a.act_in + (uint64_t)(g0 + rr) * a.I;
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(256, 3) void grouped_gemm_kernel(GemmArgs a) {
     auto gload = [&](int k0) {
 #pragma unroll
         for (int q = 0; q < AQ; ++q) {
-            const int c = threadIdx.x + 256 * q, col = (c & 7) * 8;
+            const int c = threadIdx.x + 256 * q, col = (c % CPR) * 8;
             ra[q] = *reinterpret_cast<const u32x4*>(arow[q] + k0 + col);
         }
 #pragma unroll
