@@ -486,6 +486,7 @@ def main():
             log("dsv4 D9 all-hit at %.1f%% of 8 TB/s = %.1f%% of its two-burst ceiling (%.2f us, %.1f%%)"
                 % (100 * hit["frac"], 100 * hit["frac_of_burst_ceiling"], two, 100 * two_frac))
         result["cache_ctl_stress"] = bench_cache_ctl_alone()
+        result["stress_legs"] = bench_stress_legs()
         if args.cold_start_gb > 0:
             result["cold_start"] = bench_cold_start(cfg, args.cold_start_gb)
     print(json.dumps(result), flush=True)
@@ -529,6 +530,25 @@ def bench_dsv4_legs(ratios=((300, 1000), (1000, 1000)), warm=32, steps=64, timin
     out["roofline_all_hit"] = wl.all_hit(0)
     wl.close()
     del wl
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_stress_legs(ps=(0.0, 0.3, 0.6, 0.9), Ts=(1, 16), warm=8, steps=24, rec_steps=384, rec_at=(128, 256)):
+    """The stress shapes (DeepSeek-V4-Flash layers, MXFP4, 4096 slots, K = 64, BP:BH 1000:1000) in
+    a short form of their two sweeps: tok/s and miss rate against step-to-step routing overlap p at
+    batch 1 and 16, and the batch-1 miss rate by 32-step window across cache_rebuild 40% -> 15% ->
+    40%. The host pool holds 4 pool layers (layer l reads pool layer l mod 4), drawn as one layer
+    and copied: the bytes per fill are those of the full bank."""
+    import torch
+    from gen.configs import STRESS
+    cfg = STRESS
+    wl = DecodeWorkload(cfg, 4, 1, 4)
+    out = {"workload": "stress shapes: DeepSeek-V4-Flash layers (43, top-6 of 256, MXFP4), 4096 slots, "
+                       "K = 64, BP:BH 1000:1000, 4 pinned pool layers",
+           "locality_sweep": bench_locality_sweep(wl.ctx, cfg, ps=ps, Ts=Ts, warm=warm, steps=steps),
+           "rebuild_recovery": bench_rebuild_recovery(wl.ctx, cfg, steps=rec_steps, at=rec_at)}
+    wl.close()
     torch.cuda.empty_cache()
     return out
 
