@@ -758,6 +758,40 @@ __global__ __launch_bounds__(NT) void ctl_kernel(const float* logits, const int3
     qq = min(qq, (int64_t)(C - h));
     const int q = qq > 0 ? (int)qq : 0;
 
+    // 4b. with host-side experts, the mailbox is published and the doorbell rung here, before the
+    //     victim selection: the host's work needs only the host list, the host-side pairs'
+    //     rewritten ids, the weights and x, all known now. Mailbox in pinned host memory:
+    //     [counts 8][host_list n][rewritten n][w n][x bytes], n = T*k; cache-side pairs read 0 there
+    //     (the host computes the pairs with negative ids only). Every writer makes its stores
+    //     visible system-wide before the block barrier, then one thread publishes the sequence.
+    //     s_slot holds the unique experts' early ids meanwhile (each thread has read its residency
+    //     above; step 6 overwrites them with the final slots).
+    if (a.host_branch && m - q > 0) {
+        int32_t* mb = a.sb.mailbox;
+        const bool host_r = miss && midx >= q;
+        if (valid) s_slot[r] = host_r ? -(1 + midx - q) : 0;
+        if (host_r) mb[CNT_N + (midx - q)] = u;
+        if (tid == 0) {
+            mb[CNT_U] = U; mb[CNT_H] = h; mb[CNT_M] = m; mb[CNT_Q] = q; mb[CNT_HOST] = m - q;
+            mb[CNT_GPU] = U - (m - q); mb[6] = T; mb[7] = l;
+        }
+        __syncthreads();
+        for (int i = tid; i < n; i += kCtlThreads) {
+            mb[CNT_N + n + i] = s_slot[s_pos[i]];
+            reinterpret_cast<float*>(mb)[CNT_N + 2 * n + i] = s_w[i];
+        }
+        const uint4* xs = reinterpret_cast<const uint4*>(a.x);
+        uint4* xd = reinterpret_cast<uint4*>(mb + CNT_N + 3 * n + ((4 - (3 * n) % 4) % 4));
+        for (int i = tid; i < a.x_bytes / 16; i += kCtlThreads) xd[i] = xs[i];
+        __threadfence_system(); // each thread's mailbox stores are complete before the barrier
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t sq = *a.st.hseq + 1;
+            *a.st.hseq = sq;
+            __hip_atomic_store(a.doorbell, sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+
     // 5. victims: the q oldest slots not hit in this step (empty slots first, in slot order),
     //    in one pass over the slot table read above (select_victims); slots past C and slots
     //    hit in this step are not candidates
@@ -845,7 +879,7 @@ __global__ __launch_bounds__(NT) void ctl_kernel(const float* logits, const int3
     // work descriptor of each cache-side expert: slot, first entry in tok_pairs, pair count, first pair
     if (valid && s_g[r] >= 0) a.sb.gpu_desc[s_g[r]] = make_int4(slot_r, off, cnt, s_first[r]);
 
-    // 8. counts, stats, clock; mailbox for the host branch
+    // 8. counts, stats, clock (the mailbox went out after step 4)
     if (tid == 0) {
         int32_t* c = a.sb.counts;
         c[CNT_U] = U; c[CNT_H] = h; c[CNT_M] = m; c[CNT_Q] = q; c[CNT_HOST] = m - q; c[CNT_GPU] = n_gpu;
@@ -854,31 +888,6 @@ __global__ __launch_bounds__(NT) void ctl_kernel(const float* logits, const int3
         st[ST_STEPS] += 1; st[ST_HITS] += h; st[ST_MISSES] += m; st[ST_FILLS] += q;
         st[ST_HOST] += m - q; st[ST_EVICT] += n_ev;
         *a.st.clock = clk + 1;
-    }
-    if (a.host_branch && m - q > 0) {
-        // mailbox in pinned host memory: [counts 8][host_list n][rewritten n][w n][x bytes], n = T*k.
-        // The host branch polls the doorbell; every writer makes its stores visible system-wide
-        // before the block barrier, then one thread publishes the new sequence number.
-        int32_t* mb = a.sb.mailbox;
-        if (tid == 0) {
-            mb[CNT_U] = U; mb[CNT_H] = h; mb[CNT_M] = m; mb[CNT_Q] = q; mb[CNT_HOST] = m - q; mb[CNT_GPU] = n_gpu;
-            mb[6] = T; mb[7] = l;
-        }
-        if (valid && cls == CLS_HOST) mb[CNT_N + (-slot_r - 1)] = u;
-        for (int i = tid; i < n; i += kCtlThreads) {
-            mb[CNT_N + n + i] = s_slot[s_pos[i]];
-            reinterpret_cast<float*>(mb)[CNT_N + 2 * n + i] = s_w[i];
-        }
-        const uint4* xs = reinterpret_cast<const uint4*>(a.x);
-        uint4* xd = reinterpret_cast<uint4*>(mb + CNT_N + 3 * n + ((4 - (3 * n) % 4) % 4));
-        for (int i = tid; i < a.x_bytes / 16; i += kCtlThreads) xd[i] = xs[i];
-        __threadfence_system(); // each thread's mailbox stores are complete before the barrier
-        __syncthreads();
-        if (tid == 0) {
-            const uint32_t sq = *a.st.hseq + 1;
-            *a.st.hseq = sq;
-            __hip_atomic_store(a.doorbell, sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
     }
 }
 
