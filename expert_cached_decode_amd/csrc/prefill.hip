@@ -312,14 +312,14 @@ __global__ __launch_bounds__(256, 3) void grouped_gemm_kernel(GemmArgs a) {
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int r = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + q;
+                const int tr = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + q; // row in the tile
                 const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
-                if (r >= rows) continue;
+                if (tr >= rows) continue;
                 if constexpr (FIRST) {
                     const float gv = acc[0][i][j][q], uv = acc[1][i][j][q];
-                    a.act_out[(uint64_t)(g0 + r) * a.I + n] = f32_to_bf16_rne(gv / (1.f + expf(-gv)) * uv);
+                    a.act_out[(uint64_t)(g0 + tr) * a.I + n] = f32_to_bf16_rne(gv / (1.f + expf(-gv)) * uv);
                 } else {
-                    a.y[(uint64_t)a.perm[g0 + r] * a.H + n] = acc[0][i][j][q];
+                    a.y[(uint64_t)a.perm[g0 + tr] * a.H + n] = acc[0][i][j][q];
                 }
             }
 }
