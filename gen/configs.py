@@ -5,7 +5,7 @@ MoE is hard": DeepSeek-V4-Flash has 43 MoE layers, 6 of 256 routed experts per
 token; evaluation setup: Qwen3.6-35B-A3B in BF16, DeepSeek-V4-Flash as native
 MXFP4 expert blocks; mechanism attribution: 8192-token prefill chunks).
 """
-from dataclasses import dataclass, field, replace
+from dataclasses import dataclass, replace
 
 F32, BF16, MXFP4 = 0, 1, 2
 DTYPE_NAMES = {F32: "f32", BF16: "bf16", MXFP4: "mxfp4"}

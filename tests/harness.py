@@ -6,7 +6,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 import gen
-from gen.configs import F32, MXFP4
+from gen.configs import F32
 
 
 def row_rel_err(got, ref):

@@ -9,7 +9,7 @@ import pytest
 
 import gen
 from gen.configs import DSV4_DECODE, QWEN_DECODE
-from tests.harness import empty_out, make_ctx, make_pool
+from tests.harness import make_ctx, make_pool
 
 pytestmark = pytest.mark.gpu
 

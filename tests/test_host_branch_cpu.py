@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 
 import gen
-from gen.configs import BF16, DSV4_DECODE, F32, MXFP4, QWEN_DECODE, TINY
+from gen.configs import DSV4_DECODE, F32, QWEN_DECODE, TINY
 from oracle import moe as oracle_moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -11,7 +11,7 @@ import pytest
 
 import gen
 from gen.configs import DSV4_DECODE, QWEN_DECODE
-from tests.harness import make_ctx, make_pool, oracle_layer, out_to_host, row_rel_err, x_to_device
+from tests.harness import make_ctx, make_pool, oracle_layer, row_rel_err, x_to_device
 
 pytestmark = pytest.mark.gpu
 
