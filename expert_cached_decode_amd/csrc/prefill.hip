@@ -222,8 +222,11 @@ template <int WDT, bool FIRST, int BN>
 __global__ __launch_bounds__(256, 3) void grouped_gemm_kernel(GemmArgs a) {
     constexpr int NB = FIRST ? 2 : 1;
     constexpr int BQ = BTile<BN>::Q;
-    __shared__ uint16_t sA[BM * LDSP];
-    __shared__ uint16_t sB[NB][BN * LDSP];
+    // one LDS block: the A tile and the NB weight tiles during the K loop; afterwards the down
+    // GEMM stages its fp32 output tile there, half a tile at a time
+    __shared__ __align__(16) uint16_t s_tiles[(BM + NB * BN) * LDSP];
+    uint16_t* const sA = s_tiles;
+    uint16_t (*const sB)[BN * LDSP] = reinterpret_cast<uint16_t (*)[BN * LDSP]>(s_tiles + BM * LDSP);
     // Block b -> (M tile, N tile). The work items (expert e, N tile n, M tile m of e) are ordered
     // e, then n, then m, and cut into eight contiguous ranges, one per XCD (workgroups are dealt
     // to the XCDs in turn, b mod 8). An XCD thus runs the M tiles of one (expert, N tile) back to
@@ -306,22 +309,50 @@ __global__ __launch_bounds__(256, 3) void grouped_gemm_kernel(GemmArgs a) {
         }
     }
     // epilogue: lane holds D[(lane/16)*4 + q][lane%16] of each 16x16 tile
+    if constexpr (FIRST) {
+        // (staging these bf16 stores through LDS as well measured no faster: 67 MB per layer)
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int tr = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + q; // row in the tile
-                const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
-                if (tr >= rows) continue;
-                if constexpr (FIRST) {
+                for (int q = 0; q < 4; ++q) {
+                    const int tr = wm * (BM / 2) + i * 16 + (lane >> 4) * 4 + q; // row in the tile
+                    const int n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
+                    if (tr >= rows) continue;
                     const float gv = acc[0][i][j][q], uv = acc[1][i][j][q];
                     a.act_out[(uint64_t)(g0 + tr) * a.I + n] = f32_to_bf16_rne(gv / (1.f + expf(-gv)) * uv);
-                } else {
-                    a.y[(uint64_t)a.perm[g0 + tr] * a.H + n] = acc[0][i][j][q];
                 }
+    } else {
+        // The fp32 outputs go through LDS, one half of the tile's rows at a time (the wavefronts
+        // with wm = half write theirs), and leave as whole-row segments of 16 bytes per lane, so
+        // each scattered output row y[perm[g]] is written in full 128-byte lines.
+        constexpr int CP = BN + 4; // row pitch in floats: rows 4 apart start 16 banks apart
+        static_assert((BM / 2) * CP * 4 <= (BM + NB * BN) * LDSP * 2, "output half-tile fits the tile LDS");
+        constexpr int LPR = BN / 4; // lanes per output row (16 bytes each)
+        float* const sC = reinterpret_cast<float*>(s_tiles);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            __syncthreads(); // the K loop's (or the previous half's) reads of this LDS are done
+            if (wm == half)
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            sC[(i * 16 + (lane >> 4) * 4 + q) * CP + wn * (BN / 2) + j * 16 + (lane & 15)] =
+                                acc[0][i][j][q];
+            __syncthreads();
+#pragma unroll
+            for (int rr = threadIdx.x / LPR; rr < BM / 2; rr += 256 / LPR) {
+                const int tr = half * (BM / 2) + rr, c4 = (threadIdx.x % LPR) * 4;
+                if (tr < rows)
+                    *reinterpret_cast<f32x4*>(a.y + (uint64_t)a.perm[g0 + tr] * a.H + n0 + c4) =
+                        *reinterpret_cast<const f32x4*>(sC + rr * CP + c4);
             }
+        }
+    }
 }
 
 // out[t][h] = sum_j w[t,j] * y[t*k+j][h], j in order; four adjacent outputs per thread (H is a
