@@ -25,7 +25,7 @@ typedef float f2v __attribute__((ext_vector_type(2)));
 // prefetch arrays stay in registers; arrays of uint4 were placed in private memory)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BK = 64, LDSP = BK + 8; // LDS row pitch in bf16 elements
+constexpr int BM = 128, BK = 64, LDSP = BK; // LDS row pitch in bf16 elements (rows are swizzled, not padded)
 constexpr int CPR = BK / 8;           // 16-byte chunks per tile row
 constexpr int AQ = BM * BK / 8 / 256; // 16-byte chunks per thread of an A tile
 static_assert(AQ * 256 * 8 == BM * BK, "tile chunks per thread");
@@ -185,17 +185,23 @@ __device__ __forceinline__ void load_b(const uint8_t* W, const uint8_t* Ws, int 
     }
 }
 
+// LDS tiles: row r keeps its 16-byte chunk c at chunk position c ^ ((r / 2) mod CPR). A row is
+// 128 bytes, so two consecutive rows fill the 64 banks once (tile stores: two rows per 16 lanes,
+// no conflict), and the 16 rows a fragment read touches at one chunk land on 16 distinct groups
+// of four banks.
+__device__ __forceinline__ int lds_swz(int row, int col) { return row * LDSP + (((col >> 3) ^ ((row >> 1) & (CPR - 1))) << 3); }
+
 template <int NQ>
 __device__ __forceinline__ void store_lds(uint16_t* lds, const u32x4 (&r)[NQ]) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const int c = threadIdx.x + 256 * q, row = c / CPR, col = (c % CPR) * 8;
-        *reinterpret_cast<u32x4*>(lds + row * LDSP + col) = r[q];
+        *reinterpret_cast<u32x4*>(lds + lds_swz(row, col)) = r[q];
     }
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* lds, int row, int col) {
-    uint4 u = *reinterpret_cast<const uint4*>(lds + row * LDSP + col);
+    uint4 u = *reinterpret_cast<const uint4*>(lds + lds_swz(row, col));
     return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -224,7 +230,8 @@ __global__ __launch_bounds__(256, 3) void grouped_gemm_kernel(GemmArgs a) {
     constexpr int BQ = BTile<BN>::Q;
     // one LDS block: the A tile and the NB weight tiles during the K loop; afterwards the down
     // GEMM stages its fp32 output tile there, half a tile at a time
-    __shared__ __align__(16) uint16_t s_tiles[(BM + NB * BN) * LDSP];
+    constexpr int kTileElems = (BM + NB * BN) * LDSP, kOutElems = FIRST ? 0 : (BM / 2) * (BN + 4) * 2;
+    __shared__ __align__(16) uint16_t s_tiles[kTileElems > kOutElems ? kTileElems : kOutElems];
     uint16_t* const sA = s_tiles;
     uint16_t (*const sB)[BN * LDSP] = reinterpret_cast<uint16_t (*)[BN * LDSP]>(s_tiles + BM * LDSP);
     // Block b -> (M tile, N tile). The work items (expert e, N tile n, M tile m of e) are ordered
@@ -328,7 +335,7 @@ __global__ __launch_bounds__(256, 3) void grouped_gemm_kernel(GemmArgs a) {
         // with wm = half write theirs), and leave as whole-row segments of 16 bytes per lane, so
         // each scattered output row y[perm[g]] is written in full 128-byte lines.
         constexpr int CP = BN + 4; // row pitch in floats: rows 4 apart start 16 banks apart
-        static_assert((BM / 2) * CP * 4 <= (BM + NB * BN) * LDSP * 2, "output half-tile fits the tile LDS");
+        static_assert((BM / 2) * CP * 2 <= kOutElems, "output half-tile fits the tile LDS");
         constexpr int LPR = BN / 4; // lanes per output row (16 bytes each)
         float* const sC = reinterpret_cast<float*>(s_tiles);
 #pragma unroll
