@@ -99,3 +99,14 @@ def test_prefill_grouping_odd_shapes(E, k, T, H):
     rng = np.random.default_rng(E + T)
     check_rows(cfg, 0, o, x, lg, sorted(set([0, T - 1] + list(rng.choice(T, min(T, 24), replace=False)))))
     ctx.close()
+
+
+def test_prefill_mxfp4_odd_shapes():
+    """MXFP4 weights (decoded to bf16 in the tile loads) through the same grouping and GEMMs at odd
+    shapes: 40 experts, top-3, 300 tokens, H = 320 (the down GEMM's 64-wide tiles), I = 256."""
+    cfg = DSV4_DECODE.with_(L=1, E=40, k=3, K=3, H=320, I=256, slots=0, T=300)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool, C=0, T=1, prefill=300)
+    (o, x, lg), = run_prefill(cfg, ctx, [0], 300)
+    check_rows(cfg, 0, o, x, lg, [0, 1, 77, 150, 298, 299])
+    ctx.close()
