@@ -126,6 +126,53 @@ def test_gate_up_forms(wd, H, I, T):
     ctx.close()
 
 
+def random_shapes(n=12, seed=20261202):
+    """Seeded draws over the shapes the library accepts: any dtype; H and I multiples of 64 (up to
+    512 for f32, 1024 for bf16, 2048 for MXFP4, so that whole and guarded rows of every width
+    occur); 2..320 experts; top-k up to 32 (a quarter of the draws) or 8; 1..8 tokens; cache slots
+    0..2E over two layers; K 0..64 (0: the library's default, min(64, U_max)); BP:BH on both sides
+    of 1. Pools above 384 MB are redrawn."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        wd = int(rng.choice([F32, BF16, MXFP4, BF16, MXFP4]))
+        maxd = {F32: 512, BF16: 1024, MXFP4: 2048}[wd]
+        H = 64 * int(rng.integers(1, maxd // 64 + 1))
+        I = 64 * int(rng.integers(1, maxd // 64 + 1))
+        E = int(rng.integers(2, 321))
+        k = int(rng.integers(1, min(32, E) + 1)) if rng.random() < 0.25 else int(rng.integers(1, min(8, E) + 1))
+        T = int(rng.integers(1, 9))
+        if T * k > 1024:
+            continue
+        es = {F32: 12 * H * I, BF16: 6 * H * I, MXFP4: 3 * H * I // 2 + 3 * H * I // 32}[wd]
+        if 2 * E * es > (384 << 20):
+            continue
+        C = int(rng.integers(0, 2 * E + 1))
+        K = int(rng.integers(0, 65))
+        bp, bh = [(300, 1000), (1000, 1000), (2000, 1000), (500, 1000), (700, 300)][int(rng.integers(0, 5))]
+        out.append((wd, H, I, E, k, T, C, K, bp, bh))
+    return out
+
+
+@pytest.mark.parametrize("i,shape", list(enumerate(random_shapes())))
+def test_random_shapes(i, shape):
+    """Decode at seeded random shapes within the accepted ranges: outputs of every second step of both
+    layers against the oracle, cache counters of all steps against the literal LRU simulator."""
+    wd, H, I, E, k, T, C, K, bp, bh = shape
+    print("shape", i, dict(wd=wd, H=H, I=I, E=E, k=k, T=T, C=C, K=K, bp=bp, bh=bh), flush=True)
+    cfg = TINY.with_(L=2, E=E, k=k, H=H, I=I, wdtype=wd, slots=C, K=K, T=T, bp=bp, bh=bh, p=0.5,
+                     seed=TINY.seed + 1000 + i)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool)
+    outs, logits = run_decode(cfg, ctx, 6, 2, T, lambda s, l: s % 2 == 1)
+    check_against_oracle(cfg, outs, 1e-5 if wd == F32 else 1e-2)
+    st = ctx.stats()
+    K_eff = K if K else min(64, min(E, T * k))  # victim_k 0 selects min(64, U_max)
+    ref = sim_counts(cfg, logits, 2, T, C, K_eff, bp, bh)
+    assert {k_: st[k_] for k_ in ref} == ref
+    ctx.close()
+
+
 @pytest.mark.parametrize("wd,split", [(BF16, (300, 1000, 40)), (BF16, (1000, 1000, 40)), (BF16, (2000, 1000, 40)),
                                       (BF16, (300, 1000, 0)), (BF16, (1000, 1000, 1024)),
                                       (MXFP4, (1000, 1000, 24)), (MXFP4, (2000, 1000, 64)),
