@@ -110,3 +110,40 @@ def test_prefill_mxfp4_odd_shapes():
     (o, x, lg), = run_prefill(cfg, ctx, [0], 300)
     check_rows(cfg, 0, o, x, lg, [0, 1, 77, 150, 298, 299])
     ctx.close()
+
+
+def random_prefill_shapes(n=8, seed=20261203):
+    """Seeded draws over prefill shapes: bf16 or MXFP4 weights; 2..600 experts; top-1..12; 1..2500
+    tokens; H a multiple of 64 up to 2048 (64- and 128-wide down tiles both occur) and I a multiple
+    of 64 up to 1024. Pools above 384 MB are redrawn."""
+    from gen.configs import BF16, MXFP4
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        wd = int(rng.choice([BF16, MXFP4]))
+        H = 64 * int(rng.integers(1, 33))
+        I = 64 * int(rng.integers(1, 17))
+        E = int(rng.integers(2, 601))
+        k = int(rng.integers(1, min(12, E) + 1))
+        T = int(rng.integers(1, 2501))
+        es = 6 * H * I if wd == BF16 else 3 * H * I // 2 + 3 * H * I // 32
+        if E * es > (384 << 20):
+            continue
+        out.append((wd, H, I, E, k, T))
+    return out
+
+
+@pytest.mark.parametrize("i,shape", list(enumerate(random_prefill_shapes())))
+def test_prefill_random_shapes(i, shape):
+    """Prefill at seeded random shapes: the first and last rows and 14 sampled ones against the
+    oracle."""
+    wd, H, I, E, k, T = shape
+    print("shape", i, dict(wd=wd, H=H, I=I, E=E, k=k, T=T), flush=True)
+    base = QWEN_PREFILL if wd == QWEN_PREFILL.wdtype else DSV4_DECODE
+    cfg = base.with_(L=1, E=E, k=k, K=k, H=H, I=I, slots=0, T=T, seed=base.seed + 2000 + i)
+    pool = make_pool(cfg)
+    ctx = make_ctx(cfg, pool, C=0, T=1, prefill=T)
+    (o, x, lg), = run_prefill(cfg, ctx, [0], T)
+    rng = np.random.default_rng(1000 + i)
+    check_rows(cfg, 0, o, x, lg, sorted(set([0, T - 1] + list(rng.choice(T, min(T, 14), replace=False)))))
+    ctx.close()
