@@ -345,6 +345,9 @@ void ecg_decode_logits(uint64_t seed, int steps, int L, int T, int E, int k, dou
             if (s > 0) {
                 int keep = 0;
                 for (int j = 0; j < k; ++j) keep += (u01_open(stream_u64(key, c++)) < p);
+                /* the fresh draws come from the E - k experts outside the previous set: when fewer
+                   remain than k - keep, the shortfall is kept from the previous set instead */
+                if (k - keep > E - k) keep = 2 * k - E;
                 /* partial Fisher-Yates over the previous set */
                 for (int j = 0; j < keep; ++j) {
                     int r = j + (int)below(key, c++, (uint32_t)(k - j));

@@ -221,3 +221,38 @@ def test_invalid_id_sets_device_error():
         EC.binding.check(EC.lib().ec_get_stats(ctx.handle, EC.binding.ctypes.byref(EC.binding.ec_stats()), 0),
                          ctx.handle)
     ctx.close()
+
+
+def random_traces(n=10, seed=20261204):
+    """Seeded draws over the control step's accepted ranges: 1..6 layers, 2..4096 experts (log-
+    uniform), top-1..32, 1..64 tokens with T k <= 1024, 0..min(L E, 12000) slots (past the 5120 held
+    in registers sometimes), K 0..64, BP:BH on both sides of 1, routing overlap 0..0.9, routing
+    separate or fused into the control kernel, and a rebuild at step 12 in a third of the traces."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        L = int(rng.integers(1, 7))
+        E = int(round(2 ** rng.uniform(1, 12)))
+        k = int(rng.integers(1, min(32, E) + 1))
+        T = int(rng.integers(1, 65))
+        if T * k > 1024:
+            continue
+        C = int(rng.integers(0, min(L * E, 12000) + 1))
+        K = int(rng.integers(0, 65))
+        bp, bh = [(300, 1000), (1000, 1000), (2000, 1000), (700, 300)][int(rng.integers(0, 4))]
+        p = float(rng.choice([0.0, 0.3, 0.6, 0.9]))
+        fused = bool(rng.integers(0, 2))
+        rebuild = {12: int(rng.integers(0, 10001))} if rng.random() < 1 / 3 else None
+        out.append((L, E, k, T, C, K, bp, bh, p, fused, rebuild))
+    return out
+
+
+@pytest.mark.parametrize("i,trace", list(enumerate(random_traces())))
+def test_random_traces(i, trace):
+    """24-step traces at seeded random shapes: every decision of every step bit-exact against the
+    simulator, and the final residency, slot keys and LRU order."""
+    L, E, k, T, C, K, bp, bh, p, fused, rebuild = trace
+    print("trace", i, dict(L=L, E=E, k=k, T=T, C=C, K=K, bp=bp, bh=bh, p=p, fused=fused, rebuild=rebuild),
+          flush=True)
+    cfg = TINY.with_(L=L, E=E, k=k, T=T, slots=C, K=K, bp=bp, bh=bh, p=p, seed=TINY.seed + 3000 + i)
+    run_trace(cfg, 24, T=T, rebuild=rebuild, fused=fused)
