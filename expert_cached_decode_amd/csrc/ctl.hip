@@ -324,8 +324,36 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
 // to q. Should the candidates not fit in LDS (only with slot tables beyond the registers), a
 // bisection over key values first narrows mu to the exact q-th smallest key.
 
+// The value of lane (lane ^ m), for a mask m known at compile time once the callers' loops are
+// unrolled, without an LDS round trip (the whole wavefront must be active):
+//   m = 1, 2: one DPP quad permutation ([1,0,3,2], [2,3,0,1]);
+//   m = 4: the quad reversal (lane ^ 3) and then the half-row mirror (lane ^ 7);
+//   m = 8: the half-row mirror (lane ^ 7) and then the row mirror (lane ^ 15);
+//   m = 16, 32: v_permlane16_swap / v_permlane32_swap of the value with itself leaves the other
+//     half's copy in one of the two results: lanes whose bit m is clear take the second.
+// Other masks go through ds_bpermute.
+__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int m) {
+    switch (m) {
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+    case 4: return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, false), 0x141, 0xF,
+                                                      0xF, false);
+    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false), 0x140, 0xF,
+                                                      0xF, false);
+    case 16: {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane_id() & 16) ? r[0] : r[1];
+    }
+    case 32: {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane_id() & 32) ? r[0] : r[1];
+    }
+    default: return (uint32_t)__shfl_xor((int)v, m);
+    }
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m), hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+    const uint32_t lo = shfl_xor_u32((uint32_t)v, m), hi = shfl_xor_u32((uint32_t)(v >> 32), m);
     return ((uint64_t)hi << 32) | lo;
 }
 
