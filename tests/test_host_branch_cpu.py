@@ -11,7 +11,7 @@ scales fall outside the range the bf16 path handles exactly (those rows take the
 BF16 host). The same jobs run under ThreadSanitizer and under AddressSanitizer +
 UndefinedBehaviorSanitizer: every job is run several times back to back on one worker pool
 (spinning workers, as in decode), and every run must give bit-identical sums and leave the
-GPU-side pairs' entries untouched (the driver checks both).
+GPU-side pairs' entries untouched (harness.cpp checks both).
 """
 import os
 import subprocess
