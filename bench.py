@@ -335,6 +335,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.steady_steps < 1 or args.timing_steps < 1:
+        print("bench.py: need --steps, --steady-steps and --timing-steps >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     from gen.configs import MXFP4, QWEN_PREFILL

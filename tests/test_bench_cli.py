@@ -1,5 +1,5 @@
-"""bench.py's command line, on the CPU: it measures one GPU and says so for any other count, and
-its options parse."""
+"""bench.py's command line, on the CPU: it measures one GPU and says so for any other count, it
+refuses step counts it cannot time, and its options parse."""
 import os
 import subprocess
 import sys
@@ -31,3 +31,10 @@ def test_options_parse():
     assert r.returncode == 0
     for opt in ("--steps", "--warmup", "--workload", "--prefill-only", "--counters-only", "--bpbh"):
         assert opt in r.stdout
+
+
+def test_step_counts_it_cannot_time_are_refused():
+    for args in (("--steps", "0"), ("--warmup", "-1"), ("--steady-steps", "0"), ("--timing-steps", "0")):
+        r = run(*args)
+        assert r.returncode == 2, args
+        assert ">= 1" in r.stderr, args
